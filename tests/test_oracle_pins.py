@@ -1,0 +1,499 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix.
+
+Nothing here compares the oracle with itself: each test checks it against
+a value printed on the pages (tests/golden/), a hand-worked case, a
+library routine (torch's scaled_dot_product_attention, numpy.lexsort), a
+closed form, an invariant, or the full-history brute force in
+tests/bruteforce.py.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import OracleState, OracleError
+from bounded_memory_decode_amd import synth
+from bruteforce import BruteForce
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def tiny(**kw):
+    base = synth.WORKLOADS["layer_b1"].with_(
+        name="tiny", wid=100, B=2, L=1, H=4, G=2, d=8, R=7, N=4, C=2,
+        t0=0, bank_n=0, steps=40, qkv_std=1.0, w_std=0.5, ring_full=False)
+    return base.with_(**kw)
+
+
+def make_oracle(w, seed):
+    st = synth.initial_state(w, seed)
+    o = OracleState.from_synth(st, H=w.H, G=w.G, d=w.d, R=w.R, N=w.N, C=w.C)
+    return o, st
+
+
+def run_decode(o, w, seed, step, wg, layer=0, compute_out=True, **override):
+    x = synth.step_inputs(w, seed, layer, step)
+    x.update(override)
+    out = o.decode_step(layer, x["q"], x["k"], x["v"], x["ck"], x["cv"], x["cs"], wg[layer],
+                        compute_out=compute_out)
+    if o.pend_n[layer] == o.C:
+        o.admit(layer)
+    return out, x
+
+
+def f32(h):
+    return synth.bf16_to_f32(h).astype(np.float64)
+
+
+# --------------------------------------------------------------- the pages
+
+
+def read_golden_table(name):
+    vals = {}
+    with open(os.path.join(GOLDEN, name)) as fh:
+        for line in fh:
+            line = line.split("#", 1)[0].strip()
+            if line:
+                k, v = line.split()
+                vals[k] = float(v)
+    return vals
+
+
+def test_geometry_from_memory_table():
+    """The page's MiB table fixes the record size: bf16 K and V of head
+    dimension 256 in 4 groups of 8 layers, with 1,024 anchors, 256
+    pending slots and a 1,023-slot ring."""
+    g = read_golden_table("memory_table.txt")
+    w = synth.WORKLOADS["stack_b512"]
+    mib = 2.0 ** 20
+    rec = 2 * w.d * 2  # K and V, bf16
+    units = w.L * w.G
+    assert (w.L, w.G) == (g["rma_layers"], g["kv_groups"])
+    assert w.R + 1 == g["local_window"] and w.R == g["ring_slots"]
+    assert w.N == g["anchors_per_group"] and w.C == g["pending_positions"] == g["commit_interval"]
+    assert round(units * w.N * rec / mib, 2) == g["committed_anchors_mib"]
+    assert round(units * w.C * rec / mib, 2) == g["pending_candidates_mib"]
+    assert round(units * w.R * rec / mib, 2) == g["local_window_kv_mib"]
+    total = units * (w.N + w.C + w.R) * rec / mib
+    assert round(total) == g["attention_kv_mib"]
+    assert round(100 * (1 - g["attention_kv_mib"] / g["qwen_256k_mib"]), 1) == g["reduction_percent"]
+    # the head dimension is the only one consistent with 32.00 MiB
+    assert g["committed_anchors_mib"] * mib / (units * w.N * 2 * 2) == 256
+
+
+# ----------------------------------------------------------------- rounding
+
+
+def test_round_bf16_exact():
+    r = oracle.round_bf16
+    cases = [
+        (1.0, 0x3F80),
+        (1.0 + 2.0 ** -8, 0x3F80),                # tie -> even (down)
+        (1.0 + 3 * 2.0 ** -8, 0x3F82),            # tie -> even (up)
+        (1.0 + 2.0 ** -8 + 2.0 ** -30, 0x3F81),   # above the tie: rounding to
+                                                  # float first would lose it
+        (-(1.0 + 2.0 ** -8 + 2.0 ** -30), 0xBF81),
+        (0.0, 0x0000),
+        (-0.0, 0x8000),
+        (3.0e38 * 10, 0x7F80),                    # overflow to inf
+        (float("inf"), 0x7F80),
+        (2.0 ** -133, 0x0001),                    # smallest bf16 subnormal
+    ]
+    got = r(np.array([c[0] for c in cases]))
+    assert [int(x) for x in got] == [c[1] for c in cases]
+    assert int(r(np.array([float("nan")]))[0]) & 0x7FFF > 0x7F80
+
+
+# ----------------------------------------------------------- brute force
+
+
+@pytest.mark.parametrize("t0,bank_n,steps", [(0, 0, 40), (14, 4, 30), (16, 3, 25), (8, 1, 20)])
+def test_oracle_equals_full_history_bruteforce(t0, bank_n, steps):
+    w = tiny(t0=t0, bank_n=bank_n, steps=steps, ring_full=t0 > 0)
+    seed = 7
+    o, st = make_oracle(w, seed)
+    wg = synth.gate_weights(w, seed)
+    bfs = []
+    for b in range(w.B):
+        bfs.append(BruteForce(w.H, w.G, w.d, w.R, w.N, w.C, w.d ** -0.5, t0,
+                              st["ring_k"][0, b], st["ring_v"][0, b], st["bank_k"][0, b],
+                              st["bank_v"][0, b], st["bscore"][0, b], st["bsrc"][0, b],
+                              st["bank_n"][0, b]))
+    for s in range(steps):
+        out, x = run_decode(o, w, seed, s, wg)
+        for b in range(w.B):
+            ref = bfs[b].step(x["q"][b], x["k"][b], x["v"][b], x["ck"][b], x["cv"][b],
+                              x["cs"][b], wg[0])
+            np.testing.assert_allclose(out[b], ref, rtol=0, atol=1e-12)
+            for g in range(w.G):
+                n = o.bank_n[0, b, g]
+                assert sorted(o.bsrc[0, b, g, :n].tolist()) == bfs[b].bank_positions(g)
+    assert o.t[0] == t0 + steps
+
+
+def test_ring_holds_exactly_the_last_positions():
+    w = tiny(steps=3 * 7 + 5)
+    seed = 3
+    o, _ = make_oracle(w, seed)
+    wg = synth.gate_weights(w, seed)
+    ks = []
+    for s in range(w.steps):
+        _, x = run_decode(o, w, seed, s, wg, compute_out=False)
+        ks.append(x["k"])
+    T = w.steps
+    for p in range(T - w.R, T):
+        np.testing.assert_array_equal(o.ring_k[0, :, :, p % w.R], ks[p])
+
+
+# --------------------------------------------------- library routine (SDPA)
+
+
+def _sdpa(q, K, V):
+    """torch's scaled_dot_product_attention (default scale 1/sqrt(d)) in
+    float64 for one query vector over a key list."""
+    qt = torch.from_numpy(q)[None, None, None, :]
+    Kt = torch.from_numpy(K)[None, None]
+    Vt = torch.from_numpy(V)[None, None]
+    return torch.nn.functional.scaled_dot_product_attention(qt, Kt, Vt)[0, 0, 0].numpy()
+
+
+@pytest.mark.parametrize("gate", ["zero", "random"])
+def test_oracle_equals_sdpa_reads(gate):
+    """At the real geometry, each head's output is SDPA over the window
+    (ring positions t-1023..t-1 plus the current token) plus the gate times
+    SDPA over the committed bank."""
+    w = synth.WORKLOADS["sharp_b1"].with_(bank_n=700)
+    seed = 11
+    o, st = make_oracle(w, seed)
+    wg = synth.gate_weights(w, seed)
+    if gate == "zero":
+        wg[:] = 0
+    x = synth.step_inputs(w, seed, 0, 0)
+    out = o.decode_step(0, x["q"], x["k"], x["v"], x["ck"], x["cv"], x["cs"], wg[0])
+    t = w.t0
+    hpg = w.H // w.G
+    for h in range(0, w.H, 3):
+        g = h // hpg
+        pos = np.arange(t - w.R, t)
+        K = np.concatenate([f32(st["ring_k"][0, 0, g, pos % w.R]), f32(x["k"][0, g])[None]])
+        V = np.concatenate([f32(st["ring_v"][0, 0, g, pos % w.R]), f32(x["v"][0, g])[None]])
+        q = f32(x["q"][0, h])
+        loc = _sdpa(q, K, V)
+        n = w.bank_n
+        anc = _sdpa(q, f32(st["bank_k"][0, 0, g, :n]), f32(st["bank_v"][0, 0, g, :n]))
+        gv = math.tanh(float(q @ wg[0, h].astype(np.float64)))
+        np.testing.assert_allclose(out[0, h], loc + gv * anc, rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------- closed forms
+
+
+def test_constant_values_give_one_plus_gate():
+    """V == c everywhere: each read returns c, so out = c (1 + tanh(q.w_g));
+    with an empty bank out = c."""
+    for bank_n in (1024, 0):
+        w = synth.WORKLOADS["sharp_b1"].with_(bank_n=bank_n)
+        seed = 5
+        o, _ = make_oracle(w, seed)
+        c = np.uint16(0x3EC0)  # 0.375
+        o.ring_v[...] = c
+        o.bank_v[...] = c
+        wg = synth.gate_weights(w, seed)
+        x = synth.step_inputs(w, seed, 0, 0)
+        x["v"][...] = c
+        out = o.decode_step(0, x["q"], x["k"], x["v"], x["ck"], x["cv"], x["cs"], wg[0])
+        qf = f32(x["q"][0])
+        gate = np.tanh((qf * wg[0].astype(np.float64)).sum(-1)) if bank_n else np.zeros(w.H)
+        np.testing.assert_allclose(out[0], np.broadcast_to(0.375 * (1 + gate)[:, None], out[0].shape),
+                                   rtol=1e-12, atol=0)
+
+
+def test_identical_keys_give_mean_of_values():
+    w = synth.WORKLOADS["layer_b1"].with_(bank_n=300)
+    seed = 9
+    o, st = make_oracle(w, seed)
+    kk = o.ring_k[0, 0, 0, 0].copy()
+    o.ring_k[...] = kk
+    o.bank_k[...] = kk
+    wg = synth.gate_weights(w, seed)
+    x = synth.step_inputs(w, seed, 0, 0)
+    x["k"][...] = kk
+    out = o.decode_step(0, x["q"], x["k"], x["v"], x["ck"], x["cv"], x["cs"], wg[0])
+    for g in range(w.G):
+        mloc = np.concatenate([f32(st["ring_v"][0, 0, g]), f32(x["v"][0, g])[None]]).mean(0)
+        manc = f32(st["bank_v"][0, 0, g, :300]).mean(0)
+        for h in range(4 * g, 4 * g + 4):
+            gv = math.tanh(float(f32(x["q"][0, h]) @ wg[0, h].astype(np.float64)))
+            np.testing.assert_allclose(out[0, h], mloc + gv * manc, rtol=0, atol=1e-15)
+
+
+def test_planted_key_dominates_local_read():
+    """A ring key equal to lambda*q takes (almost) all the softmax weight:
+    the local read returns its value (gate zero)."""
+    w = synth.WORKLOADS["sharp_b1"]
+    seed = 13
+    o, st = make_oracle(w, seed)
+    wg = np.zeros((1, w.H, w.d), np.float32)
+    x = synth.step_inputs(w, seed, 0, 0)
+    h, g = 5, 1
+    slot = 123
+    o.ring_k[0, 0, g, slot] = synth.bf16_bits(8.0 * synth.bf16_to_f32(x["q"][0, h]))
+    out = o.decode_step(0, x["q"], x["k"], x["v"], x["ck"], x["cv"], x["cs"], wg[0])
+    np.testing.assert_allclose(out[0, h], f32(st["ring_v"][0, 0, g, slot]), rtol=0, atol=1e-6)
+
+
+# ----------------------------------------------------------- invariances
+
+
+def test_slot_permutations_do_not_change_outputs():
+    w = synth.WORKLOADS["layer_b1"].with_(bank_n=1000)
+    seed = 17
+    o, _ = make_oracle(w, seed)
+    wg = synth.gate_weights(w, seed)
+    x = synth.step_inputs(w, seed, 0, 0)
+    ref = o.clone().decode_step(0, x["q"], x["k"], x["v"], x["ck"], x["cv"], x["cs"], wg[0])
+    rng = np.random.default_rng(0)
+    pr = rng.permutation(w.R)   # t0 >= R: every ring slot is in the window
+    pb = rng.permutation(1000)
+    p = o.clone()
+    p.ring_k[...] = p.ring_k[:, :, :, pr]
+    p.ring_v[...] = p.ring_v[:, :, :, pr]
+    for a in ("bank_k", "bank_v", "bscore", "bsrc"):
+        arr = getattr(p, a)
+        arr[:, :, :, :1000] = arr[:, :, :, pb]
+    out = p.decode_step(0, x["q"], x["k"], x["v"], x["ck"], x["cv"], x["cs"], wg[0])
+    np.testing.assert_allclose(out, ref, rtol=1e-12, atol=1e-16)
+
+
+def test_sequences_are_independent():
+    w = synth.WORKLOADS["layer_b1"].with_(B=3, bank_n=512)
+    seed = 19
+    o, _ = make_oracle(w, seed)
+    wg = synth.gate_weights(w, seed)
+    x = synth.step_inputs(w, seed, 0, 0)
+    ref = o.clone().decode_step(0, x["q"], x["k"], x["v"], x["ck"], x["cv"], x["cs"], wg[0])
+    perm = [2, 0, 1]
+    p = o.clone()
+    for a in ("ring_k", "ring_v", "bank_k", "bank_v", "bscore", "bsrc", "bank_n"):
+        getattr(p, a)[...] = getattr(p, a)[:, perm]
+    xp = {k: v[perm] for k, v in x.items()}
+    out = p.decode_step(0, xp["q"], xp["k"], xp["v"], xp["ck"], xp["cv"], xp["cs"], wg[0])
+    np.testing.assert_array_equal(out, ref[perm])
+
+
+# ------------------------------------------------------------------ admit
+
+
+def parse_admit_cases():
+    cases, cur = [], None
+    with open(os.path.join(GOLDEN, "admit_cases.txt")) as fh:
+        for line in fh:
+            line = line.split("#", 1)[0].strip()
+            if not line:
+                continue
+            key, *rest = line.split()
+            if key == "case":
+                cur = {"name": rest[0]}
+                cases.append(cur)
+            else:
+                cur[key] = rest
+    return cases
+
+
+def _admit_tiny_state(n, bscore, pscore, N=4, C=2, d=2):
+    o = OracleState(L=1, B=1, H=1, G=1, d=d, R=3, N=N, C=C)
+    for i in range(n):
+        o.bank_k[0, 0, 0, i] = 0x1000 + i   # record "A<i>"
+        o.bank_v[0, 0, 0, i] = 0x2000 + i
+        o.bscore[0, 0, 0, i] = bscore[i]
+        o.bsrc[0, 0, 0, i] = 10 * i
+    o.bank_n[...] = n
+    for j in range(C):
+        o.pend_k[0, 0, 0, j] = 0x3000 + j    # record "C<j>"
+        o.pend_v[0, 0, 0, j] = 0x4000 + j
+        o.pscore[0, 0, 0, j] = pscore[j]
+    o.t[0] = 100 + C
+    o.pend_n[0] = C
+    return o
+
+
+def _record_name(o, i):
+    k, v = int(o.bank_k[0, 0, 0, i, 0]), int(o.bank_v[0, 0, 0, i, 0])
+    if k >= 0x3000:
+        assert v == 0x4000 + (k - 0x3000)
+        return f"C{k - 0x3000}"
+    if k >= 0x1000:
+        assert v == 0x2000 + (k - 0x1000)
+        return f"A{k - 0x1000}"
+    return "-"
+
+
+@pytest.mark.parametrize("case", parse_admit_cases(), ids=lambda c: c["name"])
+def test_admit_hand_worked_cases(case):
+    n = int(case["n"][0])
+    bscore = [float(x) for x in case.get("bscore", [])]
+    pscore = [float(x) for x in case["pscore"]]
+    o = _admit_tiny_state(n, bscore, pscore)
+    moved = o.admit(0)
+    nn = int(case["n_after"][0])
+    assert o.bank_n[0, 0, 0] == nn
+    assert [_record_name(o, i) for i in range(4)] == case["records_after"]
+    exp_sc = np.array([float(x) for x in case["bscore_after"]], np.float32)
+    np.testing.assert_array_equal(o.bscore[0, 0, 0, :nn].view(np.uint32), exp_sc.view(np.uint32))
+    assert o.bsrc[0, 0, 0, :nn].tolist() == [int(x) for x in case["bsrc_after"]]
+    assert moved[0, 0] == sum(r.startswith("C") for r in case["records_after"])
+    assert o.pend_n[0] == 0
+
+
+def _kept_set_lexsort(bscore, pscore, N):
+    n, C = len(bscore), len(pscore)
+    score = np.concatenate([bscore, pscore]).astype(np.float64)
+    gidx = np.concatenate([np.arange(n), N + np.arange(C)])
+    # numpy puts NaN last when sorting ascending, so -score sorts NaN below -inf
+    order = np.lexsort((gidx, -score))
+    K = min(N, n + C)
+    return set(gidx[order[:K]].tolist())
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_admit_selection_equals_lexsort_with_heavy_ties(seed):
+    rng = np.random.default_rng(seed)
+    N, C = 64, 16
+    for n in (0, 5, 48, 50, 63, 64):
+        levels = np.array([0.0, -0.0, 1.0, 2.0, -np.inf, np.inf, np.nan], np.float32)
+        bs = levels[rng.integers(0, len(levels), n)] if n else np.zeros(0, np.float32)
+        ps = levels[rng.integers(0, len(levels), C)]
+        o = OracleState(L=1, B=1, H=1, G=1, d=2, R=3, N=N, C=C)
+        o.bscore[0, 0, 0, :n] = bs
+        o.bsrc[0, 0, 0, :n] = np.arange(n)
+        o.bank_n[...] = n
+        o.pscore[0, 0, 0] = ps
+        o.t[0] = 1000 * C
+        o.pend_n[0] = C
+        o.admit(0)
+        K = int(o.bank_n[0, 0, 0])
+        assert K == min(N, n + C)
+        block = 1000 * C - C
+        got = set()
+        for s in o.bsrc[0, 0, 0, :K].tolist():
+            got.add(s if s < block else N + (s - block))
+        assert got == _kept_set_lexsort(bs, ps, N)
+
+
+def test_admit_compaction_invariants_full_geometry():
+    """Full geometry (N=1024, C=256), scores on 64 levels: retained anchors
+    keep their slots bit for bit, admitted candidates fill the evicted
+    slots in ascending slot order and pending order, the bank stays a dense
+    prefix of size min(N, n + C), and the kept set is numpy.lexsort's."""
+    w = synth.WORKLOADS["admit_b512"].with_(B=2, L=1)
+    seed = 23
+    for bank_n in (1024, 900, 0):
+        ww = w.with_(bank_n=bank_n)
+        st = synth.initial_state(ww, seed)
+        pf = synth.pending_fill(ww, seed)
+        o = OracleState.from_synth(st)
+        o.pend_k[...] = pf["pend_k"]
+        o.pend_v[...] = pf["pend_v"]
+        o.pscore[...] = pf["pscore"]
+        o.pend_n[0] = w.C
+        before = o.clone()
+        moved = o.admit(0)
+        block = int(o.t[0]) - w.C
+        for b in range(w.B):
+            for g in range(w.G):
+                n = bank_n
+                K = min(w.N, n + w.C)
+                assert o.bank_n[0, b, g] == K
+                kept = _kept_set_lexsort(before.bscore[0, b, g, :n], before.pscore[0, b, g], w.N)
+                anchors_kept = sorted(i for i in kept if i < w.N)
+                cands = sorted(i - w.N for i in kept if i >= w.N)
+                evicted = sorted(set(range(n)) - set(anchors_kept))
+                dst = evicted + list(range(n, K))
+                assert len(dst) == len(cands) == moved[b, g]
+                for i in anchors_kept:
+                    np.testing.assert_array_equal(o.bank_k[0, b, g, i], before.bank_k[0, b, g, i])
+                    np.testing.assert_array_equal(o.bank_v[0, b, g, i], before.bank_v[0, b, g, i])
+                    assert o.bsrc[0, b, g, i] == before.bsrc[0, b, g, i]
+                for slot, j in zip(dst, cands):
+                    np.testing.assert_array_equal(o.bank_k[0, b, g, slot], before.pend_k[0, b, g, j])
+                    np.testing.assert_array_equal(o.bank_v[0, b, g, slot], before.pend_v[0, b, g, j])
+                    assert o.bscore[0, b, g, slot] == before.pscore[0, b, g, j]
+                    assert o.bsrc[0, b, g, slot] == block + j
+                # untouched beyond the prefix
+                np.testing.assert_array_equal(o.bank_k[0, b, g, K:], before.bank_k[0, b, g, K:])
+
+
+# -------------------------------------------------------------- visibility
+
+
+def test_new_anchor_invisible_until_next_block():
+    """Reads use the committed bank; an admitted record becomes visible in
+    the next block (model card, "How Rock Memory Anchors work").  A planted
+    candidate with a huge score and a key aligned with a later query leaves
+    every output of its own block bit-identical, and changes the first
+    output of the next block."""
+    w = synth.WORKLOADS["layer_b1"]
+    seed = 29
+    base, _ = make_oracle(w, seed)
+    plant = base.clone()
+    wg = synth.gate_weights(w, seed)
+    xf = synth.step_inputs(w, seed, 0, w.C)  # first query of the next block
+    h, g = 6, 1
+    ck_plant = synth.bf16_bits(1024.0 * synth.bf16_to_f32(xf["q"][0, h]))
+    for s in range(w.C):
+        x = synth.step_inputs(w, seed, 0, s)
+        a = base.decode_step(0, x["q"], x["k"], x["v"], x["ck"], x["cv"], x["cs"], wg[0])
+        if s == 3:
+            x["ck"][0, g] = ck_plant
+            x["cs"][0, g] = 1e30
+        b = plant.decode_step(0, x["q"], x["k"], x["v"], x["ck"], x["cv"], x["cs"], wg[0])
+        np.testing.assert_array_equal(a, b)
+    base.admit(0)
+    plant.admit(0)
+    assert (plant.bsrc[0, 0, g] == w.t0 + 3).sum() == 1
+    x = synth.step_inputs(w, seed, 0, w.C)
+    a = base.decode_step(0, x["q"], x["k"], x["v"], x["ck"], x["cv"], x["cs"], wg[0])
+    b = plant.decode_step(0, x["q"], x["k"], x["v"], x["ck"], x["cv"], x["cs"], wg[0])
+    assert np.abs(a[0, h] - b[0, h]).max() > 1e-3
+    # other groups never see it
+    np.testing.assert_array_equal(a[0, :4], b[0, :4])
+
+
+# ------------------------------------------------------------ error codes
+
+
+def test_oracle_status_codes():
+    w = tiny(t0=0, bank_n=0)
+    seed = 1
+    o, _ = make_oracle(w, seed)
+    wg = synth.gate_weights(w, seed)
+    with pytest.raises(OracleError) as e:
+        o.admit(0)
+    assert e.value.code == oracle.ORC_E_NOT_BOUNDARY
+    for s in range(w.C):
+        x = synth.step_inputs(w, seed, 0, s)
+        o.decode_step(0, x["q"], x["k"], x["v"], x["ck"], x["cv"], x["cs"], wg[0])
+    x = synth.step_inputs(w, seed, 0, w.C)
+    with pytest.raises(OracleError) as e:
+        o.decode_step(0, x["q"], x["k"], x["v"], x["ck"], x["cv"], x["cs"], wg[0])
+    assert e.value.code == oracle.ORC_E_PENDING_FULL
+    o.admit(0)
+    o.decode_step(0, x["q"], x["k"], x["v"], x["ck"], x["cv"], x["cs"], wg[0])
+    xb = synth.block_inputs(w, seed, 0, w.C + 1, 1)
+    with pytest.raises(OracleError) as e:
+        o.prefill_block(0, xb["q"], xb["k"], xb["v"], xb["ck"], xb["cv"], xb["cs"], wg[0])
+    assert e.value.code == oracle.ORC_E_NOT_BOUNDARY
+
+
+def test_synth_slices_are_consistent():
+    w = synth.WORKLOADS["layer_b1"].with_(B=4)
+    full = synth.initial_state(w, 3)
+    one = synth.initial_state(w, 3, batch=[2])
+    for k in ("ring_k", "bank_v", "bscore", "bsrc"):
+        np.testing.assert_array_equal(full[k][:, 2], one[k][:, 0])
+    a = synth.step_inputs(w, 3, 0, 17)
+    b = synth.step_inputs(w, 3, 0, 17, batch=[1, 3])
+    np.testing.assert_array_equal(a["q"][[1, 3]], b["q"])
