@@ -1,0 +1,284 @@
+#!/usr/bin/env python3
+"""RMA-layer decode benchmark on one MI355X.
+
+One step = one decode token through the whole RMA stack: for each of the 8
+layers, the local-ring read, the anchor-bank read, the signed gate, the
+ring write and the pending append; plus, every 256 tokens, the admit of
+all layers.  Workload: 512 sequences, state pre-filled as after a 32K
+prompt (ring and bank full), synthetic N(0,1)/16 bf16 inputs from a
+device-resident pool of 16 input sets per layer (the pool changes none of
+the state traffic).  Prints ONE JSON line.
+
+    python bench.py [--gpus 1] [--steps 1024] [--warmup 16]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0      # MI355X HBM3E, published
+POOL = 16                  # input sets per layer kept on the device
+
+# Algorithmic bytes of one (sequence, layer, group) decode step.
+#   read : ring K/V 1,023 x 1,024 B, bank K/V 1,024 x 1,024 B,
+#          q of 4 heads 2,048 B, current K/V 1,024 B, candidate K/V 1,024 B
+#          + score 4 B
+#   write: out of 4 heads 2,048 B, ring slot 1,024 B, pending slot 1,024 B
+#          + score 4 B
+RING_BYTES = 1023 * 1024
+BANK_BYTES = 1024 * 1024
+UNIT_READ = RING_BYTES + BANK_BYTES + 2048 + 1024 + 1028
+UNIT_WRITE = 2048 + 1024 + 1028
+UNIT_BYTES = UNIT_READ + UNIT_WRITE          # 2,104,328
+
+
+def kernel_sources_sha() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "bounded_memory_decode_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+def make_state(w, seed, device):
+    """RMA state of workload `w` on `device`, filled with seeded synthetic
+    records drawn on the device (torch generator per tensor and layer)."""
+    import torch
+    from bounded_memory_decode_amd import rma, synth
+    cfg = rma.config_default(layers=w.L, q_heads=w.H, kv_groups=w.G, head_dim=w.d,
+                             window=w.R + 1, bank_cap=w.N, commit=w.C, scale=w.d ** -0.5)
+    S = rma.State(cfg, w.B, device, start_pos=w.t0, bank_n=w.bank_n)
+    filled = min(w.t0, w.R)
+    for l in range(w.L):
+        for name, kind, slots in (("ring_k", 1, w.R), ("ring_v", 2, w.R),
+                                  ("bank_k", 3, w.N), ("bank_v", 4, w.N)):
+            x = synth.torch_normal_bf16((1, w.B, w.G, slots, w.d), w.qkv_std, seed, device,
+                                        (w.wid, synth.KIND[name], l))
+            if name.startswith("ring") and filled < w.R:
+                x[:, :, :, filled:] = 0
+            if name.startswith("bank") and w.bank_n < w.N:
+                x[:, :, :, w.bank_n:] = 0
+            S.write(name, x.view(torch.int16), layers=slice(l, l + 1))
+            del x
+        sc = synth.torch_scores((1, w.B, w.G, w.N), w, seed, device, (w.wid, synth.KIND["bscore"], l))
+        sc[..., w.bank_n:] = 0
+        S.write("bscore", sc, layers=slice(l, l + 1))
+        src = torch.arange(w.N, dtype=torch.int32, device=device).expand(1, w.B, w.G, w.N)
+        S.write("bsrc", src, layers=slice(l, l + 1))
+    zero16 = torch.zeros((), dtype=torch.int16, device=device)
+    S.region_view("pend_k").fill_(zero16)
+    S.region_view("pend_v").fill_(zero16)
+    S.region_view("pscore").zero_()
+    torch.cuda.synchronize(device)
+    return S
+
+
+def make_pool(w, seed, device, pool=POOL):
+    """Per layer, `pool` sets of step inputs and the gate weights."""
+    import torch
+    from bounded_memory_decode_amd import synth
+    sets = []
+    for l in range(w.L):
+        per = []
+        for p in range(pool):
+            key = lambda kind: (w.wid, synth.KIND[kind], l, p, 1)
+            per.append({
+                "q": synth.torch_normal_bf16((w.B, w.H, w.d), w.qkv_std, seed, device, key("q")),
+                "k": synth.torch_normal_bf16((w.B, w.G, w.d), w.qkv_std, seed, device, key("k")),
+                "v": synth.torch_normal_bf16((w.B, w.G, w.d), w.qkv_std, seed, device, key("v")),
+                "ck": synth.torch_normal_bf16((w.B, w.G, w.d), w.qkv_std, seed, device, key("ck")),
+                "cv": synth.torch_normal_bf16((w.B, w.G, w.d), w.qkv_std, seed, device, key("cv")),
+                "cs": synth.torch_scores((w.B, w.G), w, seed, device, key("cs")),
+            })
+        sets.append(per)
+    g = torch.Generator(device=device)
+    g.manual_seed(seed * 7919 + w.wid)
+    wg = (torch.randn((w.L, w.H, w.d), generator=g, device=device) * w.w_std).contiguous()
+    outs = [torch.empty((w.B, w.H, w.d), dtype=torch.bfloat16, device=device) for _ in range(w.L)]
+    return sets, wg, outs
+
+
+def run_step(S, sets, wg, outs, step, events=None):
+    """One token through all layers (+ admit at the block end)."""
+    L = S.cfg.layers
+    for l in range(L):
+        x = sets[l][step % len(sets[l])]
+        if events is not None:
+            events[l][0].record()
+        S.decode_step(l, x["q"], x["k"], x["v"], x["ck"], x["cv"], x["cs"], wg[l], outs[l])
+        if events is not None:
+            events[l][1].record()
+    if S.pend_n[0] == S.cfg.commit:
+        S.admit(-1)
+        return True
+    return False
+
+
+def cpu_baseline(S, w, sets, wg, sample_b: int, seed: int):
+    """The oracle, timed on the host cores on a bounded sample: `sample_b`
+    sequences of the same state, one token through all layers."""
+    import numpy as np
+    import torch
+    import oracle
+    from oracle import OracleState
+    b_idx = list(range(sample_b))
+    o = OracleState(L=w.L, B=sample_b, H=w.H, G=w.G, d=w.d, R=w.R, N=w.N, C=w.C,
+                    scale=float(S.cfg.scale))
+    for name in ("ring_k", "ring_v", "bank_k", "bank_v", "pend_k", "pend_v"):
+        getattr(o, name)[...] = S.read(name, batch=b_idx).cpu().numpy().view(np.uint16)
+    for name in ("bscore", "bsrc", "pscore", "bank_n"):
+        getattr(o, name)[...] = S.read(name, batch=b_idx).cpu().numpy()
+    o.t[:] = S.t[:w.L]
+    o.pend_n[:] = S.pend_n[:w.L]
+    ins = []
+    for l in range(w.L):
+        x = sets[l][0]
+        ins.append({k: (v[:sample_b].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+                        if v.dtype == torch.bfloat16 else v[:sample_b].cpu().numpy())
+                    for k, v in x.items()})
+    wgn = wg.cpu().numpy()
+    t0 = time.perf_counter()
+    for l in range(w.L):
+        x = ins[l]
+        o.decode_step(l, x["q"], x["k"], x["v"], x["ck"], x["cv"], x["cs"], wgn[l])
+    dt = time.perf_counter() - t0
+    cores = oracle.num_threads()
+    return {"value": sample_b / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{sample_b} of {w.B} sequences, 1 token through all {w.L} layers "
+                      f"(decode + ring write + pending append), {dt:.2f} s wall on {cores} threads"}
+
+
+def read_traffic(sha: str):
+    """HBM traffic per decode launch from the committed rocprofv3 counter
+    summary, if it was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "decode_stack_b512_counters.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.split("=", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_sources_sha") != sha:
+        return None
+    try:
+        return float(kv["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1024)
+    ap.add_argument("--warmup", type=int, default=16)
+    ap.add_argument("--workload", default="stack_b512")
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--cpu-sample", type=int, default=32,
+                    help="sequences in the CPU-oracle sample (0: skip)")
+    ap.add_argument("--quiet", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: the RMA state of a sequence never leaves its GPU, "
+              f"so --gpus {args.gpus} is not a supported configuration (run with --gpus 1).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from bounded_memory_decode_amd import rma, synth
+    rma.lib()  # fail loudly if the HIP library is missing
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    device = torch.device("cuda", 0)
+    torch.cuda.set_device(device)
+    w = synth.WORKLOADS[args.workload]
+
+    def say(m):
+        if not args.quiet:
+            print(m, file=sys.stderr, flush=True)
+
+    say(f"[bench] building state: {w.name} B={w.B} L={w.L}")
+    S = make_state(w, args.seed, device)
+    sets, wg, outs = make_pool(w, args.seed, device)
+    say(f"[bench] state {S.buf.numel() / 2**30:.2f} GiB; warmup {args.warmup} steps")
+    for s in range(args.warmup):
+        run_step(S, sets, wg, outs, s)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(w.L)] for _ in range(K)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    say(f"[bench] timing {K} steps")
+    admits = 0
+    torch.cuda.synchronize()
+    t_wall = time.perf_counter()
+    start.record()
+    for s in range(K):
+        admits += run_step(S, sets, wg, outs, args.warmup + s, ev[s])
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    ms_total = start.elapsed_time(stop)
+    ms_step = ms_total / K
+    dec_ms = [ev[s][l][0].elapsed_time(ev[s][l][1]) for s in range(K) for l in range(w.L)]
+    dec_avg_ms = sum(dec_ms) / len(dec_ms)
+
+    units = w.B * w.G
+    launch_bytes = units * UNIT_BYTES
+    step_bytes = launch_bytes * w.L
+    achieved = launch_bytes / (dec_avg_ms * 1e-3) / 1e9
+    tokens_s = w.B * K / (ms_total * 1e-3)
+    sha = kernel_sources_sha()
+    traffic = read_traffic(sha)
+
+    result = {
+        "metric": "RMA-layer decode tokens/s at batch 512x8 layers; achieved HBM GB/s vs peak",
+        "value": round(tokens_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{w.name}: RMA stack, {w.L} layers x batch {w.B}, 16 q heads, "
+                               f"4 KV groups, head_dim 256, ring 1023 + current, bank 1024, "
+                               f"commit 256, start position {w.t0} (ring and bank full)",
+                   "batch": w.B, "layers": w.L, "admit_rounds": admits,
+                   "step_bytes_algorithmic": step_bytes,
+                   "step_GBps": round(step_bytes / (ms_step * 1e-3) / 1e9, 1)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": traffic,
+                     "kernel": "rma_decode_step (attention + combine launches of one layer)",
+                     "avg_launch_ms": round(dec_avg_ms, 5),
+                     "bytes_per_launch": launch_bytes,
+                     "kernel_sources_sha": sha},
+        "cpu_baseline": None,
+    }
+    say(f"[bench] {tokens_s:,.0f} tok/s, {ms_step:.3f} ms/step, decode launch {dec_avg_ms*1e3:.1f} us "
+        f"= {achieved:,.0f} GB/s ({100*achieved/HBM_PEAK_GBS:.1f}% of peak); wall {wall:.2f} s")
+    if args.cpu_sample > 0:
+        say(f"[bench] CPU oracle on {args.cpu_sample} sequences")
+        result["cpu_baseline"] = cpu_baseline(S, w, sets, wg, args.cpu_sample, args.seed)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,409 @@
+// Decode step of the RMA layer on gfx950: split-K attention over the local
+// ring and the committed anchor bank, then a combine kernel that merges the
+// split partials, folds in the current token, applies the signed gate and
+// performs the ring write and the pending append.
+//
+// Semantics: EdgeRock model card (ModelScope), "How Rock Memory Anchors
+// work" (local window of 1,024 positions, committed-bank reads, signed gate)
+// and the persistent-history table note (ring of 1,023 preceding positions
+// plus the current token); ai-primer "EdgeRock-4B fixes its attention KV
+// cache at 72 MiB", three-operation list (Write, Retrieve).  Gate reading:
+// out = o_local + tanh(q . w_g) * o_anchor.
+//
+// Data layout (owned by this library, see include/rma.h): K planes are
+// stored in 16-byte chunks, chunk-major, so that a wave loading chunk c of
+// 64 consecutive slots reads 1 KiB of contiguous memory with one key per
+// lane; V planes are row-major so that a half-wave loads one 512-byte row.
+// Neither read needs an LDS transpose.
+#include "rma_kernels.h"
+
+namespace rma {
+namespace {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
+                                          __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+__device__ __forceinline__ float bf_lo(uint32_t x) { return __uint_as_float(x << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
+__device__ __forceinline__ float bf1(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// A wave-uniform read of memory no kernel of this launch writes, through
+// the constant address space: a scalar load, so it never waits on the
+// vector-memory counter (and never drains the load pipeline).
+__device__ __forceinline__ int32_t scalar_load(const int32_t* p) {
+  return *(const __attribute__((address_space(4))) int32_t*)p;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+// fp32 -> bf16, round to nearest, ties to even.
+__device__ __forceinline__ uint16_t to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+constexpr int kWaves = 4;
+
+// One work item = one part (a contiguous range of 64-key tiles) of one
+// read (ring or bank) of one (sequence, group) unit.  Items are numbered
+// unit-major: item = u * S + r, r < splits_ring for ring parts.
+struct Item {
+  const uint4* K4;  // K plane of the unit (chunk-major, `slots` slots)
+  const uint4* V4;  // V rows of the unit
+  const uint4* q4;  // the unit's 4 query rows (2 KiB)
+  int slots, count, ta, tb;
+};
+
+__device__ __forceinline__ Item item_info(const DecodeArgs& a, int item) {
+  const int S = a.splits_ring + a.splits_bank;
+  const int u = item / S, r = item - u * S;
+  const int b = u / a.G, g = u - b * a.G;
+  Item it;
+  int tiles, t0;
+  if (r < a.splits_ring) {
+    it.count = a.ring_count;
+    it.slots = a.R;
+    it.K4 = reinterpret_cast<const uint4*>(a.ring_k + (size_t)u * a.R * kD);
+    it.V4 = reinterpret_cast<const uint4*>(a.ring_v + (size_t)u * a.R * kD);
+    tiles = a.tiles_ring;
+    t0 = r * tiles;
+  } else {
+    it.count = scalar_load(a.bank_n + u);
+    it.slots = a.N;
+    it.K4 = reinterpret_cast<const uint4*>(a.bank_k + (size_t)u * a.N * kD);
+    it.V4 = reinterpret_cast<const uint4*>(a.bank_v + (size_t)u * a.N * kD);
+    tiles = a.tiles_bank;
+    t0 = (r - a.splits_ring) * tiles;
+  }
+  it.q4 = reinterpret_cast<const uint4*>(a.q + (size_t)b * a.q_bs + (size_t)g * kHpg * kD);
+  const int ntiles = (it.count + kTile - 1) / kTile;
+  int t1 = t0 + tiles;
+  t1 = t1 < ntiles ? t1 : ntiles;
+  it.ta = t0 < t1 ? t0 : t1;
+  it.tb = t1;
+  return it;
+}
+
+// grid: persistent, a few workgroups per CU; block: 256 = 4 independent
+// waves.  Wave gw takes items gw, gw + W, gw + 2W, ... (W = all waves).
+// Per tile i of an item, in issue order:
+//   V(i) loads -> QK(i) on K(i) already in registers -> softmax ->
+//   K(i+1) loads (or the next item's first tile and query) -> P.V(i).
+// The vector-memory counter retires loads in order, so QK(i) never waits
+// for V(i) and P.V(i) never waits for K(i+1); a wave keeps 32-66 16-byte
+// loads in flight across tile and item boundaries.  The output of an item
+// is its partial (m, l, o[4][256]) in the log2 domain, merged by the
+// combine kernel.  No workgroup barrier: each wave owns its LDS slices.
+__global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a, int items) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int W = gridDim.x * kWaves;
+  int item = blockIdx.x * kWaves + wave;
+  if (item >= items) return;
+
+  __shared__ uint4 q_s[kWaves][kHpg * kChunks];  // each wave's 4 query rows
+  __shared__ float4 p_s[kWaves][kTile];          // per-key probabilities
+
+  const int half = lane >> 5, c32 = lane & 31;
+  uint4 kr[kChunks];
+  uint4 vr[kTile / 2];
+  uint4 qn0, qn1;  // next query rows (2 x 16 B per lane)
+
+  Item cur = item_info(a, item);
+  auto load_k = [&](const Item& it, int tile) {
+    const int key = tile * kTile + lane;
+    const int hi = it.count > 0 ? it.count - 1 : 0;
+    const int ks = key < hi ? key : hi;
+#pragma unroll
+    for (int c = 0; c < kChunks; ++c) kr[c] = it.K4[(size_t)c * it.slots + ks];
+  };
+  qn0 = cur.q4[2 * lane];
+  qn1 = cur.q4[2 * lane + 1];
+  load_k(cur, cur.ta);
+
+  for (;;) {
+    q_s[wave][2 * lane] = qn0;
+    q_s[wave][2 * lane + 1] = qn1;
+    __builtin_amdgcn_wave_barrier();
+
+    const int nitem = item + W;
+    const bool has_next = nitem < items;
+    const Item nxt = item_info(a, has_next ? nitem : item);
+
+    float m[kHpg], l[kHpg], acc[kHpg][8];
+#pragma unroll
+    for (int h = 0; h < kHpg; ++h) {
+      m[h] = -INFINITY;
+      l[h] = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[h][i] = 0.f;
+    }
+
+    for (int tile = cur.ta; tile < cur.tb; ++tile) {
+      const int tbase = tile * kTile;
+      const bool valid = tbase + lane < cur.count;
+
+#pragma unroll
+      for (int j = 0; j < kTile / 2; ++j) {
+        const int k2 = tbase + 2 * j + half;
+        vr[j] = cur.V4[(size_t)(k2 < cur.count ? k2 : cur.count - 1) * kChunks + c32];
+      }
+      __builtin_amdgcn_sched_barrier(0);  // keep the V loads ahead of QK
+
+      // scores of this lane's key against the 4 heads
+      float s[kHpg] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < kChunks; ++c) {
+        const uint4 kv = kr[c];
+#pragma unroll
+        for (int h = 0; h < kHpg; ++h) {
+          const uint4 qv = q_s[wave][h * kChunks + c];
+          s[h] = dot2(qv.x, kv.x, s[h]);
+          s[h] = dot2(qv.y, kv.y, s[h]);
+          s[h] = dot2(qv.z, kv.z, s[h]);
+          s[h] = dot2(qv.w, kv.w, s[h]);
+        }
+      }
+
+      // online softmax update (log2 domain)
+      float p[kHpg];
+#pragma unroll
+      for (int h = 0; h < kHpg; ++h) {
+        const float sv = valid ? s[h] * a.sl2e : -INFINITY;
+        const float mn = fmaxf(m[h], wave_max(sv));
+        const float al = fast_exp2(m[h] - mn);
+        p[h] = fast_exp2(sv - mn);
+        l[h] = l[h] * al + p[h];
+        m[h] = mn;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[h][i] *= al;
+      }
+      p_s[wave][lane] = make_float4(p[0], p[1], p[2], p[3]);
+      __builtin_amdgcn_wave_barrier();
+
+      // prefetch: the next tile of this item, else the next item's first
+      // tile and query rows, else (last item) this tile again, a cache hit
+      {
+        const bool more = tile + 1 < cur.tb;
+        const bool go_next = !more && has_next;
+        Item tg;
+        tg.K4 = go_next ? nxt.K4 : cur.K4;
+        tg.slots = go_next ? nxt.slots : cur.slots;
+        tg.count = go_next ? nxt.count : cur.count;
+        const int tt = more ? tile + 1 : (go_next ? nxt.ta : tile);
+        // query rows first: the item switch then waits for them alone
+        const uint4* q4 = go_next ? nxt.q4 : cur.q4;
+        qn0 = q4[2 * lane];
+        qn1 = q4[2 * lane + 1];
+        load_k(tg, tt);
+      }
+      __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of P.V
+
+      // P.V: a half-wave per key, 8 dims per lane
+#pragma unroll
+      for (int j = 0; j < kTile / 2; ++j) {
+        const uint4 vv = vr[j];
+        const float4 pp = p_s[wave][2 * j + half];
+        const float x[8] = {bf_lo(vv.x), bf_hi(vv.x), bf_lo(vv.y), bf_hi(vv.y),
+                            bf_lo(vv.z), bf_hi(vv.z), bf_lo(vv.w), bf_hi(vv.w)};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          acc[0][i] = fmaf(pp.x, x[i], acc[0][i]);
+          acc[1][i] = fmaf(pp.y, x[i], acc[1][i]);
+          acc[2][i] = fmaf(pp.z, x[i], acc[2][i]);
+          acc[3][i] = fmaf(pp.w, x[i], acc[3][i]);
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+    }
+
+    // the item's partial: l over all lanes, o over the two half-waves
+    float* P = a.part + (size_t)item * kPart;
+#pragma unroll
+    for (int h = 0; h < kHpg; ++h) {
+      l[h] = wave_sum(l[h]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[h][i] += __shfl_xor(acc[h][i], 32, 64);
+    }
+    if (lane < 32) {
+#pragma unroll
+      for (int h = 0; h < kHpg; ++h) {
+        float4* dst = reinterpret_cast<float4*>(P + h * kD + 8 * c32);
+        dst[0] = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
+        dst[1] = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
+      }
+    }
+    if (lane < kHpg) {
+      float mm = m[0], ll = l[0];
+#pragma unroll
+      for (int h = 1; h < kHpg; ++h) {
+        mm = lane == h ? m[h] : mm;
+        ll = lane == h ? l[h] : ll;
+      }
+      P[kHpg * kD + lane] = mm;
+      P[kHpg * kD + kHpg + lane] = ll;
+    }
+
+    if (!has_next) break;
+    if (cur.ta == cur.tb) {  // empty item: nothing was prefetched for nxt
+      qn0 = nxt.q4[2 * lane];
+      qn1 = nxt.q4[2 * lane + 1];
+      load_k(nxt, nxt.ta);
+    }
+    cur = nxt;
+    item = nitem;
+  }
+}
+
+// grid: units; block: 256 (thread = dimension).
+__global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
+  const int u = blockIdx.x;
+  const int b = u / a.G, g = u - b * a.G;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  __shared__ float red[8][kWaves];
+
+  const uint16_t* qb = a.q + (size_t)b * a.q_bs + (size_t)g * kHpg * kD;
+  const size_t kvo = (size_t)b * a.kv_bs + (size_t)g * kD;
+  float qf[kHpg];
+#pragma unroll
+  for (int h = 0; h < kHpg; ++h) qf[h] = bf1(qb[h * kD + tid]);
+  const float kf = bf1(a.k[kvo + tid]);
+  const float vf = bf1(a.v[kvo + tid]);
+
+  // q.k_t (current-token score) and q.w_g (gate argument) for the 4 heads
+  float dts[8];
+#pragma unroll
+  for (int h = 0; h < kHpg; ++h) {
+    dts[h] = wave_sum(qf[h] * kf);
+    dts[kHpg + h] = wave_sum(qf[h] * a.w_g[(size_t)(g * kHpg + h) * kD + tid]);
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) red[j][wave] = dts[j];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 8; ++j) dts[j] = (red[j][0] + red[j][1]) + (red[j][2] + red[j][3]);
+
+  const int S = a.splits_ring + a.splits_bank;
+  const float* P = a.part + (size_t)u * S * kPart;
+  const int n = a.bank_n[u];
+  uint16_t* outp = a.out + (size_t)b * a.out_bs + (size_t)g * kHpg * kD;
+
+#pragma unroll
+  for (int h = 0; h < kHpg; ++h) {
+    // local read: ring splits plus the current token
+    const float sc = dts[h] * a.sl2e;
+    float M = sc;
+    for (int s = 0; s < a.splits_ring; ++s) M = fmaxf(M, P[s * kPart + kHpg * kD + h]);
+    float L = fast_exp2(sc - M);
+    float o = L * vf;
+    for (int s = 0; s < a.splits_ring; ++s) {
+      const float f = fast_exp2(P[s * kPart + kHpg * kD + h] - M);  // -inf -> 0
+      o = fmaf(P[s * kPart + h * kD + tid], f, o);
+      L = fmaf(P[s * kPart + kHpg * kD + kHpg + h], f, L);
+    }
+    const float oloc = o / L;
+
+    // anchor read: bank splits (empty bank reads as zero)
+    float oanc = 0.f;
+    if (n > 0) {
+      float M2 = -INFINITY;
+      for (int s = a.splits_ring; s < S; ++s) M2 = fmaxf(M2, P[s * kPart + kHpg * kD + h]);
+      float o2 = 0.f, L2 = 0.f;
+      for (int s = a.splits_ring; s < S; ++s) {
+        const float ms = P[s * kPart + kHpg * kD + h];
+        const float f = (ms == -INFINITY) ? 0.f : fast_exp2(ms - M2);
+        o2 = fmaf(P[s * kPart + h * kD + tid], f, o2);
+        L2 = fmaf(P[s * kPart + kHpg * kD + kHpg + h], f, L2);
+      }
+      oanc = o2 / L2;
+    }
+    const float gate = tanhf(dts[kHpg + h]);
+    outp[(size_t)h * kD + tid] = to_bf16(fmaf(gate, oanc, oloc));
+  }
+
+  // Write: ring slot t mod R takes the current K/V (after every read of
+  // this step, which all finished in the attention kernel), and pending
+  // slot t mod C takes the candidate record and score.
+  if (tid < 32) {
+    uint4* rk = reinterpret_cast<uint4*>(a.ring_k + (size_t)u * a.R * kD);
+    rk[(size_t)tid * a.R + a.ring_slot] = reinterpret_cast<const uint4*>(a.k + kvo)[tid];
+  } else if (tid < 64) {
+    uint4* rv = reinterpret_cast<uint4*>(a.ring_v + ((size_t)u * a.R + a.ring_slot) * kD);
+    rv[tid - 32] = reinterpret_cast<const uint4*>(a.v + kvo)[tid - 32];
+  } else if (tid < 96) {
+    uint4* pk = reinterpret_cast<uint4*>(a.pend_k + ((size_t)u * a.C + a.pend_slot) * kD);
+    pk[tid - 64] = reinterpret_cast<const uint4*>(a.ck + kvo)[tid - 64];
+  } else if (tid < 128) {
+    uint4* pv = reinterpret_cast<uint4*>(a.pend_v + ((size_t)u * a.C + a.pend_slot) * kD);
+    pv[tid - 96] = reinterpret_cast<const uint4*>(a.cv + kvo)[tid - 96];
+  } else if (tid == 128) {
+    a.pscore[(size_t)u * a.C + a.pend_slot] = a.cs[(size_t)b * a.cs_bs + g];
+  }
+}
+
+__global__ void fill_i32_kernel(int32_t* p, int32_t value, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = value;
+}
+
+}  // namespace
+
+// Workgroups of the attention kernel that are resident at once on the
+// current device (CUs x workgroups per CU), computed once per device.
+static int resident_workgroups() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int cus = 0, per_cu = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      cus = 256;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_attn_kernel, 256, 0) !=
+            hipSuccess || per_cu < 1)
+      per_cu = 1;
+    cached[dev] = cus * per_cu;
+  }
+  return cached[dev];
+}
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
+  const int S = a.splits_ring + a.splits_bank;
+  const int items = a.units * S;
+  int grid = (items + kWaves - 1) / kWaves;
+  const int res = resident_workgroups();
+  if (grid > res) grid = res;
+  hipLaunchKernelGGL(decode_attn_kernel, dim3(grid), dim3(256), 0, s, a, items);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(decode_combine_kernel, dim3(a.units), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_i32(int32_t* p, int32_t value, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t blocks = (n + 255) / 256;
+  hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p, value, n);
+  return hipGetLastError();
+}
+
+}  // namespace rma

@@ -1,0 +1,345 @@
+// Host side of librma.so: the C ABI declared in include/rma.h.
+//
+// Everything here is argument checking, state bookkeeping (the lockstep
+// position, pending and bank counters of every layer are mirrored on the
+// host) and kernel launches.  No arithmetic of the layer runs on the host.
+#include "rma.h"
+
+#include <cmath>
+#include <cstring>
+
+#include "rma_kernels.h"
+
+namespace {
+
+using rma::kD;
+using rma::kHpg;
+using rma::kMaxSplits;
+using rma::kPart;
+using rma::kTile;
+
+constexpr uint64_t kAlign = 256;
+
+uint64_t align_up(uint64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// RMA_OK, RMA_E_ARG (nonsense) or RMA_E_UNSUPPORTED (valid, not built for).
+int check_config(const rma_config* c) {
+  if (!c) return RMA_E_ARG;
+  if (c->layers < 1 || c->layers > RMA_MAX_LAYERS || c->q_heads < 1 || c->kv_groups < 1 ||
+      c->head_dim < 1 || c->window < 2 || c->bank_cap < 1 || c->commit < 1 ||
+      !std::isfinite(c->scale) || c->q_heads % c->kv_groups != 0)
+    return RMA_E_ARG;
+  if (c->head_dim != kD || c->q_heads != kHpg * c->kv_groups) return RMA_E_UNSUPPORTED;
+  if (c->window > 8193 || c->commit > 256 || c->bank_cap + c->commit > 2048)
+    return RMA_E_UNSUPPORTED;
+  return RMA_OK;
+}
+
+int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+// Split-K policy: every read (ring, bank) of a (sequence, group) unit is
+// cut into parts of whole 64-key tiles so that there are at least ~1,024
+// parts in a launch (one per wave of the persistent attention kernel on a
+// 256-CU device).  A function of the batch only, so that the scratch size
+// is known before the first call.
+struct Splits {
+  int ring, bank, tiles_ring, tiles_bank;
+};
+
+Splits choose_splits(const rma_config* c, int32_t batch) {
+  const int units = batch * c->kv_groups;
+  const int tr = ceil_div(c->window - 1, kTile);
+  const int tb = ceil_div(c->bank_cap, kTile);
+  const int tmax = tr > tb ? tr : tb;
+  int s = 1;
+  while (s < kMaxSplits && units * 2 * s < 1024 && s < tmax) s *= 2;
+  Splits r;
+  r.tiles_ring = ceil_div(tr, s);
+  r.tiles_bank = ceil_div(tb, s);
+  // no part starts past the last tile
+  r.ring = ceil_div(tr, r.tiles_ring);
+  r.bank = ceil_div(tb, r.tiles_bank);
+  return r;
+}
+
+int make_layout(const rma_config* c, int32_t batch, rma_layout* L) {
+  std::memset(L, 0, sizeof(*L));
+  const uint64_t units = (uint64_t)c->layers * batch * c->kv_groups;
+  const uint64_t R = c->window - 1, N = c->bank_cap, C = c->commit, d = c->head_dim;
+  const uint64_t rec_half = d * 2;  // bytes of K (or V) of one record
+  uint64_t off = 0;
+  auto take = [&](uint64_t bytes) {
+    const uint64_t at = off;
+    off = align_up(off + bytes);
+    return at;
+  };
+  L->ring_k = take(units * R * rec_half);
+  L->ring_v = take(units * R * rec_half);
+  L->bank_k = take(units * N * rec_half);
+  L->bank_v = take(units * N * rec_half);
+  L->pend_k = take(units * C * rec_half);
+  L->pend_v = take(units * C * rec_half);
+  L->bscore = take(units * N * 4);
+  L->bsrc = take(units * N * 4);
+  L->pscore = take(units * C * 4);
+  L->bank_n = take(units * 4);
+  const Splits sp = choose_splits(c, batch);
+  L->scratch_bytes = (uint64_t)batch * c->kv_groups * (sp.ring + sp.bank) * kPart * 4;
+  L->scratch = take(L->scratch_bytes);
+  L->total_bytes = off;
+  L->ring_bytes = units * R * rec_half * 2;
+  L->bank_bytes = units * N * rec_half * 2;
+  L->pend_bytes = units * C * rec_half * 2;
+  L->meta_bytes = units * (N * 8 + C * 4 + 4);
+  return RMA_OK;
+}
+
+bool aligned16(const void* p) { return p && ((uintptr_t)p & 15u) == 0; }
+
+int check_state(const rma_state* st, int32_t layer) {
+  if (!st || !st->base) return RMA_E_ARG;
+  const int rc = check_config(&st->cfg);
+  if (rc != RMA_OK) return rc;
+  if (layer < 0 || layer >= st->cfg.layers || st->batch < 1) return RMA_E_ARG;
+  return RMA_OK;
+}
+
+template <typename T>
+T* region(const rma_state* st, uint64_t off) {
+  return reinterpret_cast<T*>(static_cast<char*>(st->base) + off);
+}
+
+int hip_fail(rma_state* st, hipError_t e) {
+  st->hip_error = (int32_t)e;
+  return RMA_E_HIP;
+}
+
+// Fill the launch arguments of one token (or one token of a block) of a
+// layer.  Token inputs are [B][...] slices with the given batch strides.
+rma::DecodeArgs decode_args(const rma_state* st, int32_t layer, int64_t t, const void* q,
+                            const void* k, const void* v, const void* ck, const void* cv,
+                            const float* cs, const float* w_g, void* out, int64_t q_bs,
+                            int64_t kv_bs, int64_t cs_bs, int64_t out_bs) {
+  const rma_config& c = st->cfg;
+  const rma_layout& L = st->layout;
+  const int B = st->batch, G = c.kv_groups;
+  const int R = c.window - 1, N = c.bank_cap, C = c.commit;
+  const uint64_t unit0 = (uint64_t)layer * B * G;
+  const Splits sp = choose_splits(&c, B);
+  rma::DecodeArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.ck = static_cast<const uint16_t*>(ck);
+  a.cv = static_cast<const uint16_t*>(cv);
+  a.cs = cs;
+  a.w_g = w_g;
+  a.out = static_cast<uint16_t*>(out);
+  a.ring_k = region<uint16_t>(st, L.ring_k) + unit0 * R * kD;
+  a.ring_v = region<uint16_t>(st, L.ring_v) + unit0 * R * kD;
+  a.bank_k = region<uint16_t>(st, L.bank_k) + unit0 * N * kD;
+  a.bank_v = region<uint16_t>(st, L.bank_v) + unit0 * N * kD;
+  a.bank_n = region<int32_t>(st, L.bank_n) + unit0;
+  a.pend_k = region<uint16_t>(st, L.pend_k) + unit0 * C * kD;
+  a.pend_v = region<uint16_t>(st, L.pend_v) + unit0 * C * kD;
+  a.pscore = region<float>(st, L.pscore) + unit0 * C;
+  a.part = region<float>(st, L.scratch);
+  a.q_bs = q_bs;
+  a.kv_bs = kv_bs;
+  a.cs_bs = cs_bs;
+  a.out_bs = out_bs;
+  a.units = B * G;
+  a.G = G;
+  a.H = c.q_heads;
+  a.R = R;
+  a.N = N;
+  a.C = C;
+  a.ring_count = (int)(t < R ? t : R);
+  a.ring_slot = (int)(t % R);
+  a.pend_slot = (int)(t % C);
+  a.splits_ring = sp.ring;
+  a.splits_bank = sp.bank;
+  a.tiles_ring = sp.tiles_ring;
+  a.tiles_bank = sp.tiles_bank;
+  a.sl2e = (float)((double)c.scale * 1.4426950408889634);
+  return a;
+}
+
+}  // namespace
+
+extern "C" {
+
+int rma_config_default(rma_config* cfg) {
+  if (!cfg) return RMA_E_ARG;
+  cfg->layers = 8;
+  cfg->q_heads = 16;
+  cfg->kv_groups = 4;
+  cfg->head_dim = 256;
+  cfg->window = 1024;
+  cfg->bank_cap = 1024;
+  cfg->commit = 256;
+  cfg->scale = 0.0625f;
+  return RMA_OK;
+}
+
+size_t rma_state_bytes(const rma_config* cfg, int32_t batch) {
+  if (check_config(cfg) != RMA_OK || batch < 1) return 0;
+  rma_layout L;
+  make_layout(cfg, batch, &L);
+  return (size_t)L.total_bytes;
+}
+
+int rma_state_layout(const rma_config* cfg, int32_t batch, rma_layout* out) {
+  if (!out || batch < 1) return RMA_E_ARG;
+  const int rc = check_config(cfg);
+  if (rc != RMA_OK) return rc;
+  return make_layout(cfg, batch, out);
+}
+
+int rma_state_init(rma_state* st, const rma_config* cfg, int32_t batch, void* dev_buf,
+                   size_t bytes, int64_t start_pos, int32_t bank_n, void* stream) {
+  if (!st || !dev_buf || batch < 1 || start_pos < 0) return RMA_E_ARG;
+  const int rc = check_config(cfg);
+  if (rc != RMA_OK) return rc;
+  if (((uintptr_t)dev_buf % kAlign) != 0) return RMA_E_ARG;
+  if (bank_n < 0 || bank_n > cfg->bank_cap) return RMA_E_ARG;
+  rma_layout L;
+  make_layout(cfg, batch, &L);
+  if (bytes < L.total_bytes) return RMA_E_ARG;
+  rma_state s;
+  std::memset(&s, 0, sizeof(s));
+  s.cfg = *cfg;
+  s.batch = batch;
+  s.base = dev_buf;
+  s.bytes = bytes;
+  s.layout = L;
+  for (int l = 0; l < cfg->layers; ++l) {
+    s.t[l] = start_pos;
+    s.bank_n[l] = bank_n;
+    s.pend_n[l] = (int32_t)(start_pos % cfg->commit);
+  }
+  const int64_t units = (int64_t)cfg->layers * batch * cfg->kv_groups;
+  const hipError_t e = rma::launch_fill_i32(region<int32_t>(&s, L.bank_n), bank_n, units,
+                                            static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) {
+    st->hip_error = (int32_t)e;
+    return RMA_E_HIP;
+  }
+  *st = s;
+  return RMA_OK;
+}
+
+int rma_decode_step(rma_state* st, int32_t layer, const void* q, const void* k, const void* v,
+                    const void* cand_k, const void* cand_v, const float* cand_score,
+                    const float* w_g, void* out, void* stream) {
+  int rc = check_state(st, layer);
+  if (rc != RMA_OK) return rc;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(cand_k) ||
+      !aligned16(cand_v) || !cand_score || !w_g || !aligned16(out))
+    return RMA_E_ARG;
+  const rma_config& c = st->cfg;
+  if (st->pend_n[layer] >= c.commit) return RMA_E_PENDING_FULL;
+  const int64_t t = st->t[layer];
+  const int64_t H = c.q_heads, G = c.kv_groups;
+  const rma::DecodeArgs a = decode_args(st, layer, t, q, k, v, cand_k, cand_v, cand_score, w_g,
+                                        out, H * kD, G * kD, G, H * kD);
+  const hipError_t e = rma::launch_decode(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(st, e);
+  st->t[layer] = t + 1;
+  st->pend_n[layer] += 1;
+  return RMA_OK;
+}
+
+int rma_prefill_block(rma_state* st, int32_t layer, int32_t n_tokens, const void* q,
+                      const void* k, const void* v, const void* cand_k, const void* cand_v,
+                      const float* cand_score, const float* w_g, void* out, void* stream) {
+  int rc = check_state(st, layer);
+  if (rc != RMA_OK) return rc;
+  const rma_config& c = st->cfg;
+  if (n_tokens < 1 || n_tokens > c.commit) return RMA_E_ARG;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(cand_k) ||
+      !aligned16(cand_v) || !cand_score || !w_g || !aligned16(out))
+    return RMA_E_ARG;
+  const int64_t t0 = st->t[layer];
+  if (st->pend_n[layer] != 0 || t0 % c.commit != 0) return RMA_E_NOT_BOUNDARY;
+  const int64_t H = c.q_heads, G = c.kv_groups, n = n_tokens;
+  const uint16_t* q16 = static_cast<const uint16_t*>(q);
+  const uint16_t* k16 = static_cast<const uint16_t*>(k);
+  const uint16_t* v16 = static_cast<const uint16_t*>(v);
+  const uint16_t* ck16 = static_cast<const uint16_t*>(cand_k);
+  const uint16_t* cv16 = static_cast<const uint16_t*>(cand_v);
+  uint16_t* o16 = static_cast<uint16_t*>(out);
+  // token i of every sequence: rows i of the [B][n][...] inputs
+  for (int64_t i = 0; i < n; ++i) {
+    const rma::DecodeArgs a =
+        decode_args(st, layer, t0 + i, q16 + i * H * kD, k16 + i * G * kD, v16 + i * G * kD,
+                    ck16 + i * G * kD, cv16 + i * G * kD, cand_score + i * G, w_g,
+                    o16 + i * H * kD, n * H * kD, n * G * kD, n * G, n * H * kD);
+    const hipError_t e = rma::launch_decode(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) {
+      st->t[layer] = t0 + i;
+      st->pend_n[layer] = (int32_t)i;
+      return hip_fail(st, e);
+    }
+  }
+  st->t[layer] = t0 + n;
+  st->pend_n[layer] = (int32_t)n;
+  return RMA_OK;
+}
+
+int rma_admit(rma_state* st, int32_t layer, void* stream) {
+  if (!st) return RMA_E_ARG;
+  const int lo = layer == -1 ? 0 : layer;
+  const int hi = layer == -1 ? st->cfg.layers : layer + 1;
+  int rc = check_state(st, lo);
+  if (rc != RMA_OK) return rc;
+  if (layer < -1 || hi > st->cfg.layers) return RMA_E_ARG;
+  const rma_config& c = st->cfg;
+  for (int l = lo; l < hi; ++l)
+    if (st->pend_n[l] != c.commit || st->t[l] % c.commit != 0) return RMA_E_NOT_BOUNDARY;
+  const rma_layout& L = st->layout;
+  const int BG = st->batch * c.kv_groups;
+  rma::AdmitArgs a;
+  a.bank_k = region<uint16_t>(st, L.bank_k);
+  a.bank_v = region<uint16_t>(st, L.bank_v);
+  a.bscore = region<float>(st, L.bscore);
+  a.bsrc = region<int32_t>(st, L.bsrc);
+  a.bank_n = region<int32_t>(st, L.bank_n);
+  a.pend_k = region<const uint16_t>(st, L.pend_k);
+  a.pend_v = region<const uint16_t>(st, L.pend_v);
+  a.pscore = region<const float>(st, L.pscore);
+  a.N = c.bank_cap;
+  a.C = c.commit;
+  // one launch over consecutive layers at the same position
+  int l = lo;
+  while (l < hi) {
+    int e_end = l + 1;
+    while (e_end < hi && st->t[e_end] == st->t[l]) ++e_end;
+    a.unit0 = l * BG;
+    a.units = (e_end - l) * BG;
+    a.block_start = st->t[l] - c.commit;
+    const hipError_t e = rma::launch_admit(a, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(st, e);
+    for (int x = l; x < e_end; ++x) {
+      const int nn = st->bank_n[x] + c.commit;
+      st->bank_n[x] = nn < c.bank_cap ? nn : c.bank_cap;
+      st->pend_n[x] = 0;
+    }
+    l = e_end;
+  }
+  return RMA_OK;
+}
+
+const char* rma_strerror(int status) {
+  switch (status) {
+    case RMA_OK: return "ok";
+    case RMA_E_ARG: return "invalid argument (null or misaligned pointer, bad size or index)";
+    case RMA_E_PENDING_FULL: return "pending buffer full: admit before the next decode step";
+    case RMA_E_NOT_BOUNDARY: return "not at a block boundary";
+    case RMA_E_HIP: return "HIP launch failed";
+    case RMA_E_UNSUPPORTED: return "geometry not supported by the kernels";
+    default: return "unknown status";
+  }
+}
+
+}  // extern "C"

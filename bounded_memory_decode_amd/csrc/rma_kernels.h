@@ -1,0 +1,72 @@
+// Internal launcher interface between the C-ABI host code (rma_host.cpp)
+// and the gfx950 kernels.  Not installed; not part of the public ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rma {
+
+constexpr int kD = 256;       // head dimension the kernels are built for
+constexpr int kHpg = 4;       // query heads per KV group
+constexpr int kTile = 64;     // keys per wave tile (one key per lane)
+constexpr int kChunks = kD / 8;  // 16-byte chunks per K/V row
+constexpr int kPart = kHpg * kD + 2 * kHpg;  // floats per split partial
+constexpr int kMaxSplits = 16;  // split-K parts per read (ring, bank)
+
+// One decode token of one layer.
+struct DecodeArgs {
+  const uint16_t* q;       // [B][H][D]
+  const uint16_t* k;       // [B][G][D]
+  const uint16_t* v;
+  const uint16_t* ck;
+  const uint16_t* cv;
+  const float* cs;         // [B][G]
+  const float* w_g;        // [H][D]
+  uint16_t* out;           // [B][H][D]
+  uint16_t* ring_k;        // layer base, unit stride R*D
+  uint16_t* ring_v;
+  const uint16_t* bank_k;  // layer base, unit stride N*D
+  const uint16_t* bank_v;
+  const int32_t* bank_n;   // [B*G] of this layer
+  uint16_t* pend_k;        // layer base, unit stride C*D
+  uint16_t* pend_v;
+  float* pscore;           // layer base, unit stride C
+  float* part;             // scratch: [units][splits][kPart]
+  int64_t q_bs;            // elements between sequences in q
+  int64_t kv_bs;           // ... in k, v, ck, cv
+  int64_t cs_bs;           // ... in cs
+  int64_t out_bs;          // ... in out
+  int units;               // B*G
+  int G, H, R, N, C;
+  int ring_count;          // valid ring slots: min(t, R)
+  int ring_slot;           // t mod R
+  int pend_slot;           // t mod C
+  int splits_ring, splits_bank;
+  int tiles_ring, tiles_bank;  // tiles per split
+  float sl2e;              // scale * log2(e)
+};
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+
+// Admit of one or more layers.
+struct AdmitArgs {
+  uint16_t* bank_k;        // region base (unit 0)
+  uint16_t* bank_v;
+  float* bscore;
+  int32_t* bsrc;
+  int32_t* bank_n;
+  const uint16_t* pend_k;
+  const uint16_t* pend_v;
+  const float* pscore;
+  int unit0;               // first unit (layer * B * G)
+  int units;               // units to admit
+  int N, C;
+  int64_t block_start;     // position of pending slot 0
+};
+
+hipError_t launch_admit(const AdmitArgs& a, hipStream_t s);
+
+// Fill an int32 array on the device.
+hipError_t launch_fill_i32(int32_t* p, int32_t value, int64_t n, hipStream_t s);
+
+}  // namespace rma

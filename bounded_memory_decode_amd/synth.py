@@ -20,8 +20,9 @@ far from uniform.
 
 Two generators:
   * numpy: one ``SeedSequence(seed, spawn_key=(workload, kind, layer,
-    step, b))`` stream per tensor slice, so any slice can be regenerated on
-    its own (parity tests, oracle inputs);
+    step, b))`` stream per tensor (start state: per sequence, so one
+    sequence can be regenerated on its own; step inputs: per token for the
+    whole batch);
   * torch: one seeded ``torch.Generator`` per (kind, layer[, step]) on the
     target device, used only where numpy would be too slow (full-size bench
     state).  Its values differ from the numpy stream; parity at that size
@@ -91,10 +92,13 @@ WORKLOADS: Dict[str, Workload] = {
 
 def bf16_bits(x: np.ndarray) -> np.ndarray:
     """fp32 -> bf16 bit patterns, round to nearest, ties to even."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    nan = np.isnan(np.asarray(x, dtype=np.float32))
-    r = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
-    r[nan] = 0x7FC0
+    f = np.ascontiguousarray(x, dtype=np.float32)
+    u = f.view(np.uint32)
+    # finite values and infinities cannot carry out of 32 bits; NaNs are
+    # replaced below
+    r = ((u + np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))) >> np.uint32(16))
+    r = r.astype(np.uint16)
+    r[np.isnan(f)] = 0x7FC0
     return r
 
 
@@ -205,22 +209,16 @@ def step_inputs(w: Workload, seed: int, layer: int, step: int,
                 batch: Optional[Sequence[int]] = None) -> Dict[str, np.ndarray]:
     """Inputs of one decode token of one layer: q [b][H][d], k, v, ck, cv
     [b][G][d] (bf16 bits) and cs [b][G] f32.  `step` counts tokens from
-    t0, so the same (layer, step) always gives the same values."""
-    bl = _batch(w, batch)
+    t0, so the same (layer, step) always gives the same values.  One stream
+    per (tensor, layer, step) covers the whole batch; `batch` selects rows."""
     H, G, d = w.H, w.G, w.d
-    out = {
-        "q": np.empty((len(bl), H, d), np.uint16),
-        "k": np.empty((len(bl), G, d), np.uint16),
-        "v": np.empty((len(bl), G, d), np.uint16),
-        "ck": np.empty((len(bl), G, d), np.uint16),
-        "cv": np.empty((len(bl), G, d), np.uint16),
-        "cs": np.empty((len(bl), G), np.float32),
-    }
-    for bi, b in enumerate(bl):
-        out["q"][bi] = _normal_bf16(_rng(seed, w, "q", layer, step, b), (H, d), w.qkv_std)
-        for kind in ("k", "v", "ck", "cv"):
-            out[kind][bi] = _normal_bf16(_rng(seed, w, kind, layer, step, b), (G, d), w.qkv_std)
-        out["cs"][bi] = _scores(_rng(seed, w, "cs", layer, step, b), (G,), w)
+    out = {"q": _normal_bf16(_rng(seed, w, "q", layer, step), (w.B, H, d), w.qkv_std)}
+    for kind in ("k", "v", "ck", "cv"):
+        out[kind] = _normal_bf16(_rng(seed, w, kind, layer, step), (w.B, G, d), w.qkv_std)
+    out["cs"] = _scores(_rng(seed, w, "cs", layer, step), (w.B, G), w)
+    if batch is not None:
+        idx = [int(b) for b in batch]
+        out = {k: np.ascontiguousarray(v[idx]) for k, v in out.items()}
     return out
 
 

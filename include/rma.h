@@ -1,0 +1,201 @@
+/*
+ * rma.h - C ABI of librma.so, the Rock Memory Anchors (RMA) attention-layer
+ * step on AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes (EdgeRock model card on ModelScope, section
+ * "How Rock Memory Anchors work" and its history-component table; the
+ * ai-primer story "EdgeRock-4B fixes its attention KV cache at 72 MiB",
+ * list of the three operations Write / Admit / Retrieve):
+ *
+ *   per sequence, per RMA layer, per KV group g, a fixed-capacity history:
+ *     ring     : the K/V of the R = window-1 preceding positions
+ *     bank     : up to N committed anchor records (K, V, score, source pos)
+ *     pending  : the C candidate records of the current block (K, V, score)
+ *
+ *   decode of the token at position t, query head h of group g:
+ *     o_local  = softmax attention over ring positions max(0,t-R) .. t-1
+ *                plus the current token (the local window of R+1 positions)
+ *     o_anchor = softmax attention over committed bank slots 0 .. n-1
+ *                (zero when n == 0)
+ *     out      = o_local + tanh(q_h . w_g[h]) * o_anchor
+ *   then the token's K/V replaces ring slot t mod R and its candidate
+ *   record and score go to pending slot t mod C.
+ *
+ *   admit, once C candidates are pending: the n anchors and C candidates
+ *   of each (sequence, layer, group) compete; the first min(N, n + C) in
+ *   the order (score descending, then global index ascending; anchors have
+ *   global index = slot, candidates N + pending slot; -0.0 == +0.0; NaN
+ *   below -inf) are kept.  Evicted anchor slots, ascending, receive the
+ *   admitted candidates in ascending pending order; the remainder is
+ *   appended after slot n-1.  Retained records are not touched.  Reads of
+ *   the bank see an admitted record only from the next block on.
+ *
+ * The gate form, the tie-break and the compaction order are readings of
+ * the pages (which only say "query-dependent signed gate", "highest
+ * priority", "retained records remain separate and unchanged").
+ *
+ * Conventions for every call:
+ *   - bf16 tensors are passed as `const void*` to 16-bit IEEE bfloat16
+ *     values; fp32 as `float*`.  All tensor pointers are DEVICE pointers,
+ *     16-byte aligned, C-contiguous, owned by the caller, and must stay
+ *     valid until the work on `stream` has finished.
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Calls enqueue
+ *     work and return; nothing is synchronous.  Device-side conditions are
+ *     never reported back; argument and sequencing errors are detected on
+ *     the host before anything is enqueued, and leave the state unchanged.
+ *   - The library allocates no memory.  The caller owns the rma_state
+ *     struct and one device buffer holding the whole state (its size from
+ *     rma_state_bytes).
+ *   - Batches move in lockstep: all sequences of a layer share the
+ *     position t, which the host mirrors in rma_state.
+ *   - Kernels support head_dim 256 and 4 query heads per KV group (the
+ *     EdgeRock geometry); other shapes return RMA_E_UNSUPPORTED.
+ */
+#ifndef RMA_H
+#define RMA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RMA_MAX_LAYERS 64
+
+/* Status codes. */
+#define RMA_OK 0
+#define RMA_E_ARG (-1)          /* null/misaligned pointer, bad size or index */
+#define RMA_E_PENDING_FULL (-2) /* decode with C candidates pending, no admit */
+#define RMA_E_NOT_BOUNDARY (-3) /* admit with < C pending; prefill off a block start */
+#define RMA_E_HIP (-4)          /* a HIP launch failed; code in rma_state.hip_error */
+#define RMA_E_UNSUPPORTED (-5)  /* geometry the kernels are not built for */
+
+/* Layer geometry.  EdgeRock values (rma_config_default): 8 layers,
+ * 16 query heads, 4 KV groups, head_dim 256, window 1024 (ring 1023),
+ * bank_cap 1024, commit 256, scale 1/16 (model card history-component
+ * table; Rock Matrix models page spec list; head_dim from the card's
+ * persistent-history MiB table).  Limits: 1 <= layers <= RMA_MAX_LAYERS,
+ * q_heads == 4 * kv_groups, head_dim == 256, 2 <= window <= 4097,
+ * 1 <= bank_cap, 1 <= commit <= 256, bank_cap + commit <= 2048. */
+typedef struct {
+  int32_t layers;
+  int32_t q_heads;
+  int32_t kv_groups;
+  int32_t head_dim;
+  int32_t window;    /* local window incl. the current token; ring = window-1 */
+  int32_t bank_cap;  /* N: committed anchors per (sequence, layer, group) */
+  int32_t commit;    /* C: pending slots = tokens between admits */
+  float scale;       /* softmax scale on q.k, normally 1/sqrt(head_dim) */
+} rma_config;
+
+/* Byte offsets of the regions inside the state buffer.  Every region is
+ * indexed by unit u = (layer * batch + b) * kv_groups + g first, and is
+ * 256-byte aligned.  R = window-1, N = bank_cap, C = commit, d = head_dim.
+ *
+ *   ring_k  [units][d/8][R][8] bf16   K, split in 16-byte chunks of 8 dims,
+ *                                     chunk-major (chunk c of slot s is at
+ *                                     ((u*(d/8) + c)*R + s)*16 bytes)
+ *   ring_v  [units][R][d]      bf16   V rows
+ *   bank_k  [units][d/8][N][8] bf16   as ring_k with N slots
+ *   bank_v  [units][N][d]      bf16
+ *   pend_k  [units][C][d]      bf16   K rows of pending candidates
+ *   pend_v  [units][C][d]      bf16
+ *   bscore  [units][N]         f32    score of each committed anchor
+ *   bsrc    [units][N]         i32    source position of each anchor
+ *   pscore  [units][C]         f32    score of each pending candidate
+ *   bank_n  [units]            i32    committed anchors (dense prefix)
+ *   scratch                           split-K partials, library-private
+ */
+typedef struct {
+  uint64_t ring_k, ring_v, bank_k, bank_v, pend_k, pend_v;
+  uint64_t bscore, bsrc, pscore, bank_n, scratch;
+  uint64_t scratch_bytes;
+  uint64_t total_bytes;
+  uint64_t ring_bytes, bank_bytes, pend_bytes, meta_bytes; /* K+V+metadata totals */
+} rma_layout;
+
+/* Caller-owned state handle.  Plain data; copy it to snapshot the host
+ * counters (together with a copy of the device buffer).  Fields are read
+ * by the library and updated only by the calls below. */
+typedef struct {
+  rma_config cfg;
+  int32_t batch;
+  int32_t hip_error;            /* last HIP error code seen (0 = none) */
+  void* base;                   /* device state buffer */
+  uint64_t bytes;               /* its size */
+  rma_layout layout;
+  int64_t t[RMA_MAX_LAYERS];    /* next position per layer */
+  int32_t bank_n[RMA_MAX_LAYERS]; /* committed anchors per layer (same in
+                                     every sequence and group) */
+  int32_t pend_n[RMA_MAX_LAYERS]; /* pending candidates per layer */
+} rma_state;
+
+/* Fill *cfg with the EdgeRock geometry.  Returns RMA_OK, or RMA_E_ARG for
+ * a null pointer. */
+int rma_config_default(rma_config* cfg);
+
+/* Bytes of device memory a state for `batch` sequences needs (capacity
+ * planning before inference starts; the model card's FAQ and the
+ * tpsreport "What this means" paragraph note that fixed per-sequence
+ * memory can be computed up front).  Returns 0 for an invalid config or
+ * batch < 1. */
+size_t rma_state_bytes(const rma_config* cfg, int32_t batch);
+
+/* Region offsets for `batch` sequences.  Returns RMA_OK, RMA_E_ARG or
+ * RMA_E_UNSUPPORTED. */
+int rma_state_layout(const rma_config* cfg, int32_t batch, rma_layout* out);
+
+/* Bind `dev_buf` (at least rma_state_bytes bytes, 256-byte aligned) to
+ * *st and start every layer at position `start_pos` with `bank_n`
+ * committed anchors (0 <= bank_n <= bank_cap) and start_pos % commit
+ * pending candidates.  Enqueues a write of the device bank counts; record
+ * contents, scores and source positions are left as they are (the caller
+ * fills them through the layout, or starts from an empty history). */
+int rma_state_init(rma_state* st, const rma_config* cfg, int32_t batch,
+                   void* dev_buf, size_t bytes, int64_t start_pos,
+                   int32_t bank_n, void* stream);
+
+/* Decode one token of layer `layer` for all sequences (Retrieve, then
+ * Write; ai-primer three-operation list, items 1 and 3):
+ *   q          [batch][q_heads][head_dim]   bf16  query of the token
+ *   k, v       [batch][kv_groups][head_dim] bf16  the token's own K/V
+ *   cand_k/v   [batch][kv_groups][head_dim] bf16  its candidate record
+ *   cand_score [batch][kv_groups]           f32   the candidate's score
+ *   w_g        [q_heads][head_dim]          f32   gate weights of the layer
+ *   out        [batch][q_heads][head_dim]   bf16  result
+ * Returns RMA_E_PENDING_FULL (state unchanged) when C candidates are
+ * pending; call rma_admit first. */
+int rma_decode_step(rma_state* st, int32_t layer, const void* q, const void* k,
+                    const void* v, const void* cand_k, const void* cand_v,
+                    const float* cand_score, const float* w_g, void* out,
+                    void* stream);
+
+/* A chunked-prefill block of `n_tokens` (1 .. commit) consecutive tokens
+ * of layer `layer`, starting at a block boundary (no candidates pending).
+ * Same result as that many rma_decode_step calls: each query attends to
+ * its causal local window over the ring and the earlier tokens of the
+ * block, and to the bank committed before the block.  Shapes as in
+ * rma_decode_step with a token axis after the batch axis:
+ *   q [batch][n][q_heads][d], k/v/cand_k/cand_v [batch][n][kv_groups][d],
+ *   cand_score [batch][n][kv_groups], out [batch][n][q_heads][d].
+ * Returns RMA_E_NOT_BOUNDARY when t % commit != 0 or candidates pend. */
+int rma_prefill_block(rma_state* st, int32_t layer, int32_t n_tokens,
+                      const void* q, const void* k, const void* v,
+                      const void* cand_k, const void* cand_v,
+                      const float* cand_score, const float* w_g, void* out,
+                      void* stream);
+
+/* Admit for layer `layer`, or for every layer when layer == -1 (Admit;
+ * ai-primer list item 2, tpsreport "How it works").  Every selected
+ * layer must hold exactly C pending candidates, else RMA_E_NOT_BOUNDARY
+ * and nothing is enqueued. */
+int rma_admit(rma_state* st, int32_t layer, void* stream);
+
+/* Static text for a status code. */
+const char* rma_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* RMA_H */

@@ -1,0 +1,100 @@
+"""Helpers shared by the GPU parity tests: move synthetic inputs to the
+device, build an RMA state from a natural-layout start state, compare
+outputs with the oracle and states bit for bit."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+from bounded_memory_decode_amd import rma, synth
+
+DEV = "cuda"
+
+# Tolerance of the bf16 outputs against the oracle's unrounded double:
+#   - the stated bound: 2e-2 max-abs;
+#   - relative to the output scale: max error <= 1e-2 * max|ref|;
+#   - per element: 2^-8 |ref| (bf16 rounding is 2^-9, fp32 accumulation,
+#     exp2 and tanh add far less) + 1e-3 * max|ref| for values near zero.
+ABS_BOUND = 2e-2
+REL_BOUND = 1e-2
+
+
+def log(msg: str):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def cfg_for(w: synth.Workload) -> rma.Config:
+    return rma.config_default(layers=w.L, q_heads=w.H, kv_groups=w.G, head_dim=w.d,
+                              window=w.R + 1, bank_cap=w.N, commit=w.C, scale=w.d ** -0.5)
+
+
+def to_dev(a: np.ndarray) -> torch.Tensor:
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(DEV)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(DEV)
+
+
+def inputs_to_dev(x: dict) -> dict:
+    return {k: to_dev(v) for k, v in x.items()}
+
+
+REGIONS = ("ring_k", "ring_v", "bank_k", "bank_v", "bscore", "bsrc", "pend_k", "pend_v",
+           "pscore")
+
+
+def gpu_state(w: synth.Workload, st_np: dict) -> rma.State:
+    S = rma.State(cfg_for(w), w.B, DEV, start_pos=w.t0, bank_n=w.bank_n)
+    for name in REGIONS:
+        S.write(name, st_np[name])
+    torch.cuda.synchronize()
+    return S
+
+
+def decode(S: rma.State, layer: int, xd: dict, wg_dev: torch.Tensor) -> torch.Tensor:
+    return S.decode_step(layer, xd["q"], xd["k"], xd["v"], xd["ck"], xd["cv"], xd["cs"], wg_dev)
+
+
+def out_errors(gpu: torch.Tensor, ref: np.ndarray):
+    g = gpu.float().cpu().numpy().astype(np.float64)
+    err = np.abs(g - ref)
+    return err, np.abs(ref).max()
+
+
+def check_out(gpu: torch.Tensor, ref: np.ndarray, tag: str):
+    err, scale = out_errors(gpu, ref)
+    emax = err.max()
+    assert emax <= ABS_BOUND, f"{tag}: max abs error {emax:.3e} > {ABS_BOUND}"
+    assert emax <= REL_BOUND * scale, f"{tag}: max error {emax:.3e} > 1e-2 * {scale:.3e}"
+    bound = 2.0 ** -8 * np.abs(ref) + 1e-3 * scale
+    bad = err > bound
+    assert not bad.any(), (f"{tag}: {bad.sum()} elements beyond 2^-8|ref| + 1e-3 max|ref|; "
+                           f"worst {err[bad].max():.3e}")
+    return emax, scale
+
+
+def bits(t: torch.Tensor) -> np.ndarray:
+    return t.cpu().numpy()
+
+
+def check_state(S: rma.State, o, tag: str, layers=None, batch=None):
+    """Bit-exact comparison of every region (and counters) with the oracle."""
+    ls = slice(None) if layers is None else layers
+    bs = slice(None) if batch is None else batch
+    for name in REGIONS + ("bank_n",):
+        g = bits(S.read(name, ls, bs))
+        r = getattr(o, name)[ls][:, bs]
+        if r.dtype == np.uint16:
+            r = r.view(np.int16)
+        if r.dtype == np.float32:
+            g, r = g.view(np.uint32), r.view(np.uint32)
+        if not np.array_equal(g, r):
+            idx = np.argwhere(g != r)
+            raise AssertionError(f"{tag}: region {name} differs at {len(idx)} places, "
+                                 f"first {idx[0].tolist()}")
+    if layers is None:
+        for l in range(o.L):
+            assert S.t[l] == o.t[l], f"{tag}: t[{l}]"
+            assert S.pend_n[l] == o.pend_n[l], f"{tag}: pend_n[{l}]"

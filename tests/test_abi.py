@@ -1,0 +1,186 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol
+include/rma.h declares, reproduces the pages' memory accounting, and
+rejects bad arguments on the host before anything is enqueued."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from bounded_memory_decode_amd import rma
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rma.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(rma_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert set(names) == set(rma.EXPORTS)
+    L = rma.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    out = subprocess.run(["nm", "-D", "--defined-only", rma.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (rma_\w+)", out))
+    assert set(names) <= exported
+
+
+def test_default_config_is_edgerock_geometry():
+    c = rma.config_default()
+    assert (c.layers, c.q_heads, c.kv_groups, c.head_dim) == (8, 16, 4, 256)
+    assert (c.window, c.bank_cap, c.commit) == (1024, 1024, 256)
+    assert c.scale == 1.0 / 16
+
+
+def _golden():
+    vals = {}
+    for line in open(os.path.join(ROOT, "tests", "golden", "memory_table.txt")):
+        line = line.split("#", 1)[0].strip()
+        if line:
+            k, v = line.split()
+            vals[k] = float(v)
+    return vals
+
+
+def test_layout_matches_the_pages_memory_table():
+    """Per-sequence region sizes equal the persistent-history table of the
+    model card (32.00 / 8.00 / 31.97 MiB, 72 MiB of attention KV)."""
+    g = _golden()
+    c = rma.config_default()
+    L = rma.state_layout(c, 1)
+    mib = 2.0 ** 20
+    assert L.bank_bytes == 33_554_432 and round(L.bank_bytes / mib, 2) == g["committed_anchors_mib"]
+    assert L.pend_bytes == 8_388_608 and round(L.pend_bytes / mib, 2) == g["pending_candidates_mib"]
+    assert L.ring_bytes == 33_521_664 and round(L.ring_bytes / mib, 2) == g["local_window_kv_mib"]
+    assert round((L.ring_bytes + L.bank_bytes + L.pend_bytes) / mib) == g["attention_kv_mib"]
+    # metadata: the page prints 0.29 MiB without a layout; ours is scores,
+    # source positions and counts
+    assert 0.25 < L.meta_bytes / mib < 0.30
+    # linear in the batch apart from alignment and scratch
+    L512 = rma.state_layout(c, 512)
+    assert L512.ring_bytes == 512 * L.ring_bytes and L512.bank_bytes == 512 * L.bank_bytes
+    assert rma.state_bytes(c, 512) == L512.total_bytes
+    for name in ("ring_k", "ring_v", "bank_k", "bank_v", "pend_k", "pend_v", "bscore", "bsrc",
+                 "pscore", "bank_n", "scratch"):
+        assert getattr(L512, name) % 256 == 0
+    # regions do not overlap and are in order
+    offs = [L512.ring_k, L512.ring_v, L512.bank_k, L512.bank_v, L512.pend_k, L512.pend_v,
+            L512.bscore, L512.bsrc, L512.pscore, L512.bank_n, L512.scratch]
+    assert offs == sorted(offs)
+    assert L512.scratch + L512.scratch_bytes <= L512.total_bytes
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("head_dim", 128, rma.RMA_E_UNSUPPORTED),
+    ("q_heads", 8, rma.RMA_E_UNSUPPORTED),
+    ("q_heads", 6, rma.RMA_E_ARG),
+    ("layers", 0, rma.RMA_E_ARG),
+    ("layers", 65, rma.RMA_E_ARG),
+    ("window", 1, rma.RMA_E_ARG),
+    ("commit", 512, rma.RMA_E_UNSUPPORTED),
+    ("bank_cap", 1900, rma.RMA_E_UNSUPPORTED),
+    ("scale", float("nan"), rma.RMA_E_ARG),
+])
+def test_invalid_configs_are_rejected(field, value, code):
+    c = rma.config_default(**{field: value})
+    assert rma.state_bytes(c, 4) == 0
+    with pytest.raises(rma.RmaError) as e:
+        rma.state_layout(c, 4)
+    assert e.value.code == code
+
+
+def test_zero_batch_is_rejected():
+    c = rma.config_default()
+    assert rma.state_bytes(c, 0) == 0
+    with pytest.raises(rma.RmaError):
+        rma.state_layout(c, 0)
+
+
+def _fake_state(pend_n=0, t=32768):
+    """A host-only rma_state bound to a fake device address; only calls
+    that fail validation may be made with it."""
+    c = rma.config_default()
+    st = rma._State()
+    st.cfg = c
+    st.batch = 2
+    st.base = 0x10000000
+    st.layout = rma.state_layout(c, 2)
+    st.bytes = st.layout.total_bytes
+    for i in range(c.layers):
+        st.t[i] = t
+        st.pend_n[i] = pend_n
+        st.bank_n[i] = 1024
+    return st
+
+
+FAKE = 0x20000000  # 16-byte aligned, never dereferenced
+
+
+def _decode(st, layer=0, ptrs=None):
+    ptrs = ptrs or [FAKE] * 9
+    return rma.lib().rma_decode_step(ctypes.byref(st), layer, *ptrs)
+
+
+def test_decode_validation_on_host():
+    L = rma.lib()
+    st = _fake_state()
+    assert L.rma_decode_step(None, 0, *([FAKE] * 9)) == rma.RMA_E_ARG
+    assert _decode(st, layer=8) == rma.RMA_E_ARG
+    assert _decode(st, layer=-1) == rma.RMA_E_ARG
+    ptrs = [FAKE] * 9
+    ptrs[0] = FAKE + 2  # misaligned q
+    assert _decode(st, ptrs=ptrs) == rma.RMA_E_ARG
+    ptrs = [FAKE] * 9
+    ptrs[7] = None  # no output
+    assert _decode(st, ptrs=ptrs) == rma.RMA_E_ARG
+    full = _fake_state(pend_n=256)
+    assert _decode(full) == rma.RMA_E_PENDING_FULL
+    assert full.t[0] == 32768 and full.pend_n[0] == 256  # unchanged
+
+
+def test_admit_and_prefill_sequencing_on_host():
+    L = rma.lib()
+    st = _fake_state(pend_n=100, t=32768 + 100)
+    assert L.rma_admit(ctypes.byref(st), 0, None) == rma.RMA_E_NOT_BOUNDARY
+    assert L.rma_admit(ctypes.byref(st), -1, None) == rma.RMA_E_NOT_BOUNDARY
+    assert L.rma_admit(ctypes.byref(st), -2, None) == rma.RMA_E_ARG
+    assert L.rma_admit(ctypes.byref(st), 8, None) == rma.RMA_E_ARG
+    assert L.rma_prefill_block(ctypes.byref(st), 0, 16, *([FAKE] * 9)) == rma.RMA_E_NOT_BOUNDARY
+    st2 = _fake_state(pend_n=256)
+    assert L.rma_prefill_block(ctypes.byref(st2), 0, 16, *([FAKE] * 9)) == rma.RMA_E_NOT_BOUNDARY
+    st3 = _fake_state(pend_n=0)
+    assert L.rma_prefill_block(ctypes.byref(st3), 0, 0, *([FAKE] * 9)) == rma.RMA_E_ARG
+    assert L.rma_prefill_block(ctypes.byref(st3), 0, 257, *([FAKE] * 9)) == rma.RMA_E_ARG
+    assert st.bank_n[0] == 1024 and st.pend_n[0] == 100
+
+
+def test_state_init_validation_on_host():
+    L = rma.lib()
+    c = rma.config_default()
+    st = rma._State()
+    n = rma.state_bytes(c, 2)
+    assert L.rma_state_init(ctypes.byref(st), ctypes.byref(c), 2, None, n, 0, 0, None) == rma.RMA_E_ARG
+    assert L.rma_state_init(ctypes.byref(st), ctypes.byref(c), 2, FAKE + 16, n, 0, 0, None) == rma.RMA_E_ARG
+    assert L.rma_state_init(ctypes.byref(st), ctypes.byref(c), 2, FAKE, n - 1, 0, 0, None) == rma.RMA_E_ARG
+    assert L.rma_state_init(ctypes.byref(st), ctypes.byref(c), 2, FAKE, n, -1, 0, None) == rma.RMA_E_ARG
+    assert L.rma_state_init(ctypes.byref(st), ctypes.byref(c), 2, FAKE, n, 0, 1025, None) == rma.RMA_E_ARG
+    assert L.rma_state_init(None, ctypes.byref(c), 2, FAKE, n, 0, 0, None) == rma.RMA_E_ARG
+
+
+def test_strerror_covers_every_code():
+    L = rma.lib()
+    seen = set()
+    for code in (rma.RMA_OK, rma.RMA_E_ARG, rma.RMA_E_PENDING_FULL, rma.RMA_E_NOT_BOUNDARY,
+                 rma.RMA_E_HIP, rma.RMA_E_UNSUPPORTED):
+        s = L.rma_strerror(code).decode()
+        assert s and s != "unknown status"
+        seen.add(s)
+    assert len(seen) == 6
+    assert L.rma_strerror(12345).decode() == "unknown status"
