@@ -1,7 +1,14 @@
-// Decode step of the RMA layer on gfx950: split-K attention over the local
-// ring and the committed anchor bank, then a combine kernel that merges the
-// split partials, folds in the current token, applies the signed gate and
-// performs the ring write and the pending append.
+// Decode step of the RMA layer on gfx950: attention of each query head over
+// the local ring and over the committed anchor bank, the signed gate that
+// merges the two reads, the ring write and the pending append.
+//
+// Two launch shapes of one persistent, wave-pipelined attention kernel:
+//   * whole-unit (large batch): a wave owns a (sequence, group) unit, reads
+//     its ring then its bank, and finishes the token in-wave (current
+//     token, gate, output, ring write, pending append): one launch;
+//   * split (small batch): reads are cut into parts of 64-key tiles spread
+//     over all waves; partials go to scratch and a combine kernel finishes
+//     the token.
 //
 // Semantics: EdgeRock model card (ModelScope), "How Rock Memory Anchors
 // work" (local window of 1,024 positions, committed-bank reads, signed gate)
@@ -62,78 +69,166 @@ __device__ __forceinline__ uint16_t to_bf16(float f) {
 
 constexpr int kWaves = 4;
 
-// One work item = one part (a contiguous range of 64-key tiles) of one
-// read (ring or bank) of one (sequence, group) unit.  Items are numbered
-// unit-major: item = u * S + r, r < splits_ring for ring parts.
-struct Item {
+// A segment: one contiguous range of 64-key tiles of one read (ring or
+// bank) of one (sequence, group) unit.
+struct Seg {
   const uint4* K4;  // K plane of the unit (chunk-major, `slots` slots)
   const uint4* V4;  // V rows of the unit
   const uint4* q4;  // the unit's 4 query rows (2 KiB)
   int slots, count, ta, tb;
 };
 
-__device__ __forceinline__ Item item_info(const DecodeArgs& a, int item) {
-  const int S = a.splits_ring + a.splits_bank;
-  const int u = item / S, r = item - u * S;
+__device__ __forceinline__ Seg make_seg(const DecodeArgs& a, int u, bool ring, int t0,
+                                        int tiles) {
   const int b = u / a.G, g = u - b * a.G;
-  Item it;
-  int tiles, t0;
-  if (r < a.splits_ring) {
-    it.count = a.ring_count;
-    it.slots = a.R;
-    it.K4 = reinterpret_cast<const uint4*>(a.ring_k + (size_t)u * a.R * kD);
-    it.V4 = reinterpret_cast<const uint4*>(a.ring_v + (size_t)u * a.R * kD);
-    tiles = a.tiles_ring;
-    t0 = r * tiles;
+  Seg sg;
+  if (ring) {
+    sg.count = a.ring_count;
+    sg.slots = a.R;
+    sg.K4 = reinterpret_cast<const uint4*>(a.ring_k + (size_t)u * a.R * kD);
+    sg.V4 = reinterpret_cast<const uint4*>(a.ring_v + (size_t)u * a.R * kD);
   } else {
-    it.count = scalar_load(a.bank_n + u);
-    it.slots = a.N;
-    it.K4 = reinterpret_cast<const uint4*>(a.bank_k + (size_t)u * a.N * kD);
-    it.V4 = reinterpret_cast<const uint4*>(a.bank_v + (size_t)u * a.N * kD);
-    tiles = a.tiles_bank;
-    t0 = (r - a.splits_ring) * tiles;
+    sg.count = scalar_load(a.bank_n + u);
+    sg.slots = a.N;
+    sg.K4 = reinterpret_cast<const uint4*>(a.bank_k + (size_t)u * a.N * kD);
+    sg.V4 = reinterpret_cast<const uint4*>(a.bank_v + (size_t)u * a.N * kD);
   }
-  it.q4 = reinterpret_cast<const uint4*>(a.q + (size_t)b * a.q_bs + (size_t)g * kHpg * kD);
-  const int ntiles = (it.count + kTile - 1) / kTile;
+  sg.q4 = reinterpret_cast<const uint4*>(a.q + (size_t)b * a.q_bs + (size_t)g * kHpg * kD);
+  const int ntiles = (sg.count + kTile - 1) / kTile;
   int t1 = t0 + tiles;
   t1 = t1 < ntiles ? t1 : ntiles;
-  it.ta = t0 < t1 ? t0 : t1;
-  it.tb = t1;
-  return it;
+  sg.ta = t0 < t1 ? t0 : t1;
+  sg.tb = t1;
+  return sg;
 }
 
-// grid: persistent, a few workgroups per CU; block: 256 = 4 independent
-// waves.  Wave gw takes items gw, gw + W, gw + 2W, ... (W = all waves).
-// Per tile i of an item, in issue order:
+// Segment `sub` of work item `item`.
+//   whole-unit: item = unit, sub 0 = the ring, sub 1 = the bank;
+//   split: item = u * S + r, a single segment (part r of the ring for
+//   r < splits_ring, else part r - splits_ring of the bank).
+template <bool kWhole>
+__device__ __forceinline__ Seg seg_of(const DecodeArgs& a, int item, int sub) {
+  if (kWhole) return make_seg(a, item, sub == 0, 0, 1 << 20);
+  const int S = a.splits_ring + a.splits_bank;
+  const int u = item / S, r = item - u * S;
+  if (r < a.splits_ring) return make_seg(a, u, true, r * a.tiles_ring, a.tiles_ring);
+  return make_seg(a, u, false, (r - a.splits_ring) * a.tiles_bank, a.tiles_bank);
+}
+
+// Finish one token of unit u inside one wave (whole-unit launch): the
+// local read is the ring result (mr, lr, o_r in LDS) plus the current
+// token, the anchor read is the bank result (lb, accb in lanes 0-31); then
+// out = o_local + tanh(q . w_g) * o_anchor, the ring write and the pending
+// append.  Every read of the unit's ring by this launch is already done:
+// only this wave reads it.
+__device__ __forceinline__ void finish_unit(const DecodeArgs& a, int u, int lane,
+                                            const uint4* q_w, const float* o_r,
+                                            const float* mr, const float* lr,
+                                            const float* lb, float accb[kHpg][8]) {
+  const int b = u / a.G, g = u - b * a.G;
+  const size_t kvo = (size_t)b * a.kv_bs + (size_t)g * kD;
+  // q . k_t and q . w_g over 4 dims per lane
+  const uint2 k4 = reinterpret_cast<const uint2*>(a.k + kvo)[lane];
+  const float kf[4] = {bf_lo(k4.x), bf_hi(k4.x), bf_lo(k4.y), bf_hi(k4.y)};
+  float sc[kHpg], z[kHpg];
+#pragma unroll
+  for (int h = 0; h < kHpg; ++h) {
+    const uint2 q2 = reinterpret_cast<const uint2*>(q_w + h * kChunks)[lane];
+    const float qf[4] = {bf_lo(q2.x), bf_hi(q2.x), bf_lo(q2.y), bf_hi(q2.y)};
+    const float4 w4 = reinterpret_cast<const float4*>(a.w_g + (size_t)(g * kHpg + h) * kD)[lane];
+    float ds = qf[0] * kf[0];
+    ds = fmaf(qf[1], kf[1], ds);
+    ds = fmaf(qf[2], kf[2], ds);
+    ds = fmaf(qf[3], kf[3], ds);
+    float dz = qf[0] * w4.x;
+    dz = fmaf(qf[1], w4.y, dz);
+    dz = fmaf(qf[2], w4.z, dz);
+    dz = fmaf(qf[3], w4.w, dz);
+    sc[h] = wave_sum(ds) * a.sl2e;
+    z[h] = wave_sum(dz);
+  }
+  const int c32 = lane & 31;
+  if (lane < 32) {
+    const uint4 v4 = reinterpret_cast<const uint4*>(a.v + kvo)[c32];
+    const float vf[8] = {bf_lo(v4.x), bf_hi(v4.x), bf_lo(v4.y), bf_hi(v4.y),
+                         bf_lo(v4.z), bf_hi(v4.z), bf_lo(v4.w), bf_hi(v4.w)};
+    uint16_t* outp = a.out + (size_t)b * a.out_bs + (size_t)g * kHpg * kD + 8 * c32;
+#pragma unroll
+    for (int h = 0; h < kHpg; ++h) {
+      const float M = fmaxf(mr[h], sc[h]);
+      const float er = fast_exp2(mr[h] - M);  // ring empty: mr = -inf -> 0
+      const float ec = fast_exp2(sc[h] - M);
+      const float inv_l = 1.f / (lr[h] * er + ec);
+      const float inv_b = lb[h] > 0.f ? 1.f / lb[h] : 0.f;  // empty bank reads as zero
+      const float gate = tanhf(z[h]);
+      const float4 r0 = reinterpret_cast<const float4*>(o_r + h * kD + 8 * c32)[0];
+      const float4 r1 = reinterpret_cast<const float4*>(o_r + h * kD + 8 * c32)[1];
+      const float orr[8] = {r0.x, r0.y, r0.z, r0.w, r1.x, r1.y, r1.z, r1.w};
+      uint16_t o16[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const float oloc = fmaf(orr[i], er, ec * vf[i]) * inv_l;
+        o16[i] = to_bf16(fmaf(gate, accb[h][i] * inv_b, oloc));
+      }
+      uint4 pk;
+      pk.x = (uint32_t)o16[0] | ((uint32_t)o16[1] << 16);
+      pk.y = (uint32_t)o16[2] | ((uint32_t)o16[3] << 16);
+      pk.z = (uint32_t)o16[4] | ((uint32_t)o16[5] << 16);
+      pk.w = (uint32_t)o16[6] | ((uint32_t)o16[7] << 16);
+      *reinterpret_cast<uint4*>(outp + (size_t)h * kD) = pk;
+    }
+  }
+  // Write: ring slot t mod R, pending slot t mod C.
+  if (lane < 32) {
+    uint4* rk = reinterpret_cast<uint4*>(a.ring_k + (size_t)u * a.R * kD);
+    rk[(size_t)c32 * a.R + a.ring_slot] = reinterpret_cast<const uint4*>(a.k + kvo)[c32];
+    uint4* pk = reinterpret_cast<uint4*>(a.pend_k + ((size_t)u * a.C + a.pend_slot) * kD);
+    pk[c32] = reinterpret_cast<const uint4*>(a.ck + kvo)[c32];
+  } else {
+    uint4* rv = reinterpret_cast<uint4*>(a.ring_v + ((size_t)u * a.R + a.ring_slot) * kD);
+    rv[c32] = reinterpret_cast<const uint4*>(a.v + kvo)[c32];
+    uint4* pv = reinterpret_cast<uint4*>(a.pend_v + ((size_t)u * a.C + a.pend_slot) * kD);
+    pv[c32] = reinterpret_cast<const uint4*>(a.cv + kvo)[c32];
+  }
+  if (lane == 0) a.pscore[(size_t)u * a.C + a.pend_slot] = a.cs[(size_t)b * a.cs_bs + g];
+}
+
+// Persistent attention kernel.  grid: at most the resident workgroups;
+// block: 256 = 4 independent waves.  Wave gw takes items gw, gw + W, ...
+// (W = all waves) and walks their segments.  Per tile i, in issue order:
 //   V(i) loads -> QK(i) on K(i) already in registers -> softmax ->
-//   K(i+1) loads (or the next item's first tile and query) -> P.V(i).
+//   query rows + K(i+1) loads of the next tile, or of the next segment's
+//   first tile -> P.V(i).
 // The vector-memory counter retires loads in order, so QK(i) never waits
-// for V(i) and P.V(i) never waits for K(i+1); a wave keeps 32-66 16-byte
-// loads in flight across tile and item boundaries.  The output of an item
-// is its partial (m, l, o[4][256]) in the log2 domain, merged by the
-// combine kernel.  No workgroup barrier: each wave owns its LDS slices.
+// for V(i) and P.V(i) never waits for K(i+1): a wave keeps ~64 16-byte
+// loads in flight across tile, segment and item boundaries.  No
+// workgroup barrier: each wave owns its LDS slices.
+template <bool kWhole>
 __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a, int items) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   const int W = gridDim.x * kWaves;
   int item = blockIdx.x * kWaves + wave;
   if (item >= items) return;
+  int sub = 0;
 
   __shared__ uint4 q_s[kWaves][kHpg * kChunks];  // each wave's 4 query rows
   __shared__ float4 p_s[kWaves][kTile];          // per-key probabilities
+  __shared__ float or_s[kWhole ? kWaves : 1][kHpg * kD];  // ring result
 
   const int half = lane >> 5, c32 = lane & 31;
   uint4 kr[kChunks];
   uint4 vr[kTile / 2];
-  uint4 qn0, qn1;  // next query rows (2 x 16 B per lane)
+  uint4 qn0, qn1;  // query rows for the next segment (2 x 16 B per lane)
+  float mr[kHpg], lr[kHpg];  // whole-unit: the ring result
 
-  Item cur = item_info(a, item);
-  auto load_k = [&](const Item& it, int tile) {
+  Seg cur = seg_of<kWhole>(a, item, sub);
+  auto load_k = [&](const Seg& sg, int tile) {
     const int key = tile * kTile + lane;
-    const int hi = it.count > 0 ? it.count - 1 : 0;
+    const int hi = sg.count > 0 ? sg.count - 1 : 0;
     const int ks = key < hi ? key : hi;
 #pragma unroll
-    for (int c = 0; c < kChunks; ++c) kr[c] = it.K4[(size_t)c * it.slots + ks];
+    for (int c = 0; c < kChunks; ++c) kr[c] = sg.K4[(size_t)c * sg.slots + ks];
   };
   qn0 = cur.q4[2 * lane];
   qn1 = cur.q4[2 * lane + 1];
@@ -144,9 +239,13 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a, int item
     q_s[wave][2 * lane + 1] = qn1;
     __builtin_amdgcn_wave_barrier();
 
-    const int nitem = item + W;
+    int nitem = item, nsub = sub + 1;
+    if (!kWhole || nsub == 2) {
+      nitem = item + W;
+      nsub = 0;
+    }
     const bool has_next = nitem < items;
-    const Item nxt = item_info(a, has_next ? nitem : item);
+    const Seg nxt = seg_of<kWhole>(a, has_next ? nitem : item, has_next ? nsub : sub);
 
     float m[kHpg], l[kHpg], acc[kHpg][8];
 #pragma unroll
@@ -199,17 +298,18 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a, int item
       p_s[wave][lane] = make_float4(p[0], p[1], p[2], p[3]);
       __builtin_amdgcn_wave_barrier();
 
-      // prefetch: the next tile of this item, else the next item's first
-      // tile and query rows, else (last item) this tile again, a cache hit
+      // prefetch: the next tile of this segment, else the next segment's
+      // first tile and query rows, else (last segment) this tile again, a
+      // cache hit that keeps the loop free of conditional loads
       {
         const bool more = tile + 1 < cur.tb;
         const bool go_next = !more && has_next;
-        Item tg;
+        Seg tg;
         tg.K4 = go_next ? nxt.K4 : cur.K4;
         tg.slots = go_next ? nxt.slots : cur.slots;
         tg.count = go_next ? nxt.count : cur.count;
         const int tt = more ? tile + 1 : (go_next ? nxt.ta : tile);
-        // query rows first: the item switch then waits for them alone
+        // query rows first: the segment switch then waits for them alone
         const uint4* q4 = go_next ? nxt.q4 : cur.q4;
         qn0 = q4[2 * lane];
         qn1 = q4[2 * lane + 1];
@@ -235,41 +335,64 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a, int item
       __builtin_amdgcn_wave_barrier();
     }
 
-    // the item's partial: l over all lanes, o over the two half-waves
-    float* P = a.part + (size_t)item * kPart;
+    // segment result: l over all lanes, o over the two half-waves
 #pragma unroll
     for (int h = 0; h < kHpg; ++h) {
       l[h] = wave_sum(l[h]);
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[h][i] += __shfl_xor(acc[h][i], 32, 64);
     }
-    if (lane < 32) {
+    if (!kWhole) {
+      // the item's partial (m, l, o[4][256]) for the combine kernel
+      float* P = a.part + (size_t)item * kPart;
+      if (lane < 32) {
+#pragma unroll
+        for (int h = 0; h < kHpg; ++h) {
+          float4* dst = reinterpret_cast<float4*>(P + h * kD + 8 * c32);
+          dst[0] = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
+          dst[1] = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
+        }
+      }
+      if (lane < kHpg) {
+        float mm = m[0], ll = l[0];
+#pragma unroll
+        for (int h = 1; h < kHpg; ++h) {
+          mm = lane == h ? m[h] : mm;
+          ll = lane == h ? l[h] : ll;
+        }
+        P[kHpg * kD + lane] = mm;
+        P[kHpg * kD + kHpg + lane] = ll;
+      }
+    } else if (sub == 0) {
+      // ring result: m, l stay in registers, o goes to this wave's LDS
 #pragma unroll
       for (int h = 0; h < kHpg; ++h) {
-        float4* dst = reinterpret_cast<float4*>(P + h * kD + 8 * c32);
-        dst[0] = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
-        dst[1] = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
+        mr[h] = m[h];
+        lr[h] = l[h];
       }
-    }
-    if (lane < kHpg) {
-      float mm = m[0], ll = l[0];
+      if (lane < 32) {
 #pragma unroll
-      for (int h = 1; h < kHpg; ++h) {
-        mm = lane == h ? m[h] : mm;
-        ll = lane == h ? l[h] : ll;
+        for (int h = 0; h < kHpg; ++h) {
+          float4* dst = reinterpret_cast<float4*>(&or_s[kWhole ? wave : 0][h * kD + 8 * c32]);
+          dst[0] = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
+          dst[1] = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
+        }
       }
-      P[kHpg * kD + lane] = mm;
-      P[kHpg * kD + kHpg + lane] = ll;
+      __builtin_amdgcn_wave_barrier();
+    } else {
+      finish_unit(a, item, lane, q_s[wave], or_s[kWhole ? wave : 0], mr, lr, l, acc);
+      __builtin_amdgcn_wave_barrier();
     }
 
     if (!has_next) break;
-    if (cur.ta == cur.tb) {  // empty item: nothing was prefetched for nxt
+    if (cur.ta == cur.tb) {  // empty segment: nothing was prefetched for nxt
       qn0 = nxt.q4[2 * lane];
       qn1 = nxt.q4[2 * lane + 1];
       load_k(nxt, nxt.ta);
     }
     cur = nxt;
     item = nitem;
+    sub = nsub;
   }
 }
 
@@ -366,11 +489,11 @@ __global__ void fill_i32_kernel(int32_t* p, int32_t value, int64_t n) {
   if (i < n) p[i] = value;
 }
 
-}  // namespace
 
-// Workgroups of the attention kernel that are resident at once on the
-// current device (CUs x workgroups per CU), computed once per device.
-static int resident_workgroups() {
+// Workgroups of a kernel that are resident at once on the current device
+// (CUs x workgroups per CU), computed once per device.
+template <bool kWhole>
+int resident_workgroups() {
   static int cached[64] = {0};
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
@@ -378,21 +501,35 @@ static int resident_workgroups() {
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_attn_kernel, 256, 0) !=
-            hipSuccess || per_cu < 1)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_attn_kernel<kWhole>, 256,
+                                                     0) != hipSuccess ||
+        per_cu < 1)
       per_cu = 1;
     cached[dev] = cus * per_cu;
   }
   return cached[dev];
 }
 
+}  // namespace
+
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
+  // Whole-unit launch when there is at least one unit per resident wave and
+  // the last round of units leaves at most 1/8 of the waves idle.
+  const int res_whole = resident_workgroups<true>();
+  const int waves = res_whole * kWaves;
+  const int rounds = (a.units + waves - 1) / waves;
+  if (a.units >= waves && (int64_t)(rounds * waves - a.units) * 8 <= a.units) {
+    int grid = (a.units + kWaves - 1) / kWaves;
+    if (grid > res_whole) grid = res_whole;
+    hipLaunchKernelGGL(decode_attn_kernel<true>, dim3(grid), dim3(256), 0, s, a, a.units);
+    return hipGetLastError();
+  }
   const int S = a.splits_ring + a.splits_bank;
   const int items = a.units * S;
   int grid = (items + kWaves - 1) / kWaves;
-  const int res = resident_workgroups();
+  const int res = resident_workgroups<false>();
   if (grid > res) grid = res;
-  hipLaunchKernelGGL(decode_attn_kernel, dim3(grid), dim3(256), 0, s, a, items);
+  hipLaunchKernelGGL(decode_attn_kernel<false>, dim3(grid), dim3(256), 0, s, a, items);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_combine_kernel, dim3(a.units), dim3(256), 0, s, a);

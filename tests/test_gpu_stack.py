@@ -1,0 +1,95 @@
+"""GPU parity at batch sizes where the decode step runs as one launch per
+layer (a wave owns a whole (sequence, group) unit), including the exact
+configuration bench.py times: 512 sequences x 8 layers, state drawn on the
+device.  Sampled sequences are checked against the CPU oracle; the oracle
+gets copies of the generated inputs taken before any kernel ran."""
+import numpy as np
+import pytest
+import torch
+
+import bench
+from bounded_memory_decode_amd import rma, synth
+from oracle import OracleState
+import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+def _host_bits(t: torch.Tensor) -> np.ndarray:
+    return t.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _oracle_from_device(S: rma.State, w, batch):
+    o = OracleState(L=w.L, B=len(batch), H=w.H, G=w.G, d=w.d, R=w.R, N=w.N, C=w.C)
+    for name in ("ring_k", "ring_v", "bank_k", "bank_v", "pend_k", "pend_v"):
+        getattr(o, name)[...] = S.read(name, batch=batch).cpu().numpy().view(np.uint16)
+    for name in ("bscore", "bsrc", "pscore", "bank_n"):
+        getattr(o, name)[...] = S.read(name, batch=batch).cpu().numpy()
+    o.t[:] = S.t[:w.L]
+    o.pend_n[:] = S.pend_n[:w.L]
+    return o
+
+
+def test_whole_unit_batch256_from_empty_history():
+    """256 sequences (1,024 units): one launch per token.  Start at
+    position 0 (empty ring and bank), 300 tokens, one admit; sampled
+    outputs every 5th token, the whole state of every sequence at the end."""
+    gu.log("case whole-unit B=256 from empty history")
+    w = synth.WORKLOADS["layer_b1"].with_(B=256, t0=0, bank_n=0, ring_full=False)
+    seed = 41
+    st = synth.initial_state(w, seed)
+    S = gu.gpu_state(w, st)
+    o_all = OracleState.from_synth(st)
+    sample = [0, 97, 255]
+    o_s = OracleState.from_synth(synth.initial_state(w, seed, batch=sample))
+    wg = synth.gate_weights(w, seed)
+    wg_dev = gu.to_dev(wg[0])
+    for s in range(300):
+        x = synth.step_inputs(w, seed, 0, s)
+        out = gu.decode(S, 0, gu.inputs_to_dev(x), wg_dev)
+        o_all.decode_step(0, x["q"], x["k"], x["v"], x["ck"], x["cv"], x["cs"], wg[0],
+                          compute_out=False)
+        xs = {k: v[sample] for k, v in x.items()}
+        want = s % 5 == 0 or s in (255, 256)
+        ref = o_s.decode_step(0, xs["q"], xs["k"], xs["v"], xs["ck"], xs["cv"], xs["cs"], wg[0],
+                              compute_out=want)
+        if want:
+            gu.check_out(out[sample], ref, f"B=256 step {s}")
+        if o_all.pend_n[0] == w.C:
+            S.admit(0)
+            o_all.admit(0)
+            o_s.admit(0)
+    torch.cuda.synchronize()
+    gu.check_state(S, o_all, "B=256 end")
+
+
+@pytest.mark.parametrize("bank_n", [1024, 555])
+def test_bench_configuration_batch512_8_layers(bank_n):
+    """The launch configuration bench.py times: 512 sequences x 8 layers,
+    ring and bank full (or a partial bank), 3 tokens through all layers.
+    Outputs of sampled sequences are compared for every layer and token;
+    their ring and pending state after the tokens bit for bit."""
+    gu.log(f"case bench configuration bank_n={bank_n}")
+    w = synth.WORKLOADS["stack_b512"].with_(bank_n=bank_n)
+    seed = 3
+    dev = torch.device("cuda", 0)
+    S = bench.make_state(w, seed, dev)
+    sets, wg, outs = bench.make_pool(w, seed, dev, pool=3)
+    sample = [0, 257, 511]
+    o = _oracle_from_device(S, w, sample)
+    wgn = wg.cpu().numpy()
+    ins = [[{k: (_host_bits(v[sample]) if v.dtype == torch.bfloat16 else v[sample].cpu().numpy())
+             for k, v in sets[l][p].items()} for p in range(3)] for l in range(w.L)]
+    for step in range(3):
+        bench.run_step(S, sets, wg, outs, step)
+        torch.cuda.synchronize()
+        for l in range(w.L):
+            x = ins[l][step]
+            ref = o.decode_step(l, x["q"], x["k"], x["v"], x["ck"], x["cv"], x["cs"], wgn[l])
+            gu.check_out(outs[l][sample], ref, f"bench config step {step} layer {l}")
+    for name in ("ring_k", "ring_v", "pend_k", "pend_v", "pscore"):
+        g = S.read(name, batch=sample).cpu().numpy()
+        r = getattr(o, name)
+        r = r.view(np.int16) if r.dtype == np.uint16 else r
+        assert np.array_equal(g.view(np.uint32) if g.dtype == np.float32 else g,
+                              r.view(np.uint32) if r.dtype == np.float32 else r), name
