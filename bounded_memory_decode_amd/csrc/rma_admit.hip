@@ -137,7 +137,7 @@ __global__ __launch_bounds__(256) void admit_kernel(AdmitArgs a) {
     const int j = admitted[r];
     const int dst = r < ne ? evicted[r] : n + (r - ne);
     if (part < kChunks) {
-      bk[(size_t)part * N + dst] = pk[(size_t)j * kChunks + part];
+      bk[k_chunk_index(dst, part, N)] = pk[(size_t)j * kChunks + part];
     } else {
       const int c = part - kChunks;
       bv[(size_t)dst * kChunks + c] = pv[(size_t)j * kChunks + c];

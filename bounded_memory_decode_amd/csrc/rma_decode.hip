@@ -18,7 +18,7 @@
 // out = o_local + tanh(q . w_g) * o_anchor.
 //
 // Data layout (owned by this library, see include/rma.h): K planes are
-// stored in 16-byte chunks, chunk-major, so that a wave loading chunk c of
+// chunk-major (16-byte chunks of 8 dims), so that a wave loading chunk c of
 // 64 consecutive slots reads 1 KiB of contiguous memory with one key per
 // lane; V planes are row-major so that a half-wave loads one 512-byte row.
 // Neither read needs an LDS transpose.
@@ -181,7 +181,7 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs& a, int u, int lane
   // Write: ring slot t mod R, pending slot t mod C.
   if (lane < 32) {
     uint4* rk = reinterpret_cast<uint4*>(a.ring_k + (size_t)u * a.R * kD);
-    rk[(size_t)c32 * a.R + a.ring_slot] = reinterpret_cast<const uint4*>(a.k + kvo)[c32];
+    rk[k_chunk_index(a.ring_slot, c32, a.R)] = reinterpret_cast<const uint4*>(a.k + kvo)[c32];
     uint4* pk = reinterpret_cast<uint4*>(a.pend_k + ((size_t)u * a.C + a.pend_slot) * kD);
     pk[c32] = reinterpret_cast<const uint4*>(a.ck + kvo)[c32];
   } else {
@@ -223,12 +223,14 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a, int item
   float mr[kHpg], lr[kHpg];  // whole-unit: the ring result
 
   Seg cur = seg_of<kWhole>(a, item, sub);
+  // K of one tile: chunk c of the lane's key (keys past the count re-read
+  // the last valid key)
   auto load_k = [&](const Seg& sg, int tile) {
     const int key = tile * kTile + lane;
     const int hi = sg.count > 0 ? sg.count - 1 : 0;
     const int ks = key < hi ? key : hi;
 #pragma unroll
-    for (int c = 0; c < kChunks; ++c) kr[c] = sg.K4[(size_t)c * sg.slots + ks];
+    for (int c = 0; c < kChunks; ++c) kr[c] = sg.K4[k_chunk_index(ks, c, sg.slots)];
   };
   qn0 = cur.q4[2 * lane];
   qn1 = cur.q4[2 * lane + 1];
@@ -299,21 +301,29 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a, int item
       __builtin_amdgcn_wave_barrier();
 
       // prefetch: the next tile of this segment, else the next segment's
-      // first tile and query rows, else (last segment) this tile again, a
-      // cache hit that keeps the loop free of conditional loads
+      // first tile and query rows.  Loads with nothing to fetch (the query
+      // rows while the segment continues, K after the last segment) re-read
+      // the V row this lane loaded above, a cache hit; base and stride are
+      // selected on the scalar unit, so the loop stays free of branches.
       {
         const bool more = tile + 1 < cur.tb;
         const bool go_next = !more && has_next;
-        Seg tg;
-        tg.K4 = go_next ? nxt.K4 : cur.K4;
-        tg.slots = go_next ? nxt.slots : cur.slots;
-        tg.count = go_next ? nxt.count : cur.count;
-        const int tt = more ? tile + 1 : (go_next ? nxt.ta : tile);
+        const bool idle = !more && !has_next;
+        const int vrow = tbase + half < cur.count ? tbase + half : cur.count - 1;
+        const int voff = vrow * kChunks + c32;
         // query rows first: the segment switch then waits for them alone
-        const uint4* q4 = go_next ? nxt.q4 : cur.q4;
-        qn0 = q4[2 * lane];
-        qn1 = q4[2 * lane + 1];
-        load_k(tg, tt);
+        const uint4* qb = go_next ? nxt.q4 : cur.V4;
+        qn0 = qb[go_next ? 2 * lane : voff];
+        qn1 = qb[go_next ? 2 * lane + 1 : voff];
+        const int ktile = more ? tile + 1 : nxt.ta;
+        const int kcount = more ? cur.count : nxt.count;
+        const uint4* kb = idle ? cur.V4 : (more ? cur.K4 : nxt.K4);
+        const int kstride = idle ? 0 : (more ? cur.slots : nxt.slots);
+        const int key = ktile * kTile + lane;
+        const int hi = kcount > 0 ? kcount - 1 : 0;
+        const int koff = idle ? voff : (key < hi ? key : hi);
+#pragma unroll
+        for (int c = 0; c < kChunks; ++c) kr[c] = kb[(size_t)c * kstride + koff];
       }
       __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of P.V
 
@@ -469,7 +479,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   // slot t mod C takes the candidate record and score.
   if (tid < 32) {
     uint4* rk = reinterpret_cast<uint4*>(a.ring_k + (size_t)u * a.R * kD);
-    rk[(size_t)tid * a.R + a.ring_slot] = reinterpret_cast<const uint4*>(a.k + kvo)[tid];
+    rk[k_chunk_index(a.ring_slot, tid, a.R)] = reinterpret_cast<const uint4*>(a.k + kvo)[tid];
   } else if (tid < 64) {
     uint4* rv = reinterpret_cast<uint4*>(a.ring_v + ((size_t)u * a.R + a.ring_slot) * kD);
     rv[tid - 32] = reinterpret_cast<const uint4*>(a.v + kvo)[tid - 32];

@@ -190,16 +190,17 @@ class State:
 
     def region_view(self, name: str) -> torch.Tensor:
         """A view of one region in its stored layout (int16 for bf16 bits):
-        ring_k/bank_k [L][B][G][d/8][slots][8], ring_v/bank_v [L][B][G][slots][d],
+        ring_k/bank_k [L][B][G][slots*d] (16-byte chunks, chunk-major, see
+        include/rma.h), ring_v/bank_v [L][B][G][slots][d],
         pend_k/pend_v [L][B][G][C][d], bscore/bsrc [L][B][G][N],
         pscore [L][B][G][C], bank_n [L][B][G]."""
         c = self.cfg
         L, B, G, d = c.layers, self.batch, c.kv_groups, c.head_dim
         R, N, C = c.window - 1, c.bank_cap, c.commit
         shapes = {
-            "ring_k": ((L, B, G, d // 8, R, 8), torch.int16),
+            "ring_k": ((L, B, G, R * d), torch.int16),
             "ring_v": ((L, B, G, R, d), torch.int16),
-            "bank_k": ((L, B, G, d // 8, N, 8), torch.int16),
+            "bank_k": ((L, B, G, N * d), torch.int16),
             "bank_v": ((L, B, G, N, d), torch.int16),
             "pend_k": ((L, B, G, C, d), torch.int16),
             "pend_v": ((L, B, G, C, d), torch.int16),
@@ -219,9 +220,9 @@ class State:
         region `name` for the given layer/sequence slices."""
         v = self.region_view(name)
         if name in ("ring_k", "bank_k"):
-            dst = v[layers, batch].permute(0, 1, 2, 4, 3, 5)  # [l][b][G][S][d/8][8]
-            src = _as_bits(value).to(self.device)
-            dst.copy_(src.reshape(dst.shape))
+            dst = v[layers, batch]
+            src = _as_bits(value).to(self.device).reshape(*dst.shape[:3], -1, self.cfg.head_dim)
+            dst.copy_(_k_to_stored(src))
         else:
             dst = v[layers, batch]
             if dst.dtype == torch.int16:
@@ -234,8 +235,7 @@ class State:
         """Copy of region `name` in the natural layout (bf16 bits as int16)."""
         v = self.region_view(name)
         if name in ("ring_k", "bank_k"):
-            x = v[layers, batch].permute(0, 1, 2, 4, 3, 5).contiguous()
-            return x.reshape(*x.shape[:4], -1)
+            return _k_to_natural(v[layers, batch], self.cfg.head_dim)
         return v[layers, batch].clone()
 
     # ------------------------------------------------------------- compute
@@ -291,6 +291,20 @@ def _as_bits(x) -> torch.Tensor:
     if x.dtype == torch.int16:
         return x
     raise TypeError(f"expected bf16 bits, got {x.dtype}")
+
+
+def _k_to_stored(nat: torch.Tensor) -> torch.Tensor:
+    """[..., S, d] K rows -> [..., S*d] in the stored K order: 16-byte
+    chunks of 8 dims, chunk-major over the plane."""
+    *lead, S, d = nat.shape
+    return nat.reshape(*lead, S, d // 8, 8).transpose(-3, -2).reshape(*lead, S * d)
+
+
+def _k_to_natural(stored: torch.Tensor, d: int) -> torch.Tensor:
+    """Inverse of _k_to_stored: [..., S*d] -> [..., S, d] (a copy)."""
+    *lead, n = stored.shape
+    S = n // d
+    return stored.reshape(*lead, d // 8, S, 8).transpose(-3, -2).reshape(*lead, S, d)
 
 
 def _as_tensor(x) -> torch.Tensor:

@@ -94,8 +94,8 @@ typedef struct {
  * 256-byte aligned.  R = window-1, N = bank_cap, C = commit, d = head_dim.
  *
  *   ring_k  [units][d/8][R][8] bf16   K, split in 16-byte chunks of 8 dims,
- *                                     chunk-major (chunk c of slot s is at
- *                                     ((u*(d/8) + c)*R + s)*16 bytes)
+ *                                     chunk-major: chunk c of slot s is at
+ *                                     uint4 index c*R + s of the unit's plane
  *   ring_v  [units][R][d]      bf16   V rows
  *   bank_k  [units][d/8][N][8] bf16   as ring_k with N slots
  *   bank_v  [units][N][d]      bf16

@@ -184,3 +184,19 @@ def test_strerror_covers_every_code():
         seen.add(s)
     assert len(seen) == 6
     assert L.rma_strerror(12345).decode() == "unknown status"
+
+
+@pytest.mark.parametrize("S", [1023, 1024, 64, 63, 130, 1])
+def test_k_plane_layout_helpers_follow_the_header(S):
+    """The binding's natural <-> stored K conversion puts chunk c of slot s
+    at uint4 index c*S + s, as include/rma.h states."""
+    import torch
+    from bounded_memory_decode_amd.rma import _k_to_natural, _k_to_stored
+    d = 256
+    nat = torch.arange(S * d, dtype=torch.int64).reshape(1, S, d)
+    st = _k_to_stored(nat)[0]
+    for s in sorted({x for x in (0, 5, 63, S - 1, S // 2) if x < S}):
+        for c in (0, 7, 31):
+            i = (c * S + s) * 8
+            assert torch.equal(st[i:i + 8], nat[0, s, 8 * c:8 * c + 8])
+    assert torch.equal(_k_to_natural(st[None], d), nat)
