@@ -262,28 +262,40 @@ int rma_prefill_block(rma_state* st, int32_t layer, int32_t n_tokens, const void
     return RMA_E_ARG;
   const int64_t t0 = st->t[layer];
   if (st->pend_n[layer] != 0 || t0 % c.commit != 0) return RMA_E_NOT_BOUNDARY;
-  const int64_t H = c.q_heads, G = c.kv_groups, n = n_tokens;
-  const uint16_t* q16 = static_cast<const uint16_t*>(q);
-  const uint16_t* k16 = static_cast<const uint16_t*>(k);
-  const uint16_t* v16 = static_cast<const uint16_t*>(v);
-  const uint16_t* ck16 = static_cast<const uint16_t*>(cand_k);
-  const uint16_t* cv16 = static_cast<const uint16_t*>(cand_v);
-  uint16_t* o16 = static_cast<uint16_t*>(out);
-  // token i of every sequence: rows i of the [B][n][...] inputs
-  for (int64_t i = 0; i < n; ++i) {
-    const rma::DecodeArgs a =
-        decode_args(st, layer, t0 + i, q16 + i * H * kD, k16 + i * G * kD, v16 + i * G * kD,
-                    ck16 + i * G * kD, cv16 + i * G * kD, cand_score + i * G, w_g,
-                    o16 + i * H * kD, n * H * kD, n * G * kD, n * G, n * H * kD);
-    const hipError_t e = rma::launch_decode(a, static_cast<hipStream_t>(stream));
-    if (e != hipSuccess) {
-      st->t[layer] = t0 + i;
-      st->pend_n[layer] = (int32_t)i;
-      return hip_fail(st, e);
-    }
-  }
-  st->t[layer] = t0 + n;
-  st->pend_n[layer] = (int32_t)n;
+  const rma_layout& L = st->layout;
+  const int B = st->batch, G = c.kv_groups;
+  const int R = c.window - 1, N = c.bank_cap, C = c.commit;
+  const uint64_t unit0 = (uint64_t)layer * B * G;
+  rma::PrefillArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.ck = static_cast<const uint16_t*>(cand_k);
+  a.cv = static_cast<const uint16_t*>(cand_v);
+  a.cs = cand_score;
+  a.w_g = w_g;
+  a.out = static_cast<uint16_t*>(out);
+  a.ring_k = region<uint16_t>(st, L.ring_k) + unit0 * R * kD;
+  a.ring_v = region<uint16_t>(st, L.ring_v) + unit0 * R * kD;
+  a.bank_k = region<uint16_t>(st, L.bank_k) + unit0 * N * kD;
+  a.bank_v = region<uint16_t>(st, L.bank_v) + unit0 * N * kD;
+  a.bank_n = region<int32_t>(st, L.bank_n) + unit0;
+  a.pend_k = region<uint16_t>(st, L.pend_k) + unit0 * C * kD;
+  a.pend_v = region<uint16_t>(st, L.pend_v) + unit0 * C * kD;
+  a.pscore = region<float>(st, L.pscore) + unit0 * C;
+  a.B = B;
+  a.G = G;
+  a.H = c.q_heads;
+  a.R = R;
+  a.N = N;
+  a.C = C;
+  a.n = n_tokens;
+  a.P = t0;
+  a.sl2e = (float)((double)c.scale * 1.4426950408889634);
+  const hipError_t e = rma::launch_prefill(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(st, e);
+  st->t[layer] = t0 + n_tokens;
+  st->pend_n[layer] = n_tokens;
   return RMA_OK;
 }
 

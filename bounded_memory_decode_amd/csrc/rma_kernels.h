@@ -58,6 +58,32 @@ struct DecodeArgs {
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 
+// A chunked-prefill block of one layer.
+struct PrefillArgs {
+  const uint16_t* q;       // [B][n][H][D]
+  const uint16_t* k;       // [B][n][G][D]
+  const uint16_t* v;
+  const uint16_t* ck;
+  const uint16_t* cv;
+  const float* cs;         // [B][n][G]
+  const float* w_g;        // [H][D]
+  uint16_t* out;           // [B][n][H][D]
+  uint16_t* ring_k;        // layer bases as in DecodeArgs
+  uint16_t* ring_v;
+  const uint16_t* bank_k;
+  const uint16_t* bank_v;
+  const int32_t* bank_n;
+  uint16_t* pend_k;
+  uint16_t* pend_v;
+  float* pscore;
+  int B, G, H, R, N, C;
+  int n;                   // tokens in the block (1 .. C)
+  int64_t P;               // position of the block's first token (P % C == 0)
+  float sl2e;              // scale * log2(e)
+};
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
+
 // Admit of one or more layers.
 struct AdmitArgs {
   uint16_t* bank_k;        // region base (unit 0)

@@ -63,16 +63,28 @@ def out_errors(gpu: torch.Tensor, ref: np.ndarray):
     return err, np.abs(ref).max()
 
 
-def check_out(gpu: torch.Tensor, ref: np.ndarray, tag: str):
+def check_out(gpu: torch.Tensor, ref: np.ndarray, tag: str, p_bf16_vmax: float = 0.0):
+    """Compare bf16 outputs with the oracle's unrounded doubles.
+
+    p_bf16_vmax: for a path that rounds the softmax weights to bf16 before
+    P.V (the MFMA prefill), each weight carries a relative error <= 2^-9,
+    which moves a normalised read by at most 2^-9 * max|V| of the keys it
+    reads (independent of |out|); the local and anchor reads together (gate
+    magnitude <= 1) give 2^-8 * max|V|.  Pass that max|V| here."""
     err, scale = out_errors(gpu, ref)
     emax = err.max()
     assert emax <= ABS_BOUND, f"{tag}: max abs error {emax:.3e} > {ABS_BOUND}"
     assert emax <= REL_BOUND * scale, f"{tag}: max error {emax:.3e} > 1e-2 * {scale:.3e}"
-    bound = 2.0 ** -8 * np.abs(ref) + 1e-3 * scale
+    bound = 2.0 ** -8 * np.abs(ref) + 1e-3 * scale + 2.0 ** -8 * p_bf16_vmax
     bad = err > bound
     assert not bad.any(), (f"{tag}: {bad.sum()} elements beyond 2^-8|ref| + 1e-3 max|ref|; "
                            f"worst {err[bad].max():.3e}")
     return emax, scale
+
+
+def vmax(*arrays) -> float:
+    """Largest |value| among bf16 bit arrays."""
+    return max(float(np.abs(synth.bf16_to_f32(a)).max()) for a in arrays)
 
 
 def bits(t: torch.Tensor) -> np.ndarray:

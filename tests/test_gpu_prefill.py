@@ -1,0 +1,149 @@
+"""GPU parity of the chunked-prefill block (MFMA path) against the CPU
+oracle, which defines a block as its tokens decoded in order with no admit
+inside; plus prefill/decode equivalence on the GPU itself."""
+import numpy as np
+import pytest
+import torch
+
+from bounded_memory_decode_amd import rma, synth
+from oracle import OracleState
+import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+def _prefill(S, layer, x, wg_dev):
+    d = gu.inputs_to_dev(x)
+    return S.prefill_block(layer, d["q"], d["k"], d["v"], d["ck"], d["cv"], d["cs"], wg_dev)
+
+
+def _run_blocks(w, seed, sizes, decode_after=0, check_state_each=True):
+    """Prefill blocks of the given sizes (each starting on a block
+    boundary: a short block is completed by decode steps), admitting at
+    every block end; compare every output and the state."""
+    st = synth.initial_state(w, seed)
+    S = gu.gpu_state(w, st)
+    o = OracleState.from_synth(st, H=w.H, G=w.G, d=w.d, R=w.R, N=w.N, C=w.C)
+    wg = synth.gate_weights(w, seed)
+    wg_dev = gu.to_dev(wg[0])
+    step = 0
+    worst = 0.0
+    for n in sizes:
+        x = synth.block_inputs(w, seed, 0, step, n)
+        vm = gu.vmax(o.ring_v, o.bank_v, x["v"])
+        out = _prefill(S, 0, x, wg_dev)
+        ref = o.prefill_block(0, x["q"], x["k"], x["v"], x["ck"], x["cv"], x["cs"], wg[0])
+        e, _ = gu.check_out(out, ref, f"{w.name} prefill n={n} at step {step}", p_bf16_vmax=vm)
+        worst = max(worst, e)
+        step += n
+        # finish the block with decode steps, then admit
+        while o.pend_n[0] < w.C:
+            xs = synth.step_inputs(w, seed, 0, step)
+            outd = gu.decode(S, 0, gu.inputs_to_dev(xs), wg_dev)
+            refd = o.decode_step(0, xs["q"], xs["k"], xs["v"], xs["ck"], xs["cv"], xs["cs"], wg[0])
+            gu.check_out(outd, refd, f"{w.name} decode after prefill, step {step}")
+            step += 1
+        if check_state_each:
+            torch.cuda.synchronize()
+            gu.check_state(S, o, f"{w.name} block ending at {step}")
+        S.admit(0)
+        o.admit(0)
+    for _ in range(decode_after):
+        xs = synth.step_inputs(w, seed, 0, step)
+        outd = gu.decode(S, 0, gu.inputs_to_dev(xs), wg_dev)
+        refd = o.decode_step(0, xs["q"], xs["k"], xs["v"], xs["ck"], xs["cv"], xs["cs"], wg[0])
+        gu.check_out(outd, refd, f"{w.name} decode step {step}")
+        step += 1
+    torch.cuda.synchronize()
+    gu.check_state(S, o, f"{w.name} end")
+    gu.log(f"{w.name}: blocks {sizes}, worst prefill error {worst:.3e}")
+
+
+def test_full_block_on_full_history():
+    gu.log("case prefill full block, B=2, full ring and bank")
+    w = synth.WORKLOADS["layer_b1"].with_(B=2)
+    _run_blocks(w, 50, [256, 256], decode_after=3)
+
+
+def test_ragged_blocks_and_query_tile_edges():
+    """Blocks of 1, 17, 100 and 255 tokens (query tiles of 16 tokens with
+    ragged tails), each completed by decode steps."""
+    gu.log("case prefill ragged blocks")
+    w = synth.WORKLOADS["layer_b1"].with_(B=1, bank_n=600)
+    _run_blocks(w, 51, [1, 17, 100, 255])
+
+
+def test_from_empty_history():
+    """Position 0: the ring fills over the first four blocks (P < R), the
+    bank starts empty and grows by 256 per admit."""
+    gu.log("case prefill from empty history")
+    w = synth.WORKLOADS["layer_b1"].with_(B=2, t0=0, bank_n=0, ring_full=False)
+    _run_blocks(w, 52, [256, 256, 256, 256, 256], decode_after=2)
+
+
+def test_sharp_inputs():
+    gu.log("case prefill sharp")
+    w = synth.WORKLOADS["sharp_b1"]
+    _run_blocks(w, 53, [256, 130])
+
+
+def test_prefill_equals_decode_on_gpu():
+    """The same 256 tokens through one prefill call and through 256 decode
+    calls: identical state bit for bit, outputs within the bound."""
+    gu.log("case prefill == decode")
+    w = synth.WORKLOADS["layer_b1"].with_(B=3, bank_n=900)
+    seed = 54
+    st = synth.initial_state(w, seed)
+    A = gu.gpu_state(w, st)
+    D = gu.gpu_state(w, st)
+    wg = synth.gate_weights(w, seed)
+    wg_dev = gu.to_dev(wg[0])
+    x = synth.block_inputs(w, seed, 0, 0, w.C)
+    outp = _prefill(A, 0, x, wg_dev)
+    outs = []
+    for i in range(w.C):
+        xs = {k: v[:, i] for k, v in x.items()}
+        outs.append(gu.decode(D, 0, gu.inputs_to_dev(xs), wg_dev).clone())
+    outd = torch.stack(outs, dim=1)
+    err = (outp.float() - outd.float()).abs().max().item()
+    scale = outd.float().abs().max().item()
+    assert err <= 2e-2 and err <= 1e-2 * scale, err
+    torch.cuda.synchronize()
+    for name in gu.REGIONS + ("bank_n",):
+        assert torch.equal(A.read(name), D.read(name)), name
+    assert A.t == D.t and A.pend_n == D.pend_n
+
+
+def test_long_prompt_start_eight_layers():
+    """The long single-sequence shape: 8 layers from position 0, the first
+    4 blocks of the prompt per layer with an admit of all layers after each
+    block, then decode steps; every output and the final state."""
+    gu.log("case long prompt, 8 layers")
+    w = synth.WORKLOADS["long_b1"]
+    seed = 55
+    st = synth.initial_state(w, seed)
+    S = gu.gpu_state(w, st)
+    o = OracleState.from_synth(st)
+    wg = synth.gate_weights(w, seed)
+    wg_dev = [gu.to_dev(wg[l]) for l in range(w.L)]
+    step = 0
+    for blk in range(4):
+        for l in range(w.L):
+            x = synth.block_inputs(w, seed, l, step, w.C)
+            vm = gu.vmax(o.ring_v[l], o.bank_v[l], x["v"])
+            out = _prefill(S, l, x, wg_dev[l])
+            ref = o.prefill_block(l, x["q"], x["k"], x["v"], x["ck"], x["cv"], x["cs"], wg[l])
+            gu.check_out(out, ref, f"long block {blk} layer {l}", p_bf16_vmax=vm)
+        S.admit(-1)
+        for l in range(w.L):
+            o.admit(l)
+        step += w.C
+    for s in range(4):
+        for l in range(w.L):
+            xs = synth.step_inputs(w, seed, l, step)
+            outd = gu.decode(S, l, gu.inputs_to_dev(xs), wg_dev[l])
+            refd = o.decode_step(l, xs["q"], xs["k"], xs["v"], xs["ck"], xs["cv"], xs["cs"], wg[l])
+            gu.check_out(outd, refd, f"long decode step {step} layer {l}")
+        step += 1
+    torch.cuda.synchronize()
+    gu.check_state(S, o, "long end")
