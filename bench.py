@@ -112,7 +112,7 @@ def make_pool(w, seed, device, pool=POOL):
     return sets, wg, outs
 
 
-def run_step(S, sets, wg, outs, step, events=None):
+def run_step(S, sets, wg, outs, step, events=None, admit_events=None):
     """One token through all layers (+ admit at the block end)."""
     L = S.cfg.layers
     for l in range(L):
@@ -123,14 +123,87 @@ def run_step(S, sets, wg, outs, step, events=None):
         if events is not None:
             events[l][1].record()
     if S.pend_n[0] == S.cfg.commit:
+        if admit_events is not None:
+            admit_events.append((_event(), _event()))
+            admit_events[-1][0].record()
         S.admit(-1)
+        if admit_events is not None:
+            admit_events[-1][1].record()
         return True
     return False
 
 
-def cpu_baseline(S, w, sets, wg, sample_b: int, seed: int):
+def _event():
+    import torch
+    return torch.cuda.Event(enable_timing=True)
+
+
+# Prefill work of one 256-token block of one layer with a full ring and
+# bank, masked work excluded: per group, 1,024 query rows (256 tokens x 4
+# heads) each against 1,024 local keys and 1,024 anchors, QK and PV at
+# 2 flop per multiply-add over 256 dims.
+PREFILL_FLOP_PER_GROUP = 1024 * (1024 + 1024) * 256 * 2 * 2   # 2.147 GFLOP
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+
+
+def bench_prefill(device, seed, batch, blocks):
+    """Time rma_prefill_block on full-history states: `blocks` blocks of
+    256 tokens through all 8 layers, admit after each block."""
+    import torch
+    from bounded_memory_decode_amd import synth
+    w = synth.WORKLOADS["stack_b512"].with_(B=batch)
+    S = make_state(w, seed, device)
+    n = w.C
+    ins = []
+    for l in range(w.L):
+        key = lambda kind: (w.wid, synth.KIND[kind], l, 99, 2)
+        ins.append({
+            "q": synth.torch_normal_bf16((w.B, n, w.H, w.d), w.qkv_std, seed, device, key("q")),
+            "k": synth.torch_normal_bf16((w.B, n, w.G, w.d), w.qkv_std, seed, device, key("k")),
+            "v": synth.torch_normal_bf16((w.B, n, w.G, w.d), w.qkv_std, seed, device, key("v")),
+            "ck": synth.torch_normal_bf16((w.B, n, w.G, w.d), w.qkv_std, seed, device, key("ck")),
+            "cv": synth.torch_normal_bf16((w.B, n, w.G, w.d), w.qkv_std, seed, device, key("cv")),
+            "cs": synth.torch_scores((w.B, n, w.G), w, seed, device, key("cs")),
+        })
+    wg = (torch.randn((w.L, w.H, w.d), device=device) * w.w_std).contiguous()
+    outs = [torch.empty((w.B, n, w.H, w.d), dtype=torch.bfloat16, device=device) for _ in range(w.L)]
+
+    def block(ev=None):
+        for l in range(w.L):
+            x = ins[l]
+            if ev is not None:
+                ev[l][0].record()
+            S.prefill_block(l, x["q"], x["k"], x["v"], x["ck"], x["cv"], x["cs"], wg[l], outs[l])
+            if ev is not None:
+                ev[l][1].record()
+        S.admit(-1)
+
+    block()  # warm-up
+    torch.cuda.synchronize()
+    evs = [[(_event(), _event()) for _ in range(w.L)] for _ in range(blocks)]
+    for b in range(blocks):
+        block(evs[b])
+    torch.cuda.synchronize()
+    ms = [e0.elapsed_time(e1) for ev in evs for e0, e1 in ev]
+    avg_ms = sum(ms) / len(ms)
+    flop = PREFILL_FLOP_PER_GROUP * w.G * w.B
+    tflops = flop / (avg_ms * 1e-3) / 1e12
+    del S
+    torch.cuda.empty_cache()
+    return {"workload": f"{w.L} layers x batch {w.B}, 256-token blocks on a full ring and bank "
+                        f"(position {w.t0})",
+            "batch": w.B, "blocks": blocks, "us_per_block_layer": round(avg_ms * 1e3, 2),
+            "prefill_tokens_per_s": round(w.B * n / (avg_ms * 1e-3 * w.L), 1),
+            "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
+                         "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "flop_per_launch": flop,
+                         "kernel": "prefill_attn_kernel + prefill_commit_kernel (one layer, one block)"}}
+
+
+def cpu_baseline(S, w, sets, wg, sample_b: int, seed: int, steps: int = 8):
     """The oracle, timed on the host cores on a bounded sample: `sample_b`
-    sequences of the same state, one token through all layers."""
+    sequences of the same state, `steps` tokens through all layers."""
     import numpy as np
     import torch
     import oracle
@@ -144,22 +217,26 @@ def cpu_baseline(S, w, sets, wg, sample_b: int, seed: int):
         getattr(o, name)[...] = S.read(name, batch=b_idx).cpu().numpy()
     o.t[:] = S.t[:w.L]
     o.pend_n[:] = S.pend_n[:w.L]
-    ins = []
-    for l in range(w.L):
-        x = sets[l][0]
-        ins.append({k: (v[:sample_b].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
-                        if v.dtype == torch.bfloat16 else v[:sample_b].cpu().numpy())
-                    for k, v in x.items()})
+    ins = [[{k: (v[:sample_b].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+                 if v.dtype == torch.bfloat16 else v[:sample_b].cpu().numpy())
+             for k, v in sets[l][p].items()} for p in range(len(sets[l]))] for l in range(w.L)]
     wgn = wg.cpu().numpy()
+    admits = 0
     t0 = time.perf_counter()
-    for l in range(w.L):
-        x = ins[l]
-        o.decode_step(l, x["q"], x["k"], x["v"], x["ck"], x["cv"], x["cs"], wgn[l])
+    for s in range(steps):
+        for l in range(w.L):
+            x = ins[l][s % len(ins[l])]
+            o.decode_step(l, x["q"], x["k"], x["v"], x["ck"], x["cv"], x["cs"], wgn[l])
+        if o.pend_n[0] == w.C:
+            for l in range(w.L):
+                o.admit(l)
+            admits += 1
     dt = time.perf_counter() - t0
     cores = oracle.num_threads()
-    return {"value": sample_b / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": f"{sample_b} of {w.B} sequences, 1 token through all {w.L} layers "
-                      f"(decode + ring write + pending append), {dt:.2f} s wall on {cores} threads"}
+    return {"value": sample_b * steps / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"{sample_b} of {w.B} sequences, {steps} tokens through all {w.L} layers "
+                      f"(decode, ring write, pending append; {admits} admit rounds), "
+                      f"{dt:.2f} s wall on {cores} threads"}
 
 
 def read_traffic(sha: str):
@@ -190,6 +267,10 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--cpu-sample", type=int, default=32,
                     help="sequences in the CPU-oracle sample (0: skip)")
+    ap.add_argument("--cpu-steps", type=int, default=8,
+                    help="tokens per sequence in the CPU-oracle sample")
+    ap.add_argument("--prefill-blocks", type=int, default=4,
+                    help="256-token blocks timed per prefill batch size (0: skip)")
     ap.add_argument("--calibration-copy-gib", type=int, default=0,
                     help="before timing, copy a buffer of this many GiB three times "
                          "(a plain copy kernel of known size, for scaling HBM counters)")
@@ -239,11 +320,12 @@ def main():
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     say(f"[bench] timing {K} steps")
     admits = 0
+    admit_ev = []
     torch.cuda.synchronize()
     t_wall = time.perf_counter()
     start.record()
     for s in range(K):
-        admits += run_step(S, sets, wg, outs, args.warmup + s, ev[s])
+        admits += run_step(S, sets, wg, outs, args.warmup + s, ev[s], admit_ev)
     stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall
@@ -289,11 +371,28 @@ def main():
                      "kernel_sources_sha": sha},
         "cpu_baseline": None,
     }
+    if admit_ev:
+        adm_ms = [a.elapsed_time(b) for a, b in admit_ev]
+        result["admit"] = {"workload": f"all {w.L} layers x batch {w.B} x 4 groups: top-1024 of "
+                                       f"1024 anchors + 256 candidates each",
+                           "rounds": len(adm_ms), "ms_per_round": round(sum(adm_ms) / len(adm_ms), 4),
+                           "selections_per_s": round(w.L * w.B * w.G / (sum(adm_ms) / len(adm_ms) * 1e-3))}
     say(f"[bench] {tokens_s:,.0f} tok/s, {ms_step:.3f} ms/step, decode launch {dec_avg_ms*1e3:.1f} us "
         f"= {achieved:,.0f} GB/s ({100*achieved/HBM_PEAK_GBS:.1f}% of peak); wall {wall:.2f} s")
     if args.cpu_sample > 0:
-        say(f"[bench] CPU oracle on {args.cpu_sample} sequences")
-        result["cpu_baseline"] = cpu_baseline(S, w, sets, wg, args.cpu_sample, args.seed)
+        say(f"[bench] CPU oracle on {args.cpu_sample} sequences x {args.cpu_steps} tokens")
+        result["cpu_baseline"] = cpu_baseline(S, w, sets, wg, args.cpu_sample, args.seed,
+                                              args.cpu_steps)
+    if args.prefill_blocks > 0:
+        del S, sets, outs
+        torch.cuda.empty_cache()
+        result["prefill"] = []
+        for pb in (1, 8):
+            say(f"[bench] prefill, batch {pb}")
+            r = bench_prefill(device, args.seed, pb, args.prefill_blocks)
+            say(f"[bench] prefill batch {pb}: {r['us_per_block_layer']} us per block-layer, "
+                f"{r['roofline']['achieved']} TFLOP/s ({100 * r['roofline']['frac']:.1f}% of bf16 MFMA peak)")
+            result["prefill"].append(r)
     print(json.dumps(result), flush=True)
 
 

@@ -47,15 +47,33 @@ __device__ __forceinline__ uint16_t to_bf16(float f) {
 
 __device__ __forceinline__ float bf2f(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
 
+// All-reduce over each row of 16 lanes with DPP moves (single-cycle VALU
+// operand swizzles, no LDS round trip): swap neighbours, swap pairs, then
+// mirror within 8 and within 16 lanes.  After the first two steps the 4
+// lanes of a quad agree, so each mirror combines two already-reduced
+// groups.
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), kCtrl, 0xf, 0xf, false));
+}
+constexpr int kQuadSwap1 = 0xB1;     // quad_perm [1,0,3,2]
+constexpr int kQuadSwap2 = 0x4E;     // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+
 __device__ __forceinline__ float row16_max(float x) {
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
+  x = fmaxf(x, dpp<kQuadSwap1>(x));
+  x = fmaxf(x, dpp<kQuadSwap2>(x));
+  x = fmaxf(x, dpp<kRowHalfMirror>(x));
+  x = fmaxf(x, dpp<kRowMirror>(x));
   return x;
 }
 
 __device__ __forceinline__ float row16_sum(float x) {
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) x += __shfl_xor(x, o, 64);
+  x += dpp<kQuadSwap1>(x);
+  x += dpp<kQuadSwap2>(x);
+  x += dpp<kRowHalfMirror>(x);
+  x += dpp<kRowMirror>(x);
   return x;
 }
 
@@ -117,23 +135,45 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillArgs a) {
   };
   auto seg_count = [&](int seg) { return seg == kSegRing ? ring_valid : (seg == kSegBlock ? n : nb); };
 
+  // Uniform (scalar) source of tile t: base, key stride and chunk stride in
+  // 16-byte units for K; base and key stride for V rows.  Ring and bank K
+  // planes are chunk-major (key stride 1, chunk stride = slots); the
+  // block's K and V are rows of the [B][n][G][D] inputs.
+  struct Src {
+    const uint4* k;
+    const uint4* v;
+    int kks, kcs, vks, cnt, ti;
+  };
+  auto src_of = [&](int t) {
+    Src sr;
+    int seg, ti;
+    seg_of(t, seg, ti);
+    const uint4* kblk = reinterpret_cast<const uint4*>(a.k + ((size_t)b * n * a.G + g) * kD);
+    const uint4* vblk = reinterpret_cast<const uint4*>(a.v + ((size_t)b * n * a.G + g) * kD);
+    const bool ring = seg == kSegRing, blk = seg == kSegBlock;
+    sr.k = ring ? reinterpret_cast<const uint4*>(ring_k)
+                : (blk ? kblk : reinterpret_cast<const uint4*>(bank_k));
+    sr.v = ring ? reinterpret_cast<const uint4*>(ring_v)
+                : (blk ? vblk : reinterpret_cast<const uint4*>(bank_v));
+    sr.kks = blk ? a.G * kChunks : 1;
+    sr.kcs = ring ? R : (blk ? 1 : a.N);
+    sr.vks = blk ? a.G * kChunks : kChunks;
+    sr.cnt = seg_count(seg);
+    sr.ti = ti;
+    return sr;
+  };
+
   // cooperative V tile load: 32 keys x 32 chunks, 4 chunks per thread
   uint4 vpre[4];
   auto load_v = [&](int t) {
-    int seg, ti;
-    seg_of(t, seg, ti);
-    const int cnt = seg_count(seg);
+    const Src sr = src_of(t);
 #pragma unroll
     for (int m = 0; m < 4; ++m) {
       const int id = tid + 256 * m;
       const int key = id >> 5, c = id & 31;
-      int kk = ti * kPT + key;
-      kk = kk < cnt ? kk : cnt - 1;
-      const uint16_t* row;
-      if (seg == kSegRing) row = ring_v + (size_t)kk * kD;
-      else if (seg == kSegBlock) row = a.v + (((size_t)b * n + kk) * a.G + g) * kD;
-      else row = bank_v + (size_t)kk * kD;
-      vpre[m] = reinterpret_cast<const uint4*>(row)[c];
+      int kk = sr.ti * kPT + key;
+      kk = kk < sr.cnt ? kk : sr.cnt - 1;
+      vpre[m] = sr.v[(size_t)kk * sr.vks + c];
     }
   };
   auto store_v = [&](int buf) {
@@ -149,23 +189,14 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillArgs a) {
   // K B-operands of a tile: 2 sub-tiles of 16 keys x 8 k-steps
   uint4 kb[2][8];
   auto load_k = [&](int t) {
-    int seg, ti;
-    seg_of(t, seg, ti);
-    const int cnt = seg_count(seg);
+    const Src sr = src_of(t);
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
-      int kk = ti * kPT + sub * 16 + l16;
-      kk = kk < cnt ? kk : cnt - 1;
+      int kk = sr.ti * kPT + sub * 16 + l16;
+      kk = kk < sr.cnt ? kk : sr.cnt - 1;
 #pragma unroll
-      for (int st = 0; st < 8; ++st) {
-        const int c = st * 4 + lg;
-        if (seg == kSegRing)
-          kb[sub][st] = reinterpret_cast<const uint4*>(ring_k)[k_chunk_index(kk, c, R)];
-        else if (seg == kSegBlock)
-          kb[sub][st] = reinterpret_cast<const uint4*>(a.k + (((size_t)b * n + kk) * a.G + g) * kD)[c];
-        else
-          kb[sub][st] = reinterpret_cast<const uint4*>(bank_k)[k_chunk_index(kk, c, a.N)];
-      }
+      for (int st = 0; st < 8; ++st)
+        kb[sub][st] = sr.k[(size_t)kk * sr.kks + (size_t)(st * 4 + lg) * sr.kcs];
     }
   };
 
@@ -195,7 +226,9 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillArgs a) {
     seg_of(t, seg, ti);
     const int cnt = seg_count(seg);
     const bool has_next = t + 1 < t_all;
-    if (has_next) load_v(t + 1);
+    // prefetch without branches: past the last tile, reload the last one
+    const int tn = has_next ? t + 1 : t;
+    load_v(tn);
 
     // S = Q K^T for 32 keys
     f32x4_t s[2];
@@ -207,7 +240,7 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillArgs a) {
         s[sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[st]), as_bf16x8(kb[sub][st]),
                                                           s[sub], 0, 0, 0);
     }
-    if (has_next) load_k(t + 1);
+    load_k(tn);
 
     // mask and scale: lane's token my_tok, key = column l16 of each sub-tile
     float sv[2][4];
@@ -278,7 +311,7 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillArgs a) {
       }
       reset();
     }
-    if (has_next) store_v((t + 1) & 1);
+    store_v((t + 1) & 1);
     __syncthreads();
   }
   if (t_loc == 0) {
