@@ -47,6 +47,29 @@ __device__ __forceinline__ int32_t scalar_load(const int32_t* p) {
   return *(const __attribute__((address_space(4))) int32_t*)p;
 }
 
+// Reductions over a 16-lane row with DPP moves (swap neighbours, swap
+// pairs, mirror within 8, mirror within 16; no LDS round trip), then over
+// the 4 rows with lane reads.  The result is wave-uniform.
+template <int kCtrl>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), kCtrl, 0xf, 0xf, false));
+}
+constexpr int kQuadSwap1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int kQuadSwap2 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int kRowHalfMirror = 0x141;
+constexpr int kRowMirror = 0x140;
+
+__device__ __forceinline__ float wave_sum_u(float x) {
+  x += dpp<kQuadSwap1>(x);
+  x += dpp<kQuadSwap2>(x);
+  x += dpp<kRowHalfMirror>(x);
+  x += dpp<kRowMirror>(x);
+  return (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0)) +
+          __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16))) +
+         (__int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32)) +
+          __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48)));
+}
+
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
@@ -121,35 +144,86 @@ __device__ __forceinline__ Seg seg_of(const DecodeArgs& a, int item, int sub) {
 // out = o_local + tanh(q . w_g) * o_anchor, the ring write and the pending
 // append.  Every read of the unit's ring by this launch is already done:
 // only this wave reads it.
+// Operands of the in-wave finish of one unit, loaded ahead (with the last
+// bank tile's prefetch) so that the finish never waits on the vector-memory
+// counter: lanes 0-31 / 32-63 hold 16-byte chunk c32 of the current K / V
+// (k_or_v) and of the candidate K / V (ck_or_cv).
+struct FinOps {
+  uint4 k_or_v, ck_or_cv;
+};
+
+// Sources of the two auxiliary loads issued when a wave moves to segment
+// `nsub` of the next item: the segment's query rows, except that a
+// whole-unit wave entering the bank segment of the unit it is on (`item`)
+// keeps its query rows and fetches that unit's finish operands instead.
+struct AuxPtrs {
+  const uint4* p0;
+  const uint4* p1;
+};
+
+template <bool kWhole>
+__device__ __forceinline__ AuxPtrs aux_ptrs(const DecodeArgs& a, const Seg& nxt, int nsub,
+                                            int item, int lane) {
+  AuxPtrs ap;
+  ap.p0 = nxt.q4 + 2 * lane;
+  ap.p1 = nxt.q4 + 2 * lane + 1;
+  if (kWhole) {
+    const int b = item / a.G, g = item - b * a.G;
+    const size_t kvo = (size_t)b * a.kv_bs + (size_t)g * kD;
+    const int c32 = lane & 31;
+    const uint4* fk = reinterpret_cast<const uint4*>((lane < 32 ? a.k : a.v) + kvo) + c32;
+    const uint4* fc = reinterpret_cast<const uint4*>((lane < 32 ? a.ck : a.cv) + kvo) + c32;
+    ap.p0 = nsub == 1 ? fk : ap.p0;
+    ap.p1 = nsub == 1 ? fc : ap.p1;
+  }
+  return ap;
+}
+
+// Finish one token of unit u inside one wave (whole-unit launch): the
+// local read is the ring result (mr, lr, o_r in LDS) plus the current
+// token, the anchor read is the bank result (lb, accb in lanes 0-31); then
+// out = o_local + tanh(q . w_g) * o_anchor, the ring write and the pending
+// append.  Every read of the unit's ring by this launch is already done:
+// only this wave reads it.
 __device__ __forceinline__ void finish_unit(const DecodeArgs& a, int u, int lane,
                                             const uint4* q_w, const float* o_r,
                                             const float* mr, const float* lr,
-                                            const float* lb, float accb[kHpg][8]) {
+                                            const float* lb, float accb[kHpg][8],
+                                            const FinOps& f) {
   const int b = u / a.G, g = u - b * a.G;
-  const size_t kvo = (size_t)b * a.kv_bs + (size_t)g * kD;
-  // q . k_t and q . w_g over 4 dims per lane
-  const uint2 k4 = reinterpret_cast<const uint2*>(a.k + kvo)[lane];
-  const float kf[4] = {bf_lo(k4.x), bf_hi(k4.x), bf_lo(k4.y), bf_hi(k4.y)};
+  const int c32 = lane & 31;
+  // the current K (lanes 0-31, 8 dims each) and V (lanes 32-63)
+  const uint4 kv = f.k_or_v;
+  // q . k_t over 8 dims in lanes 0-31; q . w_g over 4 dims in all lanes
   float sc[kHpg], z[kHpg];
 #pragma unroll
   for (int h = 0; h < kHpg; ++h) {
+    const uint4 q8 = q_w[h * kChunks + c32];
+    float ds = bf_lo(q8.x) * bf_lo(kv.x);
+    ds = fmaf(bf_hi(q8.x), bf_hi(kv.x), ds);
+    ds = fmaf(bf_lo(q8.y), bf_lo(kv.y), ds);
+    ds = fmaf(bf_hi(q8.y), bf_hi(kv.y), ds);
+    ds = fmaf(bf_lo(q8.z), bf_lo(kv.z), ds);
+    ds = fmaf(bf_hi(q8.z), bf_hi(kv.z), ds);
+    ds = fmaf(bf_lo(q8.w), bf_lo(kv.w), ds);
+    ds = fmaf(bf_hi(q8.w), bf_hi(kv.w), ds);
+    ds = lane < 32 ? ds : 0.f;
     const uint2 q2 = reinterpret_cast<const uint2*>(q_w + h * kChunks)[lane];
-    const float qf[4] = {bf_lo(q2.x), bf_hi(q2.x), bf_lo(q2.y), bf_hi(q2.y)};
     const float4 w4 = reinterpret_cast<const float4*>(a.w_g + (size_t)(g * kHpg + h) * kD)[lane];
-    float ds = qf[0] * kf[0];
-    ds = fmaf(qf[1], kf[1], ds);
-    ds = fmaf(qf[2], kf[2], ds);
-    ds = fmaf(qf[3], kf[3], ds);
-    float dz = qf[0] * w4.x;
-    dz = fmaf(qf[1], w4.y, dz);
-    dz = fmaf(qf[2], w4.z, dz);
-    dz = fmaf(qf[3], w4.w, dz);
-    sc[h] = wave_sum(ds) * a.sl2e;
-    z[h] = wave_sum(dz);
+    float dz = bf_lo(q2.x) * w4.x;
+    dz = fmaf(bf_hi(q2.x), w4.y, dz);
+    dz = fmaf(bf_lo(q2.y), w4.z, dz);
+    dz = fmaf(bf_hi(q2.y), w4.w, dz);
+    sc[h] = wave_sum_u(ds) * a.sl2e;
+    z[h] = wave_sum_u(dz);
   }
-  const int c32 = lane & 31;
+  // the current V: lanes 32-63 hold it; bring chunk c32 to lane c32
+  uint4 v4;
+  v4.x = __shfl_xor(kv.x, 32, 64);
+  v4.y = __shfl_xor(kv.y, 32, 64);
+  v4.z = __shfl_xor(kv.z, 32, 64);
+  v4.w = __shfl_xor(kv.w, 32, 64);
   if (lane < 32) {
-    const uint4 v4 = reinterpret_cast<const uint4*>(a.v + kvo)[c32];
     const float vf[8] = {bf_lo(v4.x), bf_hi(v4.x), bf_lo(v4.y), bf_hi(v4.y),
                          bf_lo(v4.z), bf_hi(v4.z), bf_lo(v4.w), bf_hi(v4.w)};
     uint16_t* outp = a.out + (size_t)b * a.out_bs + (size_t)g * kHpg * kD + 8 * c32;
@@ -178,19 +252,23 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs& a, int u, int lane
       *reinterpret_cast<uint4*>(outp + (size_t)h * kD) = pk;
     }
   }
-  // Write: ring slot t mod R, pending slot t mod C.
+  // Write: ring slot t mod R (K chunks from lanes 0-31, the V row from
+  // lanes 32-63), pending slot t mod C likewise.
   if (lane < 32) {
     uint4* rk = reinterpret_cast<uint4*>(a.ring_k + (size_t)u * a.R * kD);
-    rk[k_chunk_index(a.ring_slot, c32, a.R)] = reinterpret_cast<const uint4*>(a.k + kvo)[c32];
+    rk[k_chunk_index(a.ring_slot, c32, a.R)] = kv;
     uint4* pk = reinterpret_cast<uint4*>(a.pend_k + ((size_t)u * a.C + a.pend_slot) * kD);
-    pk[c32] = reinterpret_cast<const uint4*>(a.ck + kvo)[c32];
+    pk[c32] = f.ck_or_cv;
   } else {
     uint4* rv = reinterpret_cast<uint4*>(a.ring_v + ((size_t)u * a.R + a.ring_slot) * kD);
-    rv[c32] = reinterpret_cast<const uint4*>(a.v + kvo)[c32];
+    rv[c32] = kv;
     uint4* pv = reinterpret_cast<uint4*>(a.pend_v + ((size_t)u * a.C + a.pend_slot) * kD);
-    pv[c32] = reinterpret_cast<const uint4*>(a.cv + kvo)[c32];
+    pv[c32] = f.ck_or_cv;
   }
-  if (lane == 0) a.pscore[(size_t)u * a.C + a.pend_slot] = a.cs[(size_t)b * a.cs_bs + g];
+  if (lane == 0) {
+    const float cs = *(const __attribute__((address_space(4))) float*)(a.cs + (size_t)b * a.cs_bs + g);
+    a.pscore[(size_t)u * a.C + a.pend_slot] = cs;
+  }
 }
 
 // Persistent attention kernel.  grid: at most the resident workgroups;
@@ -219,7 +297,8 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a, int item
   const int half = lane >> 5, c32 = lane & 31;
   uint4 kr[kChunks];
   uint4 vr[kTile / 2];
-  uint4 qn0, qn1;  // query rows for the next segment (2 x 16 B per lane)
+  uint4 qn0, qn1;  // auxiliary loads for the next segment (2 x 16 B per lane)
+  FinOps fin;      // whole-unit: operands of the unit's finish
   float mr[kHpg], lr[kHpg];  // whole-unit: the ring result
 
   Seg cur = seg_of<kWhole>(a, item, sub);
@@ -237,8 +316,13 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a, int item
   load_k(cur, cur.ta);
 
   for (;;) {
-    q_s[wave][2 * lane] = qn0;
-    q_s[wave][2 * lane + 1] = qn1;
+    if (!kWhole || sub == 0) {
+      q_s[wave][2 * lane] = qn0;
+      q_s[wave][2 * lane + 1] = qn1;
+    } else {
+      fin.k_or_v = qn0;
+      fin.ck_or_cv = qn1;
+    }
     __builtin_amdgcn_wave_barrier();
 
     int nitem = item, nsub = sub + 1;
@@ -311,10 +395,14 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a, int item
         const bool idle = !more && !has_next;
         const int vrow = tbase + half < cur.count ? tbase + half : cur.count - 1;
         const int voff = vrow * kChunks + c32;
-        // query rows first: the segment switch then waits for them alone
-        const uint4* qb = go_next ? nxt.q4 : cur.V4;
-        qn0 = qb[go_next ? 2 * lane : voff];
-        qn1 = qb[go_next ? 2 * lane + 1 : voff];
+        // two auxiliary loads first (the segment switch then waits for
+        // them alone): the next segment's query rows; or, whole-unit, when
+        // the ring segment of a unit hands over to its bank segment (same
+        // query rows), the operands of the unit's finish
+        const uint4* vrow_p = cur.V4 + voff;
+        const AuxPtrs ap = aux_ptrs<kWhole>(a, nxt, nsub, item, lane);
+        qn0 = *(go_next ? ap.p0 : vrow_p);
+        qn1 = *(go_next ? ap.p1 : vrow_p);
         const int ktile = more ? tile + 1 : nxt.ta;
         const int kcount = more ? cur.count : nxt.count;
         const uint4* kb = idle ? cur.V4 : (more ? cur.K4 : nxt.K4);
@@ -390,14 +478,15 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a, int item
       }
       __builtin_amdgcn_wave_barrier();
     } else {
-      finish_unit(a, item, lane, q_s[wave], or_s[kWhole ? wave : 0], mr, lr, l, acc);
+      finish_unit(a, item, lane, q_s[wave], or_s[kWhole ? wave : 0], mr, lr, l, acc, fin);
       __builtin_amdgcn_wave_barrier();
     }
 
     if (!has_next) break;
     if (cur.ta == cur.tb) {  // empty segment: nothing was prefetched for nxt
-      qn0 = nxt.q4[2 * lane];
-      qn1 = nxt.q4[2 * lane + 1];
+      const AuxPtrs ap = aux_ptrs<kWhole>(a, nxt, nsub, item, lane);
+      qn0 = *ap.p0;
+      qn1 = *ap.p1;
       load_k(nxt, nxt.ta);
     }
     cur = nxt;
