@@ -65,6 +65,14 @@ __global__ __launch_bounds__(256) void admit_kernel(AdmitArgs a) {
   const int u = a.unit0 + blockIdx.x;
   const int tid = threadIdx.x;
   const int N = a.N, C = a.C;
+  int64_t block_start = a.block_start;
+  if (a.pos != nullptr) {  // per-sequence: admit only where a block just completed
+    const int first = a.pos[blockIdx.x / a.G];
+    if (first < 0 || (a.aligned_only && first % C != 0)) return;
+    const int64_t last = (int64_t)first + a.pos_add;
+    if ((last + 1) % C != 0) return;
+    block_start = last + 1 - C;
+  }
 
   __shared__ uint64_t key[kMaxPool];
   __shared__ int evicted[kMaxPool];
@@ -147,7 +155,7 @@ __global__ __launch_bounds__(256) void admit_kernel(AdmitArgs a) {
     const int j = admitted[r];
     const int dst = r < ne ? evicted[r] : n + (r - ne);
     a.bscore[(size_t)u * N + dst] = ps[j];
-    a.bsrc[(size_t)u * N + dst] = (int32_t)(a.block_start + j);
+    a.bsrc[(size_t)u * N + dst] = (int32_t)(block_start + j);
   }
   if (tid == 0) a.bank_n[u] = K;
 }

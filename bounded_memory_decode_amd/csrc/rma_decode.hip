@@ -92,6 +92,33 @@ __device__ __forceinline__ uint16_t to_bf16(float f) {
 
 constexpr int kWaves = 4;
 
+// Where the token of sequence b sits: the valid ring slots (positions
+// max(0, t-R) .. t-1), the ring slot and pending slot it writes, and
+// whether the sequence takes part in this call (per-sequence positions:
+// a negative position leaves it out).  Wave-uniform; scalar arithmetic.
+struct TokPos {
+  int ring_count, ring_slot, pend_slot;
+  bool live;
+};
+
+__device__ __forceinline__ TokPos tok_pos(const DecodeArgs& a, int b) {
+  TokPos tp;
+  if (a.pos == nullptr) {
+    tp.ring_count = a.ring_count;
+    tp.ring_slot = a.ring_slot;
+    tp.pend_slot = a.pend_slot;
+    tp.live = true;
+    return tp;
+  }
+  const int p = scalar_load(a.pos + b);
+  const int pp = p > 0 ? p : 0;
+  tp.live = p >= 0;
+  tp.ring_count = tp.live ? (pp < a.R ? pp : a.R) : 0;
+  tp.ring_slot = pp % a.R;
+  tp.pend_slot = pp % a.C;
+  return tp;
+}
+
 // A segment: one contiguous range of 64-key tiles of one read (ring or
 // bank) of one (sequence, group) unit.
 struct Seg {
@@ -104,14 +131,15 @@ struct Seg {
 __device__ __forceinline__ Seg make_seg(const DecodeArgs& a, int u, bool ring, int t0,
                                         int tiles) {
   const int b = u / a.G, g = u - b * a.G;
+  const TokPos tp = tok_pos(a, b);
   Seg sg;
   if (ring) {
-    sg.count = a.ring_count;
+    sg.count = tp.ring_count;
     sg.slots = a.R;
     sg.K4 = reinterpret_cast<const uint4*>(a.ring_k + (size_t)u * a.R * kD);
     sg.V4 = reinterpret_cast<const uint4*>(a.ring_v + (size_t)u * a.R * kD);
   } else {
-    sg.count = scalar_load(a.bank_n + u);
+    sg.count = tp.live ? scalar_load(a.bank_n + u) : 0;
     sg.slots = a.N;
     sg.K4 = reinterpret_cast<const uint4*>(a.bank_k + (size_t)u * a.N * kD);
     sg.V4 = reinterpret_cast<const uint4*>(a.bank_v + (size_t)u * a.N * kD);
@@ -191,6 +219,8 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs& a, int u, int lane
                                             const float* lb, float accb[kHpg][8],
                                             const FinOps& f) {
   const int b = u / a.G, g = u - b * a.G;
+  const TokPos tp = tok_pos(a, b);
+  if (!tp.live) return;
   const int c32 = lane & 31;
   // the current K (lanes 0-31, 8 dims each) and V (lanes 32-63)
   const uint4 kv = f.k_or_v;
@@ -256,18 +286,18 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs& a, int u, int lane
   // lanes 32-63), pending slot t mod C likewise.
   if (lane < 32) {
     uint4* rk = reinterpret_cast<uint4*>(a.ring_k + (size_t)u * a.R * kD);
-    rk[k_chunk_index(a.ring_slot, c32, a.R)] = kv;
-    uint4* pk = reinterpret_cast<uint4*>(a.pend_k + ((size_t)u * a.C + a.pend_slot) * kD);
+    rk[k_chunk_index(tp.ring_slot, c32, a.R)] = kv;
+    uint4* pk = reinterpret_cast<uint4*>(a.pend_k + ((size_t)u * a.C + tp.pend_slot) * kD);
     pk[c32] = f.ck_or_cv;
   } else {
-    uint4* rv = reinterpret_cast<uint4*>(a.ring_v + ((size_t)u * a.R + a.ring_slot) * kD);
+    uint4* rv = reinterpret_cast<uint4*>(a.ring_v + ((size_t)u * a.R + tp.ring_slot) * kD);
     rv[c32] = kv;
-    uint4* pv = reinterpret_cast<uint4*>(a.pend_v + ((size_t)u * a.C + a.pend_slot) * kD);
+    uint4* pv = reinterpret_cast<uint4*>(a.pend_v + ((size_t)u * a.C + tp.pend_slot) * kD);
     pv[c32] = f.ck_or_cv;
   }
   if (lane == 0) {
     const float cs = *(const __attribute__((address_space(4))) float*)(a.cs + (size_t)b * a.cs_bs + g);
-    a.pscore[(size_t)u * a.C + a.pend_slot] = cs;
+    a.pscore[(size_t)u * a.C + tp.pend_slot] = cs;
   }
 }
 
@@ -501,6 +531,8 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   const int b = u / a.G, g = u - b * a.G;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   __shared__ float red[8][kWaves];
+  const TokPos tp = tok_pos(a, b);
+  if (!tp.live) return;  // the whole block: no barrier is skipped
 
   const uint16_t* qb = a.q + (size_t)b * a.q_bs + (size_t)g * kHpg * kD;
   const size_t kvo = (size_t)b * a.kv_bs + (size_t)g * kD;
@@ -527,7 +559,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
 
   const int S = a.splits_ring + a.splits_bank;
   const float* P = a.part + (size_t)u * S * kPart;
-  const int n = a.bank_n[u];
+  const int n = scalar_load(a.bank_n + u);
   uint16_t* outp = a.out + (size_t)b * a.out_bs + (size_t)g * kHpg * kD;
 
 #pragma unroll
@@ -568,24 +600,35 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   // slot t mod C takes the candidate record and score.
   if (tid < 32) {
     uint4* rk = reinterpret_cast<uint4*>(a.ring_k + (size_t)u * a.R * kD);
-    rk[k_chunk_index(a.ring_slot, tid, a.R)] = reinterpret_cast<const uint4*>(a.k + kvo)[tid];
+    rk[k_chunk_index(tp.ring_slot, tid, a.R)] = reinterpret_cast<const uint4*>(a.k + kvo)[tid];
   } else if (tid < 64) {
-    uint4* rv = reinterpret_cast<uint4*>(a.ring_v + ((size_t)u * a.R + a.ring_slot) * kD);
+    uint4* rv = reinterpret_cast<uint4*>(a.ring_v + ((size_t)u * a.R + tp.ring_slot) * kD);
     rv[tid - 32] = reinterpret_cast<const uint4*>(a.v + kvo)[tid - 32];
   } else if (tid < 96) {
-    uint4* pk = reinterpret_cast<uint4*>(a.pend_k + ((size_t)u * a.C + a.pend_slot) * kD);
+    uint4* pk = reinterpret_cast<uint4*>(a.pend_k + ((size_t)u * a.C + tp.pend_slot) * kD);
     pk[tid - 64] = reinterpret_cast<const uint4*>(a.ck + kvo)[tid - 64];
   } else if (tid < 128) {
-    uint4* pv = reinterpret_cast<uint4*>(a.pend_v + ((size_t)u * a.C + a.pend_slot) * kD);
+    uint4* pv = reinterpret_cast<uint4*>(a.pend_v + ((size_t)u * a.C + tp.pend_slot) * kD);
     pv[tid - 96] = reinterpret_cast<const uint4*>(a.cv + kvo)[tid - 96];
   } else if (tid == 128) {
-    a.pscore[(size_t)u * a.C + a.pend_slot] = a.cs[(size_t)b * a.cs_bs + g];
+    a.pscore[(size_t)u * a.C + tp.pend_slot] = a.cs[(size_t)b * a.cs_bs + g];
   }
 }
 
 __global__ void fill_i32_kernel(int32_t* p, int32_t value, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = value;
+}
+
+// bank_n of units (l * B + b) * G + g for b in [first, first + count):
+// thread i -> layer i / (count * G), offset i mod (count * G).
+__global__ void seq_bank_n_kernel(int32_t* bank_n, int L, int B, int G, int first, int count,
+                                  int32_t value) {
+  const int per = count * G;
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= L * per) return;
+  const int l = i / per, r = i - l * per;
+  bank_n[((size_t)l * B + first) * G + r] = value;
 }
 
 
@@ -632,6 +675,15 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_combine_kernel, dim3(a.units), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_seq_bank_n(int32_t* bank_n, int L, int B, int G, int first, int count,
+                             int32_t value, hipStream_t s) {
+  const int n = L * count * G;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(seq_bank_n_kernel, dim3((n + 255) / 256), dim3(256), 0, s, bank_n, L, B, G,
+                     first, count, value);
   return hipGetLastError();
 }
 

@@ -144,6 +144,7 @@ rma::DecodeArgs decode_args(const rma_state* st, int32_t layer, int64_t t, const
   a.pend_v = region<uint16_t>(st, L.pend_v) + unit0 * C * kD;
   a.pscore = region<float>(st, L.pscore) + unit0 * C;
   a.part = region<float>(st, L.scratch);
+  a.pos = nullptr;
   a.q_bs = q_bs;
   a.kv_bs = kv_bs;
   a.cs_bs = cs_bs;
@@ -164,6 +165,85 @@ rma::DecodeArgs decode_args(const rma_state* st, int32_t layer, int64_t t, const
   a.sl2e = (float)((double)c.scale * 1.4426950408889634);
   return a;
 }
+
+rma::PrefillArgs prefill_args(const rma_state* st, int32_t layer, int32_t n_tokens, int64_t P,
+                              const int32_t* pos, const void* q, const void* k, const void* v,
+                              const void* ck, const void* cv, const float* cs,
+                              const float* w_g, void* out) {
+  const rma_config& c = st->cfg;
+  const rma_layout& L = st->layout;
+  const int B = st->batch, G = c.kv_groups;
+  const int R = c.window - 1, N = c.bank_cap, C = c.commit;
+  const uint64_t unit0 = (uint64_t)layer * B * G;
+  rma::PrefillArgs a;
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.ck = static_cast<const uint16_t*>(ck);
+  a.cv = static_cast<const uint16_t*>(cv);
+  a.cs = cs;
+  a.w_g = w_g;
+  a.out = static_cast<uint16_t*>(out);
+  a.ring_k = region<uint16_t>(st, L.ring_k) + unit0 * R * kD;
+  a.ring_v = region<uint16_t>(st, L.ring_v) + unit0 * R * kD;
+  a.bank_k = region<uint16_t>(st, L.bank_k) + unit0 * N * kD;
+  a.bank_v = region<uint16_t>(st, L.bank_v) + unit0 * N * kD;
+  a.bank_n = region<int32_t>(st, L.bank_n) + unit0;
+  a.pend_k = region<uint16_t>(st, L.pend_k) + unit0 * C * kD;
+  a.pend_v = region<uint16_t>(st, L.pend_v) + unit0 * C * kD;
+  a.pscore = region<float>(st, L.pscore) + unit0 * C;
+  a.pos = pos;
+  a.B = B;
+  a.G = G;
+  a.H = c.q_heads;
+  a.R = R;
+  a.N = N;
+  a.C = C;
+  a.n = n_tokens;
+  a.P = P;
+  a.sl2e = (float)((double)c.scale * 1.4426950408889634);
+  return a;
+}
+
+rma::AdmitArgs admit_args(const rma_state* st) {
+  const rma_config& c = st->cfg;
+  const rma_layout& L = st->layout;
+  rma::AdmitArgs a;
+  a.bank_k = region<uint16_t>(st, L.bank_k);
+  a.bank_v = region<uint16_t>(st, L.bank_v);
+  a.bscore = region<float>(st, L.bscore);
+  a.bsrc = region<int32_t>(st, L.bsrc);
+  a.bank_n = region<int32_t>(st, L.bank_n);
+  a.pend_k = region<const uint16_t>(st, L.pend_k);
+  a.pend_v = region<const uint16_t>(st, L.pend_v);
+  a.pscore = region<const float>(st, L.pscore);
+  a.N = c.bank_cap;
+  a.C = c.commit;
+  a.unit0 = 0;
+  a.units = 0;
+  a.block_start = 0;
+  a.pos = nullptr;
+  a.G = c.kv_groups;
+  a.pos_add = 0;
+  a.aligned_only = 0;
+  return a;
+}
+
+// The admit launch of the per-sequence calls: every unit of the layer
+// whose sequence's last written token (pos[b] + pos_add) completes a block.
+hipError_t admit_at(const rma_state* st, int32_t layer, const int32_t* pos, int pos_add,
+                    int aligned_only, hipStream_t s) {
+  rma::AdmitArgs a = admit_args(st);
+  const int BG = st->batch * st->cfg.kv_groups;
+  a.unit0 = layer * BG;
+  a.units = BG;
+  a.pos = pos;
+  a.pos_add = pos_add;
+  a.aligned_only = aligned_only;
+  return rma::launch_admit(a, s);
+}
+
+bool aligned4(const void* p) { return p && ((uintptr_t)p & 3u) == 0; }
 
 }  // namespace
 
@@ -262,36 +342,8 @@ int rma_prefill_block(rma_state* st, int32_t layer, int32_t n_tokens, const void
     return RMA_E_ARG;
   const int64_t t0 = st->t[layer];
   if (st->pend_n[layer] != 0 || t0 % c.commit != 0) return RMA_E_NOT_BOUNDARY;
-  const rma_layout& L = st->layout;
-  const int B = st->batch, G = c.kv_groups;
-  const int R = c.window - 1, N = c.bank_cap, C = c.commit;
-  const uint64_t unit0 = (uint64_t)layer * B * G;
-  rma::PrefillArgs a;
-  a.q = static_cast<const uint16_t*>(q);
-  a.k = static_cast<const uint16_t*>(k);
-  a.v = static_cast<const uint16_t*>(v);
-  a.ck = static_cast<const uint16_t*>(cand_k);
-  a.cv = static_cast<const uint16_t*>(cand_v);
-  a.cs = cand_score;
-  a.w_g = w_g;
-  a.out = static_cast<uint16_t*>(out);
-  a.ring_k = region<uint16_t>(st, L.ring_k) + unit0 * R * kD;
-  a.ring_v = region<uint16_t>(st, L.ring_v) + unit0 * R * kD;
-  a.bank_k = region<uint16_t>(st, L.bank_k) + unit0 * N * kD;
-  a.bank_v = region<uint16_t>(st, L.bank_v) + unit0 * N * kD;
-  a.bank_n = region<int32_t>(st, L.bank_n) + unit0;
-  a.pend_k = region<uint16_t>(st, L.pend_k) + unit0 * C * kD;
-  a.pend_v = region<uint16_t>(st, L.pend_v) + unit0 * C * kD;
-  a.pscore = region<float>(st, L.pscore) + unit0 * C;
-  a.B = B;
-  a.G = G;
-  a.H = c.q_heads;
-  a.R = R;
-  a.N = N;
-  a.C = C;
-  a.n = n_tokens;
-  a.P = t0;
-  a.sl2e = (float)((double)c.scale * 1.4426950408889634);
+  const rma::PrefillArgs a = prefill_args(st, layer, n_tokens, t0, nullptr, q, k, v, cand_k,
+                                          cand_v, cand_score, w_g, out);
   const hipError_t e = rma::launch_prefill(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(st, e);
   st->t[layer] = t0 + n_tokens;
@@ -309,19 +361,8 @@ int rma_admit(rma_state* st, int32_t layer, void* stream) {
   const rma_config& c = st->cfg;
   for (int l = lo; l < hi; ++l)
     if (st->pend_n[l] != c.commit || st->t[l] % c.commit != 0) return RMA_E_NOT_BOUNDARY;
-  const rma_layout& L = st->layout;
   const int BG = st->batch * c.kv_groups;
-  rma::AdmitArgs a;
-  a.bank_k = region<uint16_t>(st, L.bank_k);
-  a.bank_v = region<uint16_t>(st, L.bank_v);
-  a.bscore = region<float>(st, L.bscore);
-  a.bsrc = region<int32_t>(st, L.bsrc);
-  a.bank_n = region<int32_t>(st, L.bank_n);
-  a.pend_k = region<const uint16_t>(st, L.pend_k);
-  a.pend_v = region<const uint16_t>(st, L.pend_v);
-  a.pscore = region<const float>(st, L.pscore);
-  a.N = c.bank_cap;
-  a.C = c.commit;
+  rma::AdmitArgs a = admit_args(st);
   // one launch over consecutive layers at the same position
   int l = lo;
   while (l < hi) {
@@ -339,6 +380,61 @@ int rma_admit(rma_state* st, int32_t layer, void* stream) {
     }
     l = e_end;
   }
+  return RMA_OK;
+}
+
+int rma_decode_step_at(rma_state* st, int32_t layer, const int32_t* pos, const void* q,
+                       const void* k, const void* v, const void* cand_k, const void* cand_v,
+                       const float* cand_score, const float* w_g, void* out, void* stream) {
+  int rc = check_state(st, layer);
+  if (rc != RMA_OK) return rc;
+  if (!aligned4(pos) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(cand_k) ||
+      !aligned16(cand_v) || !cand_score || !w_g || !aligned16(out))
+    return RMA_E_ARG;
+  const rma_config& c = st->cfg;
+  const int64_t H = c.q_heads, G = c.kv_groups;
+  rma::DecodeArgs a = decode_args(st, layer, 0, q, k, v, cand_k, cand_v, cand_score, w_g, out,
+                                  H * kD, G * kD, G, H * kD);
+  a.pos = pos;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = rma::launch_decode(a, s);
+  if (e == hipSuccess) e = admit_at(st, layer, pos, 0, 0, s);
+  if (e != hipSuccess) return hip_fail(st, e);
+  return RMA_OK;
+}
+
+int rma_prefill_block_at(rma_state* st, int32_t layer, int32_t n_tokens, const int32_t* pos,
+                         const void* q, const void* k, const void* v, const void* cand_k,
+                         const void* cand_v, const float* cand_score, const float* w_g,
+                         void* out, void* stream) {
+  int rc = check_state(st, layer);
+  if (rc != RMA_OK) return rc;
+  const rma_config& c = st->cfg;
+  if (n_tokens < 1 || n_tokens > c.commit) return RMA_E_ARG;
+  if (!aligned4(pos) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(cand_k) ||
+      !aligned16(cand_v) || !cand_score || !w_g || !aligned16(out))
+    return RMA_E_ARG;
+  const rma::PrefillArgs a = prefill_args(st, layer, n_tokens, 0, pos, q, k, v, cand_k, cand_v,
+                                          cand_score, w_g, out);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = rma::launch_prefill(a, s);
+  // only a full block can complete one (its start is a multiple of C)
+  if (e == hipSuccess && n_tokens == c.commit) e = admit_at(st, layer, pos, n_tokens - 1, 1, s);
+  if (e != hipSuccess) return hip_fail(st, e);
+  return RMA_OK;
+}
+
+int rma_seq_reset(rma_state* st, int32_t first, int32_t count, int32_t bank_n, void* stream) {
+  int rc = check_state(st, 0);
+  if (rc != RMA_OK) return rc;
+  if (first < 0 || count < 1 || first > st->batch - count || bank_n < 0 ||
+      bank_n > st->cfg.bank_cap)
+    return RMA_E_ARG;
+  const hipError_t e = rma::launch_seq_bank_n(region<int32_t>(st, st->layout.bank_n),
+                                              st->cfg.layers, st->batch, st->cfg.kv_groups,
+                                              first, count, bank_n,
+                                              static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(st, e);
   return RMA_OK;
 }
 

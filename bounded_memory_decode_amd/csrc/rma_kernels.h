@@ -42,15 +42,18 @@ struct DecodeArgs {
   uint16_t* pend_v;
   float* pscore;           // layer base, unit stride C
   float* part;             // scratch: [units][splits][kPart]
+  const int32_t* pos;      // [B] position of each sequence's token (< 0: the
+                           // sequence is left out), or null: every sequence
+                           // at the lockstep position below
   int64_t q_bs;            // elements between sequences in q
   int64_t kv_bs;           // ... in k, v, ck, cv
   int64_t cs_bs;           // ... in cs
   int64_t out_bs;          // ... in out
   int units;               // B*G
   int G, H, R, N, C;
-  int ring_count;          // valid ring slots: min(t, R)
-  int ring_slot;           // t mod R
-  int pend_slot;           // t mod C
+  int ring_count;          // lockstep: valid ring slots, min(t, R)
+  int ring_slot;           // lockstep: t mod R
+  int pend_slot;           // lockstep: t mod C
   int splits_ring, splits_bank;
   int tiles_ring, tiles_bank;  // tiles per split
   float sl2e;              // scale * log2(e)
@@ -76,9 +79,12 @@ struct PrefillArgs {
   uint16_t* pend_k;
   uint16_t* pend_v;
   float* pscore;
+  const int32_t* pos;      // [B] block start of each sequence (a sequence
+                           // whose entry is < 0 or not a multiple of C is
+                           // left out), or null: every sequence at P
   int B, G, H, R, N, C;
   int n;                   // tokens in the block (1 .. C)
-  int64_t P;               // position of the block's first token (P % C == 0)
+  int64_t P;               // lockstep: position of the block's first token
   float sl2e;              // scale * log2(e)
 };
 
@@ -97,12 +103,25 @@ struct AdmitArgs {
   int unit0;               // first unit (layer * B * G)
   int units;               // units to admit
   int N, C;
-  int64_t block_start;     // position of pending slot 0
+  int64_t block_start;     // lockstep: position of pending slot 0
+  // Per-sequence mode (pos != null, one layer, unit0 + i = unit of
+  // sequence i / G): sequence b's last written token is pos[b] + pos_add;
+  // its units are admitted iff pos[b] >= 0 (and, if aligned_only, pos[b]
+  // is a multiple of C) and that token completes a block.
+  const int32_t* pos;
+  int G;
+  int pos_add;
+  int aligned_only;
 };
 
 hipError_t launch_admit(const AdmitArgs& a, hipStream_t s);
 
 // Fill an int32 array on the device.
 hipError_t launch_fill_i32(int32_t* p, int32_t value, int64_t n, hipStream_t s);
+
+// Set the bank counts of sequences first .. first+count-1 in every layer
+// (bank_n region base; units (layer * B + b) * G + g).
+hipError_t launch_seq_bank_n(int32_t* bank_n, int L, int B, int G, int first, int count,
+                             int32_t value, hipStream_t s);
 
 }  // namespace rma

@@ -106,7 +106,12 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillArgs a) {
   }
 
   const int R = a.R;
-  const int64_t P = a.P;
+  int64_t P = a.P;
+  if (a.pos != nullptr) {  // per-sequence block start (uniform per workgroup)
+    const int p = a.pos[b];
+    if (p < 0 || p % a.C != 0) return;
+    P = p;
+  }
   const int ring_valid = (int)(P < R ? P : R);
   const int t_ring = (ring_valid + kPT - 1) / kPT;
   // block keys a query tile can see: tokens 0 .. last token of the tile
@@ -370,8 +375,14 @@ __global__ __launch_bounds__(128) void prefill_commit_kernel(PrefillArgs a) {
   const int j = blockIdx.x, u = blockIdx.y;
   const int b = u / a.G, g = u - b * a.G;
   const int tid = threadIdx.x;
+  int64_t P = a.P;
+  if (a.pos != nullptr) {
+    const int p = a.pos[b];
+    if (p < 0 || p % a.C != 0) return;
+    P = p;
+  }
   const size_t src = (((size_t)b * a.n + j) * a.G + g) * kD;
-  const int rs = (int)((a.P + j) % a.R), ps = (int)((a.P + j) % a.C);
+  const int rs = (int)((P + j) % a.R), ps = (int)((P + j) % a.C);
   const int c = tid & 31;
   if (tid < 32) {
     uint4* rk = reinterpret_cast<uint4*>(a.ring_k + (size_t)u * a.R * kD);

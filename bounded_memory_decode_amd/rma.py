@@ -29,7 +29,8 @@ RMA_OK, RMA_E_ARG, RMA_E_PENDING_FULL, RMA_E_NOT_BOUNDARY, RMA_E_HIP, RMA_E_UNSU
 
 # every symbol include/rma.h declares
 EXPORTS = ("rma_config_default", "rma_state_bytes", "rma_state_layout", "rma_state_init",
-           "rma_decode_step", "rma_prefill_block", "rma_admit", "rma_strerror")
+           "rma_decode_step", "rma_prefill_block", "rma_admit", "rma_decode_step_at",
+           "rma_prefill_block_at", "rma_seq_reset", "rma_strerror")
 
 
 class Config(ctypes.Structure):
@@ -85,6 +86,14 @@ def lib() -> ctypes.CDLL:
         L.rma_prefill_block.restype = ctypes.c_int
         L.rma_admit.argtypes = [ctypes.POINTER(_State), ctypes.c_int32, _P]
         L.rma_admit.restype = ctypes.c_int
+        L.rma_decode_step_at.argtypes = [ctypes.POINTER(_State), ctypes.c_int32] + [_P] * 10
+        L.rma_decode_step_at.restype = ctypes.c_int
+        L.rma_prefill_block_at.argtypes = [ctypes.POINTER(_State), ctypes.c_int32,
+                                           ctypes.c_int32] + [_P] * 10
+        L.rma_prefill_block_at.restype = ctypes.c_int
+        L.rma_seq_reset.argtypes = [ctypes.POINTER(_State), ctypes.c_int32, ctypes.c_int32,
+                                    ctypes.c_int32, _P]
+        L.rma_seq_reset.restype = ctypes.c_int
         L.rma_strerror.argtypes = [ctypes.c_int]
         L.rma_strerror.restype = ctypes.c_char_p
         _lib = L
@@ -239,8 +248,7 @@ class State:
         return v[layers, batch].clone()
 
     # ------------------------------------------------------------- compute
-    def decode_step(self, layer: int, q, k, v, cand_k, cand_v, cand_score, w_g,
-                    out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    def _decode_ptrs(self, q, k, v, cand_k, cand_v, cand_score, w_g, out):
         c, B = self.cfg, self.batch
         H, G, d = c.q_heads, c.kv_groups, c.head_dim
         if out is None:
@@ -251,12 +259,9 @@ class State:
                 _dev(cand_v, bf, (B, G, d), "cand_v", dev),
                 _dev(cand_score, f32, (B, G), "cand_score", dev),
                 _dev(w_g, f32, (H, d), "w_g", dev), _dev(out, bf, (B, H, d), "out", dev)]
-        _check(lib().rma_decode_step(ctypes.byref(self._st), int(layer), *ptrs,
-                                     _stream_handle(dev)), "rma_decode_step")
-        return out
+        return out, ptrs
 
-    def prefill_block(self, layer: int, q, k, v, cand_k, cand_v, cand_score, w_g,
-                      out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    def _prefill_ptrs(self, q, k, v, cand_k, cand_v, cand_score, w_g, out):
         c, B = self.cfg, self.batch
         H, G, d = c.q_heads, c.kv_groups, c.head_dim
         n = q.shape[1]
@@ -268,9 +273,50 @@ class State:
                 _dev(cand_v, bf, (B, n, G, d), "cand_v", dev),
                 _dev(cand_score, f32, (B, n, G), "cand_score", dev),
                 _dev(w_g, f32, (H, d), "w_g", dev), _dev(out, bf, (B, n, H, d), "out", dev)]
-        _check(lib().rma_prefill_block(ctypes.byref(self._st), int(layer), int(n), *ptrs,
-                                       _stream_handle(dev)), "rma_prefill_block")
+        return n, out, ptrs
+
+    def decode_step(self, layer: int, q, k, v, cand_k, cand_v, cand_score, w_g,
+                    out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        out, ptrs = self._decode_ptrs(q, k, v, cand_k, cand_v, cand_score, w_g, out)
+        _check(lib().rma_decode_step(ctypes.byref(self._st), int(layer), *ptrs,
+                                     _stream_handle(self.device)), "rma_decode_step")
         return out
+
+    def prefill_block(self, layer: int, q, k, v, cand_k, cand_v, cand_score, w_g,
+                      out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        n, out, ptrs = self._prefill_ptrs(q, k, v, cand_k, cand_v, cand_score, w_g, out)
+        _check(lib().rma_prefill_block(ctypes.byref(self._st), int(layer), int(n), *ptrs,
+                                       _stream_handle(self.device)), "rma_prefill_block")
+        return out
+
+    def decode_step_at(self, layer: int, pos: torch.Tensor, q, k, v, cand_k, cand_v, cand_score,
+                       w_g, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """Decode with per-sequence positions: `pos` is a device int32
+        tensor [batch] (negative: sequence left out, its `out` rows are not
+        written).  Admits the blocks the step completes.  The host counters
+        (t, pend_n, bank_n) are not used or updated."""
+        out, ptrs = self._decode_ptrs(q, k, v, cand_k, cand_v, cand_score, w_g, out)
+        p = _dev(pos, torch.int32, (self.batch,), "pos", self.device)
+        _check(lib().rma_decode_step_at(ctypes.byref(self._st), int(layer), p, *ptrs,
+                                        _stream_handle(self.device)), "rma_decode_step_at")
+        return out
+
+    def prefill_block_at(self, layer: int, pos: torch.Tensor, q, k, v, cand_k, cand_v,
+                         cand_score, w_g, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """Prefill block with per-sequence block starts in `pos` (device
+        int32 [batch]; sequences whose entry is negative or not a multiple of
+        the commit interval are left out).  A full block is admitted."""
+        n, out, ptrs = self._prefill_ptrs(q, k, v, cand_k, cand_v, cand_score, w_g, out)
+        p = _dev(pos, torch.int32, (self.batch,), "pos", self.device)
+        _check(lib().rma_prefill_block_at(ctypes.byref(self._st), int(layer), int(n), p, *ptrs,
+                                          _stream_handle(self.device)), "rma_prefill_block_at")
+        return out
+
+    def seq_reset(self, first: int, count: int = 1, bank_n: int = 0):
+        """Set the bank count of sequences first .. first+count-1 (all
+        layers and groups), e.g. for a new sequence in a reused slot."""
+        _check(lib().rma_seq_reset(ctypes.byref(self._st), int(first), int(count), int(bank_n),
+                                   _stream_handle(self.device)), "rma_seq_reset")
 
     def admit(self, layer: int = -1):
         _check(lib().rma_admit(ctypes.byref(self._st), int(layer), _stream_handle(self.device)),

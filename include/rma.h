@@ -192,6 +192,59 @@ int rma_prefill_block(rma_state* st, int32_t layer, int32_t n_tokens,
  * and nothing is enqueued. */
 int rma_admit(rma_state* st, int32_t layer, void* stream);
 
+/* ---- Per-sequence positions ------------------------------------------
+ * The calls above move a batch in lockstep, with the positions mirrored on
+ * the host.  The three calls below serve batches whose sequences stand at
+ * different positions (continuous batching: a sequence joins, idles or
+ * leaves without the others), and need no host bookkeeping per call, so a
+ * whole token step can be captured once in a HIP graph and replayed (the
+ * EdgeRock model card, section "Inference efficiency", credits CUDA Graphs
+ * for part of its decode speed).  Each sequence follows the same method as above; only
+ * where the positions live differs:
+ *   pos  [batch] int32, DEVICE memory, 4-byte aligned, read when the work
+ *        runs (so a graph replays with whatever pos holds then).
+ *        pos[b] >= 0: sequence b takes part, at that position;
+ *        pos[b] <  0: sequence b is left out: nothing of its state is read
+ *        or written and its rows of `out` are not written.
+ * A sequence's block is admitted by the call that writes its last
+ * candidate (the token at a position p with (p + 1) % commit == 0), after
+ * that call's reads, exactly as rma_admit would.  These calls neither read
+ * nor update the host counters t, pend_n and bank_n of rma_state: the
+ * device bank counts are the truth, and the caller owns the positions
+ * (advancing pos by one after each token, e.g. with a kernel captured in
+ * the same graph).  Mixing them with the lockstep calls on one state is
+ * the caller's business: the lockstep calls trust the host counters.
+ * A sequence that starts at a position that is not a multiple of commit
+ * finds pending slots below it as they are in the buffer (as after
+ * rma_state_init).  Device-side conditions are not reported; a position
+ * the kernels cannot honour leaves the sequence out as documented per
+ * call. */
+
+/* Decode one token for every sequence b with pos[b] >= 0, at position
+ * pos[b]; tensors as in rma_decode_step.  Then admits the blocks these
+ * tokens complete.  Returns RMA_OK, RMA_E_ARG or RMA_E_HIP. */
+int rma_decode_step_at(rma_state* st, int32_t layer, const int32_t* pos, const void* q,
+                       const void* k, const void* v, const void* cand_k, const void* cand_v,
+                       const float* cand_score, const float* w_g, void* out,
+                       void* stream);
+
+/* A prefill block of n_tokens (1 .. commit) for every sequence b whose
+ * pos[b] is >= 0 and a multiple of commit (the block's first position);
+ * other sequences are left out.  Tensors as in rma_prefill_block.  A full
+ * block (n_tokens == commit) is admitted by the same call.  Returns
+ * RMA_OK, RMA_E_ARG or RMA_E_HIP. */
+int rma_prefill_block_at(rma_state* st, int32_t layer, int32_t n_tokens, const int32_t* pos,
+                         const void* q, const void* k, const void* v, const void* cand_k,
+                         const void* cand_v, const float* cand_score, const float* w_g,
+                         void* out, void* stream);
+
+/* Give sequences first .. first+count-1 (every layer and group) a bank of
+ * `bank_n` committed anchors (0 for a new sequence in a reused batch slot;
+ * a new sequence's ring needs no clearing, the position decides which
+ * slots are read).  Enqueued on `stream`.  Returns RMA_OK, RMA_E_ARG or
+ * RMA_E_HIP. */
+int rma_seq_reset(rma_state* st, int32_t first, int32_t count, int32_t bank_n, void* stream);
+
 /* Static text for a status code. */
 const char* rma_strerror(int status);
 

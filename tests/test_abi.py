@@ -200,3 +200,28 @@ def test_k_plane_layout_helpers_follow_the_header(S):
             i = (c * S + s) * 8
             assert torch.equal(st[i:i + 8], nat[0, s, 8 * c:8 * c + 8])
     assert torch.equal(_k_to_natural(st[None], d), nat)
+
+
+def test_positioned_calls_validation_on_host():
+    """The per-sequence calls check pointers, layer, block size and the
+    reset range on the host; nothing is enqueued on failure."""
+    L = rma.lib()
+    st = _fake_state()
+    P = [FAKE] * 9
+    assert L.rma_decode_step_at(ctypes.byref(st), 0, None, *P) == rma.RMA_E_ARG
+    assert L.rma_decode_step_at(ctypes.byref(st), 0, FAKE + 2, *P) == rma.RMA_E_ARG
+    assert L.rma_decode_step_at(ctypes.byref(st), 8, FAKE, *P) == rma.RMA_E_ARG
+    bad = list(P)
+    bad[1] = FAKE + 8  # misaligned k
+    assert L.rma_decode_step_at(ctypes.byref(st), 0, FAKE, *bad) == rma.RMA_E_ARG
+    assert L.rma_decode_step_at(None, 0, FAKE, *P) == rma.RMA_E_ARG
+    assert L.rma_prefill_block_at(ctypes.byref(st), 0, 0, FAKE, *P) == rma.RMA_E_ARG
+    assert L.rma_prefill_block_at(ctypes.byref(st), 0, 257, FAKE, *P) == rma.RMA_E_ARG
+    assert L.rma_prefill_block_at(ctypes.byref(st), 0, 16, None, *P) == rma.RMA_E_ARG
+    assert L.rma_prefill_block_at(ctypes.byref(st), -1, 16, FAKE, *P) == rma.RMA_E_ARG
+    for first, count, n in ((-1, 1, 0), (0, 0, 0), (1, 2, 0), (2, 1, 0), (0, 1, -1),
+                            (0, 1, 1025)):
+        assert L.rma_seq_reset(ctypes.byref(st), first, count, n, None) == rma.RMA_E_ARG
+    assert L.rma_seq_reset(None, 0, 1, 0, None) == rma.RMA_E_ARG
+    # host counters untouched by failed calls
+    assert st.t[0] == 32768 and st.pend_n[0] == 0 and st.bank_n[0] == 1024
