@@ -42,7 +42,7 @@ UNIT_BYTES = UNIT_READ + UNIT_WRITE          # 2,104,328
 
 # Sources that define the decode kernel; the committed counter summary is
 # used only while their hash matches.
-DECODE_SOURCES = ("rma_decode.hip", "rma_kernels.h")
+DECODE_SOURCES = ("rma_decode.hip", "rma_kernels.h", "rma_admit_unit.h")
 
 
 def kernel_sources_sha() -> str:
@@ -201,6 +201,84 @@ def bench_prefill(device, seed, batch, blocks):
                          "kernel": "prefill_attn_kernel + prefill_commit_kernel (one layer, one block)"}}
 
 
+def bench_latency(device, seed, steps, warmup):
+    """One sequence, 8 layers, decoding after a 131,072-token prompt (ring
+    and bank full): the token step launched call by call (lockstep calls,
+    admit every 256 tokens) and the same step captured once in a HIP graph
+    (per-sequence calls with the admit inside, plus the position increment)
+    and replayed.  The state of one sequence (64 MiB) stays in the 256 MB
+    last-level cache, so this is a latency figure, not an HBM one."""
+    import torch
+    from bounded_memory_decode_amd import synth
+    w = synth.WORKLOADS["long_b1"].with_(t0=131072, bank_n=1024, ring_full=True)
+    S = make_state(w, seed, device)
+    sets, wg, outs = make_pool(w, seed, device, pool=4)
+    for s in range(warmup):
+        run_step(S, sets, wg, outs, s)
+    torch.cuda.synchronize()
+    e0, e1 = _event(), _event()
+    e0.record()
+    for s in range(steps):
+        run_step(S, sets, wg, outs, warmup + s)
+    e1.record()
+    torch.cuda.synchronize()
+    eager_us = e0.elapsed_time(e1) * 1e3 / steps
+
+    pos = torch.full((w.B,), S.t[0], dtype=torch.int32, device=device)
+    x = [sets[l][0] for l in range(w.L)]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for l in range(w.L):
+            S.decode_step_at(l, pos, x[l]["q"], x[l]["k"], x[l]["v"], x[l]["ck"], x[l]["cv"],
+                             x[l]["cs"], wg[l], outs[l])
+        pos.add_(1)
+    for _ in range(warmup):
+        graph.replay()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    graph_us = e0.elapsed_time(e1) * 1e3 / steps
+    del graph, S
+    torch.cuda.empty_cache()
+    return {"workload": f"long_b1 decode: 1 sequence x {w.L} layers after a {w.t0}-token prompt "
+                        f"(ring and bank full)",
+            "steps": steps,
+            "eager_us_per_token": round(eager_us, 2),
+            "graph_us_per_token": round(graph_us, 2),
+            "graph_tokens_per_s": round(1e6 / graph_us, 1),
+            "graph": "8 x rma_decode_step_at (attention, combine, admit-if-block-end) + "
+                     "position increment, captured once"}
+
+
+def bench_staggered(S, w, sets, wg, outs, steps):
+    """The headline batch with every sequence at its own offset inside the
+    256-token block (sequence b at t + b mod 256): per-sequence calls, so
+    each step admits the sequences whose block ends there, one layer at a
+    time, instead of all of them every 256th step."""
+    import torch
+    t = S.t[0]
+    pos = (t + torch.arange(w.B, device=S.device, dtype=torch.int32) % w.C).to(torch.int32)
+    e0, e1 = _event(), _event()
+    torch.cuda.synchronize()
+    e0.record()
+    for s in range(steps):
+        for l in range(w.L):
+            x = sets[l][s % len(sets[l])]
+            S.decode_step_at(l, pos, x["q"], x["k"], x["v"], x["ck"], x["cv"], x["cs"], wg[l],
+                             outs[l])
+        pos += 1
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    return {"workload": f"{w.name} with sequence b at block offset b mod {w.C} (per-sequence "
+                        f"positions; every sequence admitted once per layer per {w.C} steps)",
+            "steps": steps, "ms_per_step": round(ms / steps, 4),
+            "tokens_per_s": round(w.B * steps / (ms * 1e-3), 1)}
+
+
 def cpu_baseline(S, w, sets, wg, sample_b: int, seed: int, steps: int = 8):
     """The oracle, timed on the host cores on a bounded sample: `sample_b`
     sequences of the same state, `steps` tokens through all layers."""
@@ -265,10 +343,16 @@ def main():
     ap.add_argument("--warmup", type=int, default=16)
     ap.add_argument("--workload", default="stack_b512")
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--cpu-sample", type=int, default=32,
+    ap.add_argument("--repeats", type=int, default=3,
+                    help="timed runs of --steps steps each; the median run is reported")
+    ap.add_argument("--cpu-sample", type=int, default=64,
                     help="sequences in the CPU-oracle sample (0: skip)")
-    ap.add_argument("--cpu-steps", type=int, default=8,
+    ap.add_argument("--cpu-steps", type=int, default=32,
                     help="tokens per sequence in the CPU-oracle sample")
+    ap.add_argument("--latency-steps", type=int, default=512,
+                    help="batch-1 token steps timed eager and as graph replays (0: skip)")
+    ap.add_argument("--staggered-steps", type=int, default=256,
+                    help="steps of the per-sequence-position run at the headline batch (0: skip)")
     ap.add_argument("--prefill-blocks", type=int, default=4,
                     help="256-token blocks timed per prefill batch size (0: skip)")
     ap.add_argument("--calibration-copy-gib", type=int, default=0,
@@ -315,24 +399,33 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(w.L)] for _ in range(K)]
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    say(f"[bench] timing {K} steps")
-    admits = 0
-    admit_ev = []
-    torch.cuda.synchronize()
-    t_wall = time.perf_counter()
-    start.record()
-    for s in range(K):
-        admits += run_step(S, sets, wg, outs, args.warmup + s, ev[s], admit_ev)
-    stop.record()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_wall
-    ms_total = start.elapsed_time(stop)
+    runs = []
+    step0 = args.warmup
+    for r in range(max(1, args.repeats)):
+        ev = [[(_event(), _event()) for _ in range(w.L)] for _ in range(K)]
+        start, stop = _event(), _event()
+        say(f"[bench] timing {K} steps (run {r + 1})")
+        admits = 0
+        admit_ev = []
+        torch.cuda.synchronize()
+        t_wall = time.perf_counter()
+        start.record()
+        for s in range(K):
+            admits += run_step(S, sets, wg, outs, step0 + s, ev[s], admit_ev)
+        stop.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t_wall
+        step0 += K
+        ms_total = start.elapsed_time(stop)
+        dec_ms = [ev[s][l][0].elapsed_time(ev[s][l][1]) for s in range(K) for l in range(w.L)]
+        runs.append({"ms_total": ms_total, "dec_avg_ms": sum(dec_ms) / len(dec_ms),
+                     "admits": admits, "admit_ev": admit_ev, "wall": wall})
+        say(f"[bench] run {r + 1}: {w.B * K / (ms_total * 1e-3):,.0f} tok/s, decode launch "
+            f"{runs[-1]['dec_avg_ms'] * 1e3:.1f} us")
+    med = sorted(runs, key=lambda x: x["ms_total"])[len(runs) // 2]
+    ms_total, dec_avg_ms, admits = med["ms_total"], med["dec_avg_ms"], med["admits"]
+    admit_ev, wall = med["admit_ev"], med["wall"]
     ms_step = ms_total / K
-    dec_ms = [ev[s][l][0].elapsed_time(ev[s][l][1]) for s in range(K) for l in range(w.L)]
-    dec_avg_ms = sum(dec_ms) / len(dec_ms)
 
     units = w.B * w.G
     launch_bytes = units * UNIT_BYTES
@@ -359,6 +452,8 @@ def main():
                                f"4 KV groups, head_dim 256, ring 1023 + current, bank 1024, "
                                f"commit 256, start position {w.t0} (ring and bank full)",
                    "batch": w.B, "layers": w.L, "admit_rounds": admits,
+                   "runs": len(runs), "run_tokens_per_s": [round(w.B * K / (x["ms_total"] * 1e-3), 1)
+                                                          for x in runs],
                    "step_bytes_algorithmic": step_bytes,
                    "step_GBps": round(step_bytes / (ms_step * 1e-3) / 1e9, 1)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
@@ -383,8 +478,18 @@ def main():
         say(f"[bench] CPU oracle on {args.cpu_sample} sequences x {args.cpu_steps} tokens")
         result["cpu_baseline"] = cpu_baseline(S, w, sets, wg, args.cpu_sample, args.seed,
                                               args.cpu_steps)
+    if args.staggered_steps > 0:
+        say(f"[bench] per-sequence positions, {args.staggered_steps} steps")
+        result["staggered"] = bench_staggered(S, w, sets, wg, outs, args.staggered_steps)
+        say(f"[bench] staggered: {result['staggered']['tokens_per_s']:,.0f} tok/s")
+    del S, sets, outs
+    torch.cuda.empty_cache()
+    if args.latency_steps > 0:
+        say(f"[bench] batch-1 latency, {args.latency_steps} steps")
+        result["latency"] = bench_latency(device, args.seed, args.latency_steps, 16)
+        say(f"[bench] batch 1: eager {result['latency']['eager_us_per_token']} us/token, "
+            f"graph {result['latency']['graph_us_per_token']} us/token")
     if args.prefill_blocks > 0:
-        del S, sets, outs
         torch.cuda.empty_cache()
         result["prefill"] = []
         for pb in (1, 8):

@@ -22,7 +22,7 @@
 // 64 consecutive slots reads 1 KiB of contiguous memory with one key per
 // lane; V planes are row-major so that a half-wave loads one 512-byte row.
 // Neither read needs an LDS transpose.
-#include "rma_kernels.h"
+#include "rma_admit_unit.h"
 
 namespace rma {
 namespace {
@@ -97,6 +97,7 @@ constexpr int kWaves = 4;
 // whether the sequence takes part in this call (per-sequence positions:
 // a negative position leaves it out).  Wave-uniform; scalar arithmetic.
 struct TokPos {
+  int pos;  // per-sequence positions only
   int ring_count, ring_slot, pend_slot;
   bool live;
 };
@@ -104,6 +105,7 @@ struct TokPos {
 __device__ __forceinline__ TokPos tok_pos(const DecodeArgs& a, int b) {
   TokPos tp;
   if (a.pos == nullptr) {
+    tp.pos = 0;
     tp.ring_count = a.ring_count;
     tp.ring_slot = a.ring_slot;
     tp.pend_slot = a.pend_slot;
@@ -112,6 +114,7 @@ __device__ __forceinline__ TokPos tok_pos(const DecodeArgs& a, int b) {
   }
   const int p = scalar_load(a.pos + b);
   const int pp = p > 0 ? p : 0;
+  tp.pos = pp;
   tp.live = p >= 0;
   tp.ring_count = tp.live ? (pp < a.R ? pp : a.R) : 0;
   tp.ring_slot = pp % a.R;
@@ -525,14 +528,40 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a, int item
   }
 }
 
-// grid: units; block: 256 (thread = dimension).
+// Finish of the split launch.  grid: units; block: 256 (thread =
+// dimension).  Merges the parts of the local read (ring parts plus the
+// current token) and of the anchor read (bank parts), applies the gate,
+// writes the output, the ring slot and the pending slot; with per-sequence
+// positions, a token that completes its block is followed by the unit's
+// admit in this same workgroup.  Every part's value for this thread's
+// dimension is loaded before any is used, so the merge costs one memory
+// round trip.
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   const int u = blockIdx.x;
   const int b = u / a.G, g = u - b * a.G;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  __shared__ float red[8][kWaves];
   const TokPos tp = tok_pos(a, b);
   if (!tp.live) return;  // the whole block: no barrier is skipped
+  __shared__ float red[8][kWaves];
+  __shared__ float ml[2 * kMaxSplits][2 * kHpg];  // (m[4], l[4]) of every part
+  __shared__ AdmitShared sh;
+
+  const int sr = a.splits_ring, S = a.splits_ring + a.splits_bank;
+  const float* P = a.part + (size_t)u * S * kPart;
+  // (m, l) of part tid / 8; parts past S read as empty (m = -inf, l = 0)
+  {
+    const int sp = tid >> 3, j = tid & 7;
+    ml[sp][j] = sp < S ? P[(size_t)sp * kPart + kHpg * kD + j] : (j < kHpg ? -INFINITY : 0.f);
+  }
+  // o of every part for this dimension (parts past S re-read part S-1;
+  // their weight is 0)
+  float po[kHpg][2 * kMaxSplits];
+#pragma unroll
+  for (int sp = 0; sp < 2 * kMaxSplits; ++sp) {
+    const int sc = sp < S ? sp : S - 1;
+#pragma unroll
+    for (int h = 0; h < kHpg; ++h) po[h][sp] = P[(size_t)sc * kPart + h * kD + tid];
+  }
 
   const uint16_t* qb = a.q + (size_t)b * a.q_bs + (size_t)g * kHpg * kD;
   const size_t kvo = (size_t)b * a.kv_bs + (size_t)g * kD;
@@ -557,40 +586,40 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
 #pragma unroll
   for (int j = 0; j < 8; ++j) dts[j] = (red[j][0] + red[j][1]) + (red[j][2] + red[j][3]);
 
-  const int S = a.splits_ring + a.splits_bank;
-  const float* P = a.part + (size_t)u * S * kPart;
   const int n = scalar_load(a.bank_n + u);
   uint16_t* outp = a.out + (size_t)b * a.out_bs + (size_t)g * kHpg * kD;
 
 #pragma unroll
   for (int h = 0; h < kHpg; ++h) {
-    // local read: ring splits plus the current token
+    // local read: ring parts plus the current token
     const float sc = dts[h] * a.sl2e;
     float M = sc;
-    for (int s = 0; s < a.splits_ring; ++s) M = fmaxf(M, P[s * kPart + kHpg * kD + h]);
+#pragma unroll
+    for (int sp = 0; sp < 2 * kMaxSplits; ++sp) M = fmaxf(M, sp < sr ? ml[sp][h] : -INFINITY);
     float L = fast_exp2(sc - M);
     float o = L * vf;
-    for (int s = 0; s < a.splits_ring; ++s) {
-      const float f = fast_exp2(P[s * kPart + kHpg * kD + h] - M);  // -inf -> 0
-      o = fmaf(P[s * kPart + h * kD + tid], f, o);
-      L = fmaf(P[s * kPart + kHpg * kD + kHpg + h], f, L);
+#pragma unroll
+    for (int sp = 0; sp < 2 * kMaxSplits; ++sp) {
+      const float f = sp < sr ? fast_exp2(ml[sp][h] - M) : 0.f;  // m = -inf -> 0
+      o = fmaf(po[h][sp], f, o);
+      L = fmaf(ml[sp][kHpg + h], f, L);
     }
     const float oloc = o / L;
 
-    // anchor read: bank splits (empty bank reads as zero)
-    float oanc = 0.f;
-    if (n > 0) {
-      float M2 = -INFINITY;
-      for (int s = a.splits_ring; s < S; ++s) M2 = fmaxf(M2, P[s * kPart + kHpg * kD + h]);
-      float o2 = 0.f, L2 = 0.f;
-      for (int s = a.splits_ring; s < S; ++s) {
-        const float ms = P[s * kPart + kHpg * kD + h];
-        const float f = (ms == -INFINITY) ? 0.f : fast_exp2(ms - M2);
-        o2 = fmaf(P[s * kPart + h * kD + tid], f, o2);
-        L2 = fmaf(P[s * kPart + kHpg * kD + kHpg + h], f, L2);
-      }
-      oanc = o2 / L2;
+    // anchor read: bank parts (an empty bank reads as zero)
+    float M2 = -INFINITY;
+#pragma unroll
+    for (int sp = 0; sp < 2 * kMaxSplits; ++sp)
+      M2 = fmaxf(M2, (sp >= sr && sp < S) ? ml[sp][h] : -INFINITY);
+    float o2 = 0.f, L2 = 0.f;
+#pragma unroll
+    for (int sp = 0; sp < 2 * kMaxSplits; ++sp) {
+      const float ms = (sp >= sr && sp < S) ? ml[sp][h] : -INFINITY;
+      const float f = ms == -INFINITY ? 0.f : fast_exp2(ms - M2);
+      o2 = fmaf(po[h][sp], f, o2);
+      L2 = fmaf(ml[sp][kHpg + h], f, L2);
     }
+    const float oanc = n > 0 ? o2 / L2 : 0.f;
     const float gate = tanhf(dts[kHpg + h]);
     outp[(size_t)h * kD + tid] = to_bf16(fmaf(gate, oanc, oloc));
   }
@@ -612,6 +641,26 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
     pv[tid - 96] = reinterpret_cast<const uint4*>(a.cv + kvo)[tid - 96];
   } else if (tid == 128) {
     a.pscore[(size_t)u * a.C + tp.pend_slot] = a.cs[(size_t)b * a.cs_bs + g];
+  }
+
+  // per-sequence positions: the token completes its block -> admit now
+  // (the stores above are complete and visible to the block after the
+  // barrier; no other workgroup touches this unit)
+  if (a.pos != nullptr && (tp.pos + 1) % a.C == 0) {
+    __syncthreads();
+    AdmitUnit au;
+    au.bank_k = a.bank_k + (size_t)u * a.N * kD;
+    au.bank_v = a.bank_v + (size_t)u * a.N * kD;
+    au.bscore = a.bscore + (size_t)u * a.N;
+    au.bsrc = a.bsrc + (size_t)u * a.N;
+    au.bank_n = a.bank_n + u;
+    au.pend_k = a.pend_k + (size_t)u * a.C * kD;
+    au.pend_v = a.pend_v + (size_t)u * a.C * kD;
+    au.pscore = a.pscore + (size_t)u * a.C;
+    au.N = a.N;
+    au.C = a.C;
+    au.block_start = (int64_t)tp.pos + 1 - a.C;
+    admit_unit(au, sh);
   }
 }
 
@@ -664,7 +713,28 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
     int grid = (a.units + kWaves - 1) / kWaves;
     if (grid > res_whole) grid = res_whole;
     hipLaunchKernelGGL(decode_attn_kernel<true>, dim3(grid), dim3(256), 0, s, a, a.units);
-    return hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.pos == nullptr) return e;
+    // per-sequence positions: admit the units whose block this token ends
+    AdmitArgs ad;
+    ad.bank_k = a.bank_k;
+    ad.bank_v = a.bank_v;
+    ad.bscore = a.bscore;
+    ad.bsrc = a.bsrc;
+    ad.bank_n = a.bank_n;
+    ad.pend_k = a.pend_k;
+    ad.pend_v = a.pend_v;
+    ad.pscore = a.pscore;
+    ad.unit0 = 0;  // the pointers are already the layer's
+    ad.units = a.units;
+    ad.N = a.N;
+    ad.C = a.C;
+    ad.block_start = 0;
+    ad.pos = a.pos;
+    ad.G = a.G;
+    ad.pos_add = 0;
+    ad.aligned_only = 0;
+    return launch_admit(ad, s);
   }
   const int S = a.splits_ring + a.splits_bank;
   const int items = a.units * S;

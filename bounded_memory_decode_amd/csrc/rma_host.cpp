@@ -140,6 +140,8 @@ rma::DecodeArgs decode_args(const rma_state* st, int32_t layer, int64_t t, const
   a.bank_k = region<uint16_t>(st, L.bank_k) + unit0 * N * kD;
   a.bank_v = region<uint16_t>(st, L.bank_v) + unit0 * N * kD;
   a.bank_n = region<int32_t>(st, L.bank_n) + unit0;
+  a.bscore = region<float>(st, L.bscore) + unit0 * N;
+  a.bsrc = region<int32_t>(st, L.bsrc) + unit0 * N;
   a.pend_k = region<uint16_t>(st, L.pend_k) + unit0 * C * kD;
   a.pend_v = region<uint16_t>(st, L.pend_v) + unit0 * C * kD;
   a.pscore = region<float>(st, L.pscore) + unit0 * C;
@@ -396,9 +398,7 @@ int rma_decode_step_at(rma_state* st, int32_t layer, const int32_t* pos, const v
   rma::DecodeArgs a = decode_args(st, layer, 0, q, k, v, cand_k, cand_v, cand_score, w_g, out,
                                   H * kD, G * kD, G, H * kD);
   a.pos = pos;
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e = rma::launch_decode(a, s);
-  if (e == hipSuccess) e = admit_at(st, layer, pos, 0, 0, s);
+  const hipError_t e = rma::launch_decode(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(st, e);
   return RMA_OK;
 }

@@ -35,9 +35,11 @@ struct DecodeArgs {
   uint16_t* out;           // [B][H][D]
   uint16_t* ring_k;        // layer base, unit stride R*D
   uint16_t* ring_v;
-  const uint16_t* bank_k;  // layer base, unit stride N*D
-  const uint16_t* bank_v;
-  const int32_t* bank_n;   // [B*G] of this layer
+  uint16_t* bank_k;        // layer base, unit stride N*D (written only by
+  uint16_t* bank_v;        // the per-sequence admit)
+  int32_t* bank_n;         // [B*G] of this layer
+  float* bscore;           // layer base, unit stride N
+  int32_t* bsrc;
   uint16_t* pend_k;        // layer base, unit stride C*D
   uint16_t* pend_v;
   float* pscore;           // layer base, unit stride C
@@ -59,6 +61,8 @@ struct DecodeArgs {
   float sl2e;              // scale * log2(e)
 };
 
+// The decode of one token; with per-sequence positions (a.pos), also the
+// admit of every unit whose block the token completes.
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 
 // A chunked-prefill block of one layer.
