@@ -14,15 +14,17 @@
 // The block is a dense contraction, so it runs on MFMA:
 // v_mfma_f32_16x16x32_bf16 (A: lane l holds row l%16, k = 8*(l/16)+j;
 // B: column l%16, same k; D: register i holds row 4*(l/16)+i, column l%16).
-// One workgroup per (sequence, group, 16-token query tile); wave w owns 16
-// query rows, row = token * 4 + head, so each accumulator lane holds the 4
-// heads of one token and the mask (a function of the token) is per lane.
-//  * QK: K B-operands come straight from the chunk-major K planes (16 keys
-//    of one chunk are 256 contiguous bytes) or from the block's K rows.
-//  * P.V: V tiles of 32 keys are staged in LDS (double-buffered, shared by
-//    the 4 waves) and gathered as B-operands (8 keys of one dim per lane);
-//    P goes from the accumulator layout to the A layout through a per-wave
-//    LDS slice.
+// One workgroup per (sequence, group, tile of 16 or 32 tokens); each wave
+// owns 16 queries (4 tokens x 4 heads), one per MFMA column, so a lane
+// holds one query throughout.
+//  * Scores are computed transposed, S^T = K Q^T (A = 16 keys x 32 dims of
+//    the staged K tile, B = the wave's Q^T in registers), which leaves each
+//    lane's probabilities exactly where the B operand of O^T = V^T P^T
+//    wants them: P never leaves registers.
+//  * Every 32-key tile of K and V is staged once per workgroup in LDS
+//    (double-buffered, rows padded against bank conflicts); the V^T operand is read
+//    with ds_read_b64_tr_b16, the gfx950 LDS transpose read, straight from
+//    the row-major V rows.
 //  * Online softmax in the log2 domain; local and anchor reads separately
 //    normalised, then out = o_local + tanh(q . w_g) * o_anchor.
 #include "rma_kernels.h"
@@ -33,10 +35,17 @@ namespace {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+typedef short v8i16_t __attribute__((ext_vector_type(8)));
+
 constexpr int kPT = 32;          // keys per tile
-constexpr int kVRow = 520;       // bytes per staged V row (8-aligned, conflict-free gathers)
-constexpr int kTokPerWave = 4;
-constexpr int kTokPerWG = 16;
+// Bytes per staged row.  A 16-byte LDS read serves 16 lanes per pass and
+// an 8-byte one 32: K rows (16-byte operand reads of 16 consecutive keys)
+// are 132 dwords apart (4 mod 64 banks), V rows (8-byte transposed reads of
+// 4 lane groups x 4 keys) 136 dwords apart (8 mod 64), so that neither read
+// nor the row-wise staging writes have bank conflicts.
+constexpr int kRowK = 528;
+constexpr int kRowV = 544;
 
 __device__ __forceinline__ uint16_t to_bf16(float f) {
   uint32_t u = __float_as_uint(f);
@@ -45,62 +54,48 @@ __device__ __forceinline__ uint16_t to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
-__device__ __forceinline__ float bf2f(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
-
-// All-reduce over each row of 16 lanes with DPP moves (single-cycle VALU
-// operand swizzles, no LDS round trip): swap neighbours, swap pairs, then
-// mirror within 8 and within 16 lanes.  After the first two steps the 4
-// lanes of a quad agree, so each mirror combines two already-reduced
-// groups.
-template <int kCtrl>
-__device__ __forceinline__ float dpp(float x) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), kCtrl, 0xf, 0xf, false));
-}
-constexpr int kQuadSwap1 = 0xB1;     // quad_perm [1,0,3,2]
-constexpr int kQuadSwap2 = 0x4E;     // quad_perm [2,3,0,1]
-constexpr int kRowHalfMirror = 0x141;
-constexpr int kRowMirror = 0x140;
-
-__device__ __forceinline__ float row16_max(float x) {
-  x = fmaxf(x, dpp<kQuadSwap1>(x));
-  x = fmaxf(x, dpp<kQuadSwap2>(x));
-  x = fmaxf(x, dpp<kRowHalfMirror>(x));
-  x = fmaxf(x, dpp<kRowMirror>(x));
-  return x;
-}
-
-__device__ __forceinline__ float row16_sum(float x) {
-  x += dpp<kQuadSwap1>(x);
-  x += dpp<kQuadSwap2>(x);
-  x += dpp<kRowHalfMirror>(x);
-  x += dpp<kRowMirror>(x);
-  return x;
-}
-
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Two fp32 -> packed bf16 (a in the low half), round to nearest even: one
+// v_cvt_pk_bf16_f32 on gfx950.
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
+}
 
 // Key source of one segment (ring, block, bank).
 enum : int { kSegRing = 0, kSegBlock = 1, kSegBank = 2 };
 
-__global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillArgs a) {
+// Key slot order of a 32-key tile in the k dimension of the P.V product:
+// k slot 8 lg + j holds key 4 lg + j (j < 4, first 16-key sub-tile) or key
+// 16 + 4 lg + (j - 4) (second sub-tile), which is where the S^T accumulator
+// of lane group lg keeps them; the V^T operand is read in the same order.
+template <int kWaves>
+__global__ __launch_bounds__(64 * kWaves) void prefill_attn_kernel(PrefillArgs a) {
+  constexpr int kThreads = 64 * kWaves;
+  constexpr int kTokWG = 4 * kWaves;                     // 4 tokens (16 query rows) per wave
+  constexpr int kStage = 2 * kPT * kChunks / kThreads;   // K and V chunks staged per thread
   const int qt = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int u = b * a.G + g;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l16 = lane & 15, lg = lane >> 4;  // MFMA column / k-group
   const int n = a.n;
-  const int tok0 = qt * kTokPerWG + wave * kTokPerWave;  // first token of this wave
-  const int my_tok = tok0 + lg;                          // token of this lane's D rows
+  const int tok0 = qt * kTokWG + wave * 4;    // first token of this wave
+  const int q_tok = tok0 + (l16 >> 2);        // this lane's query: token q_tok, head q_head
+  const int q_head = l16 & 3;
 
-  __shared__ __attribute__((aligned(16))) unsigned char v_lds[2][kPT * kVRow];
-  __shared__ __attribute__((aligned(16))) uint16_t p_lds[4][16 * kPT];
+  // [buffer][32 keys][kRowK bytes] and [buffer][32 keys][kRowV bytes]
+  __shared__ __attribute__((aligned(16))) unsigned char k_lds[2][kPT * kRowK];
+  __shared__ __attribute__((aligned(16))) unsigned char v_lds[2][kPT * kRowV];
 
-  // Q as A-operands: 8 k-steps of 32 dims; row l16 -> token l16/4, head l16%4
+  // Q^T as B-operands (column = query): 8 k-steps of 32 dims
   uint4 qa[8];
   {
-    const int t = tok0 + (l16 >> 2), h = l16 & 3;
-    const bool ok = t < n;
+    const bool ok = q_tok < n;
     const uint4* qrow = reinterpret_cast<const uint4*>(
-        a.q + (((size_t)b * n + (ok ? t : 0)) * a.H + g * kHpg + h) * kD);
+        a.q + (((size_t)b * n + (ok ? q_tok : 0)) * a.H + g * kHpg + q_head) * kD);
 #pragma unroll
     for (int st = 0; st < 8; ++st) qa[st] = ok ? qrow[st * 4 + lg] : make_uint4(0, 0, 0, 0);
   }
@@ -115,7 +110,7 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillArgs a) {
   const int ring_valid = (int)(P < R ? P : R);
   const int t_ring = (ring_valid + kPT - 1) / kPT;
   // block keys a query tile can see: tokens 0 .. last token of the tile
-  int last_tok = qt * kTokPerWG + kTokPerWG - 1;
+  int last_tok = qt * kTokWG + kTokWG - 1;
   last_tok = last_tok < n - 1 ? last_tok : n - 1;
   const int t_blk = last_tok / kPT + 1;
   const int nb = a.bank_n[u];
@@ -168,155 +163,201 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillArgs a) {
     return sr;
   };
 
-  // cooperative V tile load: 32 keys x 32 chunks, 4 chunks per thread
-  uint4 vpre[4];
-  auto load_v = [&](int t) {
-    const Src sr = src_of(t);
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int id = tid + 256 * m;
-      const int key = id >> 5, c = id & 31;
-      int kk = sr.ti * kPT + key;
-      kk = kk < sr.cnt ? kk : sr.cnt - 1;
-      vpre[m] = sr.v[(size_t)kk * sr.vks + c];
-    }
+  // Cooperative staging of one tile: 32 keys x 32 chunks of K and of V.
+  // A stage is 2 K and 2 V chunks per thread (8-wave workgroups take one
+  // per tile, 4-wave ones two): chunk x = tid + kThreads * (2 part + m) of
+  // a plane.  K: key x % 32, chunk x / 32 (consecutive lanes read
+  // consecutive slots of one chunk plane); V: key x / 32, chunk x % 32 (32
+  // lanes per row).  Keys past the count re-read the last valid key.
+  // Named registers, no arrays: the stage must stay out of scratch.
+  constexpr int kParts = kStage / 4;
+  struct Stage {
+    uint4 k0, k1, v0, v1;
   };
-  auto store_v = [&](int buf) {
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int id = tid + 256 * m;
-      const int key = id >> 5, c = id & 31;
-      uint2* dst = reinterpret_cast<uint2*>(&v_lds[buf][key * kVRow + c * 16]);
-      dst[0] = make_uint2(vpre[m].x, vpre[m].y);
-      dst[1] = make_uint2(vpre[m].z, vpre[m].w);
-    }
-  };
-  // K B-operands of a tile: 2 sub-tiles of 16 keys x 8 k-steps
-  uint4 kb[2][8];
-  auto load_k = [&](int t) {
+  auto stage_load = [&](int t, int part) {
     const Src sr = src_of(t);
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      int kk = sr.ti * kPT + sub * 16 + l16;
+    // offsets in 16-byte units fit 32 bits (< 2^16 within one unit's plane)
+    auto kload = [&](int m) {
+      const int x = tid + kThreads * (2 * part + m);
+      int kk = sr.ti * kPT + (x & 31);
       kk = kk < sr.cnt ? kk : sr.cnt - 1;
-#pragma unroll
-      for (int st = 0; st < 8; ++st)
-        kb[sub][st] = sr.k[(size_t)kk * sr.kks + (size_t)(st * 4 + lg) * sr.kcs];
-    }
+      return sr.k[(uint32_t)(kk * sr.kks + (x >> 5) * sr.kcs)];
+    };
+    auto vload = [&](int m) {
+      const int x = tid + kThreads * (2 * part + m);
+      int kv = sr.ti * kPT + (x >> 5);
+      kv = kv < sr.cnt ? kv : sr.cnt - 1;
+      return sr.v[(uint32_t)(kv * sr.vks + (x & 31))];
+    };
+    Stage sg;
+    sg.k0 = kload(0);
+    sg.k1 = kload(1);
+    sg.v0 = vload(0);
+    sg.v1 = vload(1);
+    return sg;
+  };
+  auto stage_store = [&](int buf, int part, const Stage& sg) {
+    const int x0 = tid + kThreads * (2 * part), x1 = x0 + kThreads;
+    *reinterpret_cast<uint4*>(&k_lds[buf][(x0 & 31) * kRowK + (x0 >> 5) * 16]) = sg.k0;
+    *reinterpret_cast<uint4*>(&k_lds[buf][(x1 & 31) * kRowK + (x1 >> 5) * 16]) = sg.k1;
+    *reinterpret_cast<uint4*>(&v_lds[buf][(x0 >> 5) * kRowV + (x0 & 31) * 16]) = sg.v0;
+    *reinterpret_cast<uint4*>(&v_lds[buf][(x1 >> 5) * kRowV + (x1 & 31) * 16]) = sg.v1;
   };
 
-  f32x4_t o[16];    // the running read: 16 dim sub-tiles of 16 rows x 16 dims
+  f32x4_t o[16];    // running read O^T: register i of lane (lg, l16) = dim 16 dt + 4 lg + i, query l16
   f32x4_t oloc[16]; // the finished local read
-  float m[4], l[4];
+  float m_run, l_run;
   auto reset = [&]() {
 #pragma unroll
     for (int dt = 0; dt < 16; ++dt) o[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      m[i] = -INFINITY;
-      l[i] = 0.f;
-    }
+    m_run = -INFINITY;
+    l_run = 0.f;
   };
   reset();
 
-  if (t_all > 0) {
-    load_v(0);
-    store_v(0);
-    load_k(0);
-  }
+  // tile 0 into LDS; tile 1 in registers (each tile's loads are issued two
+  // tiles ahead of its use, so they have two tiles of work to land)
+  stage_store(0, 0, stage_load(0, 0));
+  if (kParts == 2) stage_store(0, 1, stage_load(0, 1));
+  const int t1 = 1 < t_all ? 1 : 0;
+  Stage pf0 = stage_load(t1, 0);
+  Stage pf1 = kParts == 2 ? stage_load(t1, 1) : pf0;
   __syncthreads();
 
   for (int t = 0; t < t_all; ++t) {
     int seg, ti;
     seg_of(t, seg, ti);
     const int cnt = seg_count(seg);
-    const bool has_next = t + 1 < t_all;
-    // prefetch without branches: past the last tile, reload the last one
-    const int tn = has_next ? t + 1 : t;
-    load_v(tn);
+    // prefetch of tile t + 2, without branches: past the last tile, reload
+    // the last one
+    const int tn = t + 2 < t_all ? t + 2 : t_all - 1;
+    const Stage next0 = stage_load(tn, 0);
+    const Stage next1 = kParts == 2 ? stage_load(tn, 1) : next0;
 
-    // S = Q K^T for 32 keys
-    f32x4_t s[2];
+    const unsigned char* kl = k_lds[t & 1];
+    const unsigned char* vl = v_lds[t & 1];
+
+    // S^T = K Q^T for the tile's two 16-key sub-tiles: A = 16 keys x 32
+    // dims (lane: key l16, chunk 4 st + lg), B = Q^T
+    f32x4_t s[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      s[sub] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int st = 0; st < 8; ++st) {
 #pragma unroll
-      for (int st = 0; st < 8; ++st)
-        s[sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qa[st]), as_bf16x8(kb[sub][st]),
+      for (int sub = 0; sub < 2; ++sub) {
+        const uint4 ka = *reinterpret_cast<const uint4*>(&kl[(sub * 16 + l16) * kRowK +
+                                                              (st * 4 + lg) * 16]);
+        s[sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka), as_bf16x8(qa[st]),
                                                           s[sub], 0, 0, 0);
-    }
-    load_k(tn);
-
-    // mask and scale: lane's token my_tok, key = column l16 of each sub-tile
-    float sv[2][4];
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      const int kk = ti * kPT + sub * 16 + l16;
-      bool vis = kk < cnt && my_tok < n;
-      if (seg == kSegRing) {
-        int age = kk - p_mod;
-        age += age < 0 ? R : 0;
-        vis = vis && age >= min_age && age >= my_tok;
-      } else if (seg == kSegBlock) {
-        vis = vis && kk <= my_tok;
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sv[sub][i] = vis ? s[sub][i] * a.sl2e : -INFINITY;
     }
 
-    // online softmax per row (token my_tok, head i)
-    float pb[2][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float mt = row16_max(fmaxf(sv[0][i], sv[1][i]));
-      const float mn = fmaxf(m[i], mt);
-      const float mref = mn == -INFINITY ? 0.f : mn;
-      const float al = __builtin_amdgcn_exp2f(m[i] - mref);
-      pb[0][i] = __builtin_amdgcn_exp2f(sv[0][i] - mref);
-      pb[1][i] = __builtin_amdgcn_exp2f(sv[1][i] - mref);
-      l[i] = l[i] * al + row16_sum(pb[0][i] + pb[1][i]);
-      m[i] = mn;
-#pragma unroll
-      for (int dt = 0; dt < 16; ++dt) o[dt][i] *= al;
+    // Mask.  A tile every key of which is visible to every query of the
+    // wave (most ring and bank tiles) skips it; the test is wave-uniform.
+    //   ring: slot kk holds age (kk - P) mod R; query token q sees ages
+    //         >= max(min_age, q); the tile's least age is 0 if it holds
+    //         slot P mod R, else that of its first slot
+    //   block: keys up to the query's own token
+    //   bank: all committed keys
+    const int kt0 = ti * kPT;
+    bool full = kt0 + kPT <= cnt;
+    if (seg == kSegRing) {
+      int a0 = kt0 - p_mod;
+      a0 += a0 < 0 ? R : 0;
+      const int amin = (p_mod >= kt0 && p_mod < kt0 + kPT) ? 0 : a0;
+      const int need = min_age > tok0 + 3 ? min_age : tok0 + 3;
+      full = full && amin >= need;
+    } else if (seg == kSegBlock) {
+      full = full && kt0 + kPT - 1 <= tok0;
     }
-    // P (bf16) to the A layout through this wave's LDS slice
-    uint16_t* ps = p_lds[wave];
+    float sv[2][4];
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) ps[(lg * 4 + i) * kPT + sub * 16 + l16] = to_bf16(pb[sub][i]);
-    __builtin_amdgcn_wave_barrier();
-    const uint4 pa = *reinterpret_cast<const uint4*>(&ps[l16 * kPT + lg * 8]);
+      for (int i = 0; i < 4; ++i) sv[sub][i] = s[sub][i];
+    if (!full) {
+#pragma unroll
+      for (int sub = 0; sub < 2; ++sub) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int kk = kt0 + sub * 16 + lg * 4 + i;
+          bool vis = kk < cnt && q_tok < n;
+          if (seg == kSegRing) {
+            int age = kk - p_mod;
+            age += age < 0 ? R : 0;
+            vis = vis && age >= min_age && age >= q_tok;
+          } else if (seg == kSegBlock) {
+            vis = vis && kk <= q_tok;
+          }
+          sv[sub][i] = vis ? sv[sub][i] : -INFINITY;
+        }
+      }
+    }
 
-    // O += P V: B-operand = 8 keys (8*lg .. 8*lg+7) of dim 16*dt + l16
-    const unsigned char* vt = v_lds[t & 1];
+    // online softmax of this lane's query (log2 domain, scale folded into
+    // the exponent): the tile's 32 keys are this lane's 8 values and those
+    // of lanes l16 + 16, + 32, + 48
+    float mt = fmaxf(fmaxf(fmaxf(sv[0][0], sv[0][1]), fmaxf(sv[0][2], sv[0][3])),
+                     fmaxf(fmaxf(sv[1][0], sv[1][1]), fmaxf(sv[1][2], sv[1][3])));
+    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    const float mn = fmaxf(m_run, mt * a.sl2e);
+    const float mref = mn == -INFINITY ? 0.f : mn;
+    const float al = __builtin_amdgcn_exp2f(m_run - mref);
+    float pr[2][4];
+    float ps = 0.f;
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        pr[sub][i] = __builtin_amdgcn_exp2f(fmaf(sv[sub][i], a.sl2e, -mref));
+        ps += pr[sub][i];
+      }
+    ps += __shfl_xor(ps, 16, 64);
+    ps += __shfl_xor(ps, 32, 64);
+    l_run = l_run * al + ps;
+    // rescale only if some lane's maximum grew (elsewhere al == 1 exactly)
+    if (__any(mn > m_run)) {
+#pragma unroll
+      for (int dt = 0; dt < 16; ++dt) o[dt] *= al;
+    }
+    m_run = mn;
+
+    // P^T B-operand straight from registers (k slot order above), bf16
+    uint4 pb;
+    pb.x = pack_bf16(pr[0][0], pr[0][1]);
+    pb.y = pack_bf16(pr[0][2], pr[0][3]);
+    pb.z = pack_bf16(pr[1][0], pr[1][1]);
+    pb.w = pack_bf16(pr[1][2], pr[1][3]);
+
+    // O^T += V^T P^T.  A = V^T rows 16 dt .. 16 dt + 15 in k slot order,
+    // read transposed from the row-major V tile: in each 16-lane group,
+    // ds_read_b64_tr_b16 gives lane 4a + b element b of the 4 elements
+    // read by lanes a, a + 4, a + 8, a + 12; so lane l16 of group lg
+    // addresses key 16 h + 4 lg + l16 / 4, dims 16 dt + 4 (l16 % 4) .. + 3
+    // (h = 0: k slots 0-3 of the group, h = 1: slots 4-7).
 #pragma unroll
     for (int dt = 0; dt < 16; ++dt) {
-      const int dim = dt * 16 + l16;
-      uint16_t e[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        e[j] = *reinterpret_cast<const uint16_t*>(&vt[(lg * 8 + j) * kVRow + dim * 2]);
-      uint4 vb;
-      vb.x = (uint32_t)e[0] | ((uint32_t)e[1] << 16);
-      vb.y = (uint32_t)e[2] | ((uint32_t)e[3] << 16);
-      vb.z = (uint32_t)e[4] | ((uint32_t)e[5] << 16);
-      vb.w = (uint32_t)e[6] | ((uint32_t)e[7] << 16);
-      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(pa), as_bf16x8(vb), o[dt], 0, 0, 0);
+      const unsigned char* v0 = &vl[(4 * lg + (l16 >> 2)) * kRowV + (16 * dt + 4 * (l16 & 3)) * 2];
+      const v4i16_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4i16_t*)(v0));
+      const v4i16_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) v4i16_t*)(v0 + 16 * kRowV));
+      const bf16x8_t va = __builtin_bit_cast(
+          bf16x8_t, (v8i16_t){lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+      o[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, as_bf16x8(pb), o[dt], 0, 0, 0);
     }
-    __builtin_amdgcn_wave_barrier();
 
     // end of the local read: normalise and keep it
     if (t == t_loc - 1) {
+      const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float inv = l[i] > 0.f ? 1.f / l[i] : 0.f;
-#pragma unroll
-        for (int dt = 0; dt < 16; ++dt) oloc[dt][i] = o[dt][i] * inv;
-      }
+      for (int dt = 0; dt < 16; ++dt) oloc[dt] = o[dt] * inv;
       reset();
     }
-    store_v((t + 1) & 1);
+    stage_store((t + 1) & 1, 0, pf0);  // tile t + 1
+    if (kParts == 2) stage_store((t + 1) & 1, 1, pf1);
+    pf0 = next0;
+    pf1 = next1;
     __syncthreads();
   }
   if (t_loc == 0) {
@@ -326,16 +367,12 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillArgs a) {
   }
 
   // anchor read (zero for an empty bank)
-  float inv_b[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) inv_b[i] = (t_bank > 0 && l[i] > 0.f) ? 1.f / l[i] : 0.f;
+  const float inv_b = (t_bank > 0 && l_run > 0.f) ? 1.f / l_run : 0.f;
 
-  // gate argument q . w_g for row l16 (token l16/4, head l16%4), summed over
-  // the 4 k-groups; then fetched for the D-layout rows (token lg, head i)
+  // gate argument q . w_g of this lane's query, summed over the 4 k-groups
   float z = 0.f;
   {
-    const int h = l16 & 3;
-    const float* wrow = a.w_g + (size_t)(g * kHpg + h) * kD;
+    const float* wrow = a.w_g + (size_t)(g * kHpg + q_head) * kD;
 #pragma unroll
     for (int st = 0; st < 8; ++st) {
       const float4 w0 = reinterpret_cast<const float4*>(wrow + st * 32 + lg * 8)[0];
@@ -353,17 +390,17 @@ __global__ __launch_bounds__(256) void prefill_attn_kernel(PrefillArgs a) {
     z += __shfl_xor(z, 16, 64);
     z += __shfl_xor(z, 32, 64);
   }
-  float gate[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) gate[i] = tanhf(__shfl(z, lg * 4 + i, 64));
+  const float gate = tanhf(z);
 
-  if (my_tok < n) {
+  if (q_tok < n) {
+    uint16_t* orow = a.out + (((size_t)b * n + q_tok) * a.H + g * kHpg + q_head) * kD;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint16_t* orow = a.out + (((size_t)b * n + my_tok) * a.H + g * kHpg + i) * kD;
+    for (int dt = 0; dt < 16; ++dt) {
+      float e[4];
 #pragma unroll
-      for (int dt = 0; dt < 16; ++dt)
-        orow[dt * 16 + l16] = to_bf16(fmaf(gate[i], o[dt][i] * inv_b[i], oloc[dt][i]));
+      for (int i = 0; i < 4; ++i) e[i] = fmaf(gate, o[dt][i] * inv_b, oloc[dt][i]);
+      *reinterpret_cast<uint2*>(orow + 16 * dt + 4 * lg) =
+          make_uint2(pack_bf16(e[0], e[1]), pack_bf16(e[2], e[3]));
     }
   }
 }
@@ -403,8 +440,15 @@ __global__ __launch_bounds__(128) void prefill_commit_kernel(PrefillArgs a) {
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
-  const int tiles = (a.n + kTokPerWG - 1) / kTokPerWG;
-  hipLaunchKernelGGL(prefill_attn_kernel, dim3(tiles, a.G, a.B), dim3(256), 0, s, a);
+  // 8-wave workgroups (32 tokens: twice the reuse of every staged tile)
+  // when that still gives a workgroup per CU; else 4-wave ones
+  const int tiles8 = (a.n + 31) / 32;
+  if ((int64_t)tiles8 * a.G * a.B >= 256) {
+    hipLaunchKernelGGL(prefill_attn_kernel<8>, dim3(tiles8, a.G, a.B), dim3(512), 0, s, a);
+  } else {
+    const int tiles4 = (a.n + 15) / 16;
+    hipLaunchKernelGGL(prefill_attn_kernel<4>, dim3(tiles4, a.G, a.B), dim3(256), 0, s, a);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(prefill_commit_kernel, dim3(a.n, a.B * a.G), dim3(128), 0, s, a);
