@@ -65,6 +65,37 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
 }
 
+// Max / sum of the values of lanes l and l ^ 16 (resp. l ^ 32), in every
+// lane: v_permlane16_swap / v_permlane32_swap with the value in both
+// operands leave the lane's own value in one result and its partner's in
+// the other (which is which depends on the lane; max and + do not care).
+// VALU only, no LDS round trip.
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u32x2_t swap16(float x) {
+  const unsigned u = __float_as_uint(x);
+  return __builtin_amdgcn_permlane16_swap(u, u, false, false);
+}
+__device__ __forceinline__ u32x2_t swap32(float x) {
+  const unsigned u = __float_as_uint(x);
+  return __builtin_amdgcn_permlane32_swap(u, u, false, false);
+}
+__device__ __forceinline__ float max16(float x) {
+  const u32x2_t r = swap16(x);
+  return fmaxf(__uint_as_float(r.x), __uint_as_float(r.y));
+}
+__device__ __forceinline__ float max32(float x) {
+  const u32x2_t r = swap32(x);
+  return fmaxf(__uint_as_float(r.x), __uint_as_float(r.y));
+}
+__device__ __forceinline__ float sum16(float x) {
+  const u32x2_t r = swap16(x);
+  return __uint_as_float(r.x) + __uint_as_float(r.y);
+}
+__device__ __forceinline__ float sum32(float x) {
+  const u32x2_t r = swap32(x);
+  return __uint_as_float(r.x) + __uint_as_float(r.y);
+}
+
 // Key source of one segment (ring, block, bank).
 enum : int { kSegRing = 0, kSegBlock = 1, kSegBank = 2 };
 
@@ -77,8 +108,24 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_kernel(PrefillArgs a
   constexpr int kThreads = 64 * kWaves;
   constexpr int kTokWG = 4 * kWaves;                     // 4 tokens (16 query rows) per wave
   constexpr int kStage = 2 * kPT * kChunks / kThreads;   // K and V chunks staged per thread
-  const int qt = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int u = b * a.G + g;
+  // Workgroup -> (query tile, sequence, group).  The hardware hands
+  // workgroup w to XCD w mod 8, each XCD with its own L2; all query tiles of
+  // one (sequence, group) read the same K/V tiles, so when the number of
+  // (sequence, group) units is a multiple of 8 they are all placed on one
+  // XCD (w mod 8 fixed) and share its L2.
+  const int nqt = (a.n + kTokWG - 1) / kTokWG;
+  const int units = a.B * a.G;
+  const int w = blockIdx.x;
+  int qt, u;
+  if ((units & 7) == 0) {
+    const int r = w >> 3;
+    qt = r % nqt;
+    u = (w & 7) + 8 * (r / nqt);
+  } else {
+    qt = w % nqt;
+    u = w / nqt;
+  }
+  const int b = u / a.G, g = u - b * a.G;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l16 = lane & 15, lg = lane >> 4;  // MFMA column / k-group
   const int n = a.n;
@@ -298,8 +345,7 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_kernel(PrefillArgs a
     // of lanes l16 + 16, + 32, + 48
     float mt = fmaxf(fmaxf(fmaxf(sv[0][0], sv[0][1]), fmaxf(sv[0][2], sv[0][3])),
                      fmaxf(fmaxf(sv[1][0], sv[1][1]), fmaxf(sv[1][2], sv[1][3])));
-    mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-    mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+    mt = max32(max16(mt));
     const float mn = fmaxf(m_run, mt * a.sl2e);
     const float mref = mn == -INFINITY ? 0.f : mn;
     const float al = __builtin_amdgcn_exp2f(m_run - mref);
@@ -312,8 +358,7 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_kernel(PrefillArgs a
         pr[sub][i] = __builtin_amdgcn_exp2f(fmaf(sv[sub][i], a.sl2e, -mref));
         ps += pr[sub][i];
       }
-    ps += __shfl_xor(ps, 16, 64);
-    ps += __shfl_xor(ps, 32, 64);
+    ps = sum32(sum16(ps));
     l_run = l_run * al + ps;
     // rescale only if some lane's maximum grew (elsewhere al == 1 exactly)
     if (__any(mn > m_run)) {
@@ -442,12 +487,13 @@ __global__ __launch_bounds__(128) void prefill_commit_kernel(PrefillArgs a) {
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
   // 8-wave workgroups (32 tokens: twice the reuse of every staged tile)
   // when that still gives a workgroup per CU; else 4-wave ones
+  const int units = a.B * a.G;
   const int tiles8 = (a.n + 31) / 32;
-  if ((int64_t)tiles8 * a.G * a.B >= 256) {
-    hipLaunchKernelGGL(prefill_attn_kernel<8>, dim3(tiles8, a.G, a.B), dim3(512), 0, s, a);
+  if ((int64_t)tiles8 * units >= 256) {
+    hipLaunchKernelGGL(prefill_attn_kernel<8>, dim3(tiles8 * units), dim3(512), 0, s, a);
   } else {
     const int tiles4 = (a.n + 15) / 16;
-    hipLaunchKernelGGL(prefill_attn_kernel<4>, dim3(tiles4, a.G, a.B), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(prefill_attn_kernel<4>, dim3(tiles4 * units), dim3(256), 0, s, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
