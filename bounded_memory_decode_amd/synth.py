@@ -38,7 +38,7 @@ import numpy as np
 KIND = {
     "ring_k": 1, "ring_v": 2, "bank_k": 3, "bank_v": 4, "bscore": 5, "bsrc": 6,
     "q": 7, "k": 8, "v": 9, "ck": 10, "cv": 11, "cs": 12, "w_g": 13,
-    "pend_k": 14, "pend_v": 15, "pscore": 16,
+    "pend_k": 14, "pend_v": 15, "pscore": 16, "q_anchor": 17,
 }
 
 
@@ -220,6 +220,22 @@ def step_inputs(w: Workload, seed: int, layer: int, step: int,
         idx = [int(b) for b in batch]
         out = {k: np.ascontiguousarray(v[idx]) for k, v in out.items()}
     return out
+
+
+def anchor_query(w: Workload, seed: int, layer: int, step: int,
+                 batch: Optional[Sequence[int]] = None) -> np.ndarray:
+    """A second query per head, [b][H][d] bf16 bits, drawn like q from its
+    own stream (one per (layer, step), the whole batch)."""
+    qa = _normal_bf16(_rng(seed, w, "q_anchor", layer, step), (w.B, w.H, w.d), w.qkv_std)
+    if batch is not None:
+        qa = np.ascontiguousarray(qa[[int(b) for b in batch]])
+    return qa
+
+
+def block_anchor_query(w: Workload, seed: int, layer: int, step0: int, n: int,
+                       batch: Optional[Sequence[int]] = None) -> np.ndarray:
+    """anchor_query for n consecutive tokens: [b][n][H][d]."""
+    return np.stack([anchor_query(w, seed, layer, step0 + i, batch) for i in range(n)], axis=1)
 
 
 def block_inputs(w: Workload, seed: int, layer: int, step0: int, n: int,

@@ -58,11 +58,11 @@ def lib():
         if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
             build(force=True)
         L = ctypes.CDLL(_LIB)
-        L.orc_decode_step.argtypes = [ctypes.POINTER(_State), ctypes.c_int32] + [_P] * 7 + [_P, ctypes.c_int32]
+        L.orc_decode_step.argtypes = [ctypes.POINTER(_State), ctypes.c_int32] + [_P] * 8 + [_P, ctypes.c_int32]
         L.orc_decode_step.restype = ctypes.c_int
         L.orc_admit.argtypes = [ctypes.POINTER(_State), ctypes.c_int32, _P]
         L.orc_admit.restype = ctypes.c_int
-        L.orc_prefill_block.argtypes = [ctypes.POINTER(_State), ctypes.c_int32, ctypes.c_int32] + [_P] * 7 + [_P]
+        L.orc_prefill_block.argtypes = [ctypes.POINTER(_State), ctypes.c_int32, ctypes.c_int32] + [_P] * 8 + [_P]
         L.orc_prefill_block.restype = ctypes.c_int
         L.orc_round_bf16.argtypes = [ctypes.c_double]
         L.orc_round_bf16.restype = ctypes.c_uint16
@@ -156,16 +156,21 @@ class OracleState:
         return s
 
     def decode_step(self, layer: int, q, k, v, ck, cv, cs, w_g,
-                    compute_out: bool = True) -> Optional[np.ndarray]:
+                    compute_out: bool = True, q_anchor=None) -> Optional[np.ndarray]:
         """One token for all B sequences of `layer`; returns out [B][H][d]
-        float64 (unrounded) or None when compute_out is False."""
+        float64 (unrounded) or None when compute_out is False.  q_anchor
+        [B][H][d] (bf16 bits), if given, is the query of the anchor read and
+        the gate; else q serves both reads."""
         B, H, G, d = self.B, self.H, self.G, self.d
-        arrs = [_c(q, np.uint16).reshape(B, H, d)] + \
-               [_c(x, np.uint16).reshape(B, G, d) for x in (k, v, ck, cv)] + \
+        qa = None if q_anchor is None else _c(q_anchor, np.uint16).reshape(B, H, d)
+        arrs = [_c(x, np.uint16).reshape(B, G, d) for x in (k, v, ck, cv)] + \
                [_c(cs, np.float32).reshape(B, G), _c(w_g, np.float32).reshape(H, d)]
+        q = _c(q, np.uint16).reshape(B, H, d)
         out = np.empty((B, H, d), np.float64) if compute_out else None
         st = self._struct()
-        rc = lib().orc_decode_step(ctypes.byref(st), layer, *[_ptr(a) for a in arrs],
+        rc = lib().orc_decode_step(ctypes.byref(st), layer, _ptr(q),
+                                   _ptr(qa) if qa is not None else None,
+                                   *[_ptr(a) for a in arrs],
                                    _ptr(out) if out is not None else None, int(compute_out))
         if rc != ORC_OK:
             raise OracleError(rc, "decode_step")
@@ -181,16 +186,19 @@ class OracleState:
         return moved
 
     def prefill_block(self, layer: int, q, k, v, ck, cv, cs, w_g,
-                      compute_out: bool = True) -> Optional[np.ndarray]:
+                      compute_out: bool = True, q_anchor=None) -> Optional[np.ndarray]:
         B, H, G, d = self.B, self.H, self.G, self.d
         q = _c(q, np.uint16)
         n = q.shape[1]
-        arrs = [q.reshape(B, n, H, d)] + \
-               [_c(x, np.uint16).reshape(B, n, G, d) for x in (k, v, ck, cv)] + \
+        q = q.reshape(B, n, H, d)
+        qa = None if q_anchor is None else _c(q_anchor, np.uint16).reshape(B, n, H, d)
+        arrs = [_c(x, np.uint16).reshape(B, n, G, d) for x in (k, v, ck, cv)] + \
                [_c(cs, np.float32).reshape(B, n, G), _c(w_g, np.float32).reshape(H, d)]
         out = np.empty((B, n, H, d), np.float64) if compute_out else None
         st = self._struct()
-        rc = lib().orc_prefill_block(ctypes.byref(st), layer, n, *[_ptr(a) for a in arrs],
+        rc = lib().orc_prefill_block(ctypes.byref(st), layer, n, _ptr(q),
+                                     _ptr(qa) if qa is not None else None,
+                                     *[_ptr(a) for a in arrs],
                                      _ptr(out) if out is not None else None)
         if rc != ORC_OK:
             raise OracleError(rc, "prefill_block")

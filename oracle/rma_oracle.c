@@ -128,11 +128,16 @@ static void attend(int d, double scale, const double* q, int nk,
  *   - anchor read: committed bank slots 0 .. n-1 of the query's group.
  *     Reading: n == 0 gives a zero anchor read.
  *   - Reading (gate form, fixed for this build): out = o_local +
- *     tanh(<q_h, w_g[h]>) * o_anchor, two separately normalised reads.
+ *     tanh(<qa_h, w_g[h]>) * o_anchor, two separately normalised reads,
+ *     where qa is the query of the anchor read.
+ *   - Reading: the anchor read and the gate use their own query qa (the
+ *     card's "separate RMA modules" and "query-dependent read"); when no
+ *     such query is given, qa = q, the attention query of the head.
  *   - Reading: heads h = g*(H/G) ... g*(H/G)+H/G-1 share group g.
  */
 static void token_output(const orc_state* st, int32_t layer, int32_t b, int32_t g,
                          int64_t t, const uint16_t* qtok /*[H][d]*/,
+                         const uint16_t* qatok /*[H][d]*/,
                          const uint16_t* kcur, const uint16_t* vcur,
                          const float* w_g /*[H][d]*/, double* out /*[H][d]*/) {
   const orc_cfg* c = &st->cfg;
@@ -171,26 +176,28 @@ static void token_output(const orc_state* st, int32_t layer, int32_t b, int32_t 
   const int ns = nloc > n ? nloc : n;
   double* s = (double*)malloc(sizeof(double) * ns);
   double* q = (double*)malloc(sizeof(double) * d);
+  double* qa = (double*)malloc(sizeof(double) * d);
   double* oloc = (double*)malloc(sizeof(double) * d);
   double* oanc = (double*)malloc(sizeof(double) * d);
 
   for (int hh = 0; hh < hpg; ++hh) {
     const int h = g * hpg + hh;
     for (int i = 0; i < d; ++i) q[i] = bf16_to_double(qtok[(size_t)h * d + i]);
+    for (int i = 0; i < d; ++i) qa[i] = bf16_to_double(qatok[(size_t)h * d + i]);
 
     attend(d, c->scale, q, nloc, lk, lv, s, oloc);
     if (n > 0) {
-      attend(d, c->scale, q, n, ak, av, s, oanc);
+      attend(d, c->scale, qa, n, ak, av, s, oanc);
     } else {
       for (int i = 0; i < d; ++i) oanc[i] = 0.0;
     }
 
     double zg = 0.0;
-    for (int i = 0; i < d; ++i) zg += q[i] * (double)w_g[(size_t)h * d + i];
+    for (int i = 0; i < d; ++i) zg += qa[i] * (double)w_g[(size_t)h * d + i];
     const double gate = tanh(zg);
     for (int i = 0; i < d; ++i) out[(size_t)h * d + i] = oloc[i] + gate * oanc[i];
   }
-  free(lk); free(lv); free(ak); free(av); free(s); free(q); free(oloc); free(oanc);
+  free(lk); free(lv); free(ak); free(av); free(s); free(q); free(qa); free(oloc); free(oanc);
 }
 
 /* Write (ai-primer list item 1; tpsreport "How it works"): the current
@@ -213,9 +220,9 @@ static void token_write(const orc_state* st, int32_t layer, int32_t b, int32_t g
 }
 
 int orc_decode_step(const orc_state* st, int32_t layer,
-                    const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                    const uint16_t* ck, const uint16_t* cv, const float* cs,
-                    const float* w_g, double* out, int32_t compute_out) {
+                    const uint16_t* q, const uint16_t* q_anchor, const uint16_t* k,
+                    const uint16_t* v, const uint16_t* ck, const uint16_t* cv,
+                    const float* cs, const float* w_g, double* out, int32_t compute_out) {
   if (!cfg_ok(st) || layer < 0 || layer >= st->cfg.L) return ORC_E_ARG;
   const orc_cfg* c = &st->cfg;
   const int64_t t = st->t[layer];
@@ -229,6 +236,7 @@ int orc_decode_step(const orc_state* st, int32_t layer,
     for (int b = 0; b < B; ++b)
       for (int g = 0; g < G; ++g)
         token_output(st, layer, b, g, t, q + (size_t)b * H * d,
+                     (q_anchor ? q_anchor : q) + (size_t)b * H * d,
                      k + ((size_t)b * G + g) * d, v + ((size_t)b * G + g) * d,
                      w_g, out + (size_t)b * H * d);
   }
@@ -349,15 +357,16 @@ int orc_admit(const orc_state* st, int32_t layer, int32_t* moved) {
  * the next block, model card "How Rock Memory Anchors work"), and admit
  * waits for the block's end. */
 int orc_prefill_block(const orc_state* st, int32_t layer, int32_t n,
-                      const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                      const uint16_t* ck, const uint16_t* cv, const float* cs,
-                      const float* w_g, double* out) {
+                      const uint16_t* q, const uint16_t* q_anchor, const uint16_t* k,
+                      const uint16_t* v, const uint16_t* ck, const uint16_t* cv,
+                      const float* cs, const float* w_g, double* out) {
   if (!cfg_ok(st) || layer < 0 || layer >= st->cfg.L) return ORC_E_ARG;
   const orc_cfg* c = &st->cfg;
   if (n < 1 || n > c->C) return ORC_E_ARG;
   if (st->pend_n[layer] != 0 || st->t[layer] % c->C != 0) return ORC_E_NOT_BOUNDARY;
   const int B = st->B, G = c->G, H = c->H, d = c->d;
   uint16_t* tq = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)B * H * d);
+  uint16_t* tqa = q_anchor ? (uint16_t*)malloc(sizeof(uint16_t) * (size_t)B * H * d) : NULL;
   uint16_t* tk = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)B * G * d);
   uint16_t* tv = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)B * G * d);
   uint16_t* tck = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)B * G * d);
@@ -368,17 +377,20 @@ int orc_prefill_block(const orc_state* st, int32_t layer, int32_t n,
   for (int i = 0; i < n && rc == ORC_OK; ++i) {
     for (int b = 0; b < B; ++b) {
       memcpy(tq + (size_t)b * H * d, q + ((size_t)b * n + i) * H * d, sizeof(uint16_t) * H * d);
+      if (tqa)
+        memcpy(tqa + (size_t)b * H * d, q_anchor + ((size_t)b * n + i) * H * d,
+               sizeof(uint16_t) * H * d);
       memcpy(tk + (size_t)b * G * d, k + ((size_t)b * n + i) * G * d, sizeof(uint16_t) * G * d);
       memcpy(tv + (size_t)b * G * d, v + ((size_t)b * n + i) * G * d, sizeof(uint16_t) * G * d);
       memcpy(tck + (size_t)b * G * d, ck + ((size_t)b * n + i) * G * d, sizeof(uint16_t) * G * d);
       memcpy(tcv + (size_t)b * G * d, cv + ((size_t)b * n + i) * G * d, sizeof(uint16_t) * G * d);
       memcpy(tcs + (size_t)b * G, cs + ((size_t)b * n + i) * G, sizeof(float) * G);
     }
-    rc = orc_decode_step(st, layer, tq, tk, tv, tck, tcv, tcs, w_g, tout, out != NULL);
+    rc = orc_decode_step(st, layer, tq, tqa, tk, tv, tck, tcv, tcs, w_g, tout, out != NULL);
     if (out)
       for (int b = 0; b < B; ++b)
         memcpy(out + ((size_t)b * n + i) * H * d, tout + (size_t)b * H * d, sizeof(double) * H * d);
   }
-  free(tq); free(tk); free(tv); free(tck); free(tcv); free(tcs); free(tout);
+  free(tq); free(tqa); free(tk); free(tv); free(tck); free(tcv); free(tcs); free(tout);
   return rc;
 }

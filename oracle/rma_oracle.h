@@ -70,7 +70,10 @@ typedef struct {
 #define ORC_E_NOT_BOUNDARY (-3)
 
 /* One decode token for every sequence of layer `layer`.
- *   q     [B][H][d] bf16       k, v   [B][G][d] bf16 (current token)
+ *   q     [B][H][d] bf16 (query of the local read)
+ *   q_anchor [B][H][d] bf16 (query of the anchor read and the gate), or
+ *         NULL: q
+ *   k, v  [B][G][d] bf16 (current token)
  *   ck,cv [B][G][d] bf16 (candidate record)   cs [B][G] float (its score)
  *   w_g   [H][d] float (gate weights of this layer)
  *   out   [B][H][d] double (unrounded output), may be NULL when
@@ -78,9 +81,9 @@ typedef struct {
  * Reads come first; then the ring write, the pending append, t += 1.
  * Returns ORC_E_PENDING_FULL when C candidates wait for an admit. */
 int orc_decode_step(const orc_state* st, int32_t layer,
-                    const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                    const uint16_t* ck, const uint16_t* cv, const float* cs,
-                    const float* w_g, double* out, int32_t compute_out);
+                    const uint16_t* q, const uint16_t* q_anchor, const uint16_t* k,
+                    const uint16_t* v, const uint16_t* ck, const uint16_t* cv,
+                    const float* cs, const float* w_g, double* out, int32_t compute_out);
 
 /* Admit for layer `layer`; requires a full pending buffer (pend_n == C,
  * which happens at t % C == 0), else ORC_E_NOT_BOUNDARY.  `moved` [B][G] (may be NULL) receives the number of candidate
@@ -91,12 +94,12 @@ int orc_admit(const orc_state* st, int32_t layer, int32_t* moved);
  * (pend_n == 0, else ORC_E_NOT_BOUNDARY):
  * the tokens are decoded in order against the committed bank, with no
  * admit inside the block.  Shapes as orc_decode_step with a token axis
- * after the batch axis: q [B][n][H][d], k [B][n][G][d], cs [B][n][G],
- * out [B][n][H][d]. */
+ * after the batch axis: q, q_anchor [B][n][H][d], k [B][n][G][d],
+ * cs [B][n][G], out [B][n][H][d]. */
 int orc_prefill_block(const orc_state* st, int32_t layer, int32_t n,
-                      const uint16_t* q, const uint16_t* k, const uint16_t* v,
-                      const uint16_t* ck, const uint16_t* cv, const float* cs,
-                      const float* w_g, double* out);
+                      const uint16_t* q, const uint16_t* q_anchor, const uint16_t* k,
+                      const uint16_t* v, const uint16_t* ck, const uint16_t* cv,
+                      const float* cs, const float* w_g, double* out);
 
 /* bf16 (round to nearest, ties to even) of a double, computed exactly. */
 uint16_t orc_round_bf16(double x);

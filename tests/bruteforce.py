@@ -50,9 +50,10 @@ class BruteForce:
                       for i in range(int(bank_n[g]))] for g in range(G)]
         self.pending = [[] for _ in range(G)]
 
-    def step(self, q, k, v, ck, cv, cs, w_g):
-        """q [H][d], k/v/ck/cv [G][d] bf16 bits, cs [G], w_g [H][d] f32.
-        Returns out [H][d] float64."""
+    def step(self, q, k, v, ck, cv, cs, w_g, q_anchor=None):
+        """q [H][d], k/v/ck/cv [G][d] bf16 bits, cs [G], w_g [H][d] f32;
+        q_anchor [H][d] (optional): the query of the anchor read and of the
+        gate, else q.  Returns out [H][d] float64."""
         H, G, d = self.H, self.G, self.d
         hpg = H // G
         t = self.t
@@ -67,14 +68,15 @@ class BruteForce:
             for hh in range(hpg):
                 h = g * hpg + hh
                 qh = _f(q[h])
+                qa = qh if q_anchor is None else _f(q_anchor[h])
                 ol = _softmax_read(qh, Kl, Vl, self.scale)
                 if self.bank[g]:
                     Kb = np.stack([r["k"] for r in self.bank[g]])
                     Vb = np.stack([r["v"] for r in self.bank[g]])
-                    oa = _softmax_read(qh, Kb, Vb, self.scale)
+                    oa = _softmax_read(qa, Kb, Vb, self.scale)
                 else:
                     oa = np.zeros(d)
-                out[h] = ol + np.tanh(qh @ np.asarray(w_g[h], np.float64)) * oa
+                out[h] = ol + np.tanh(qa @ np.asarray(w_g[h], np.float64)) * oa
             self.pending[g].append({"score": float(cs[g]), "pos": t,
                                     "k": _f(ck[g]), "v": _f(cv[g])})
             # positions older than the window are never read again

@@ -245,6 +245,90 @@ def test_planted_key_dominates_local_read():
     np.testing.assert_allclose(out[0, h], f32(st["ring_v"][0, 0, g, slot]), rtol=0, atol=1e-6)
 
 
+# ------------------------------------------------- a separate anchor query
+
+
+@pytest.mark.parametrize("t0,bank_n,steps", [(0, 0, 30), (14, 4, 24), (10, 3, 20)])
+def test_anchor_query_equals_full_history_bruteforce(t0, bank_n, steps):
+    """With q_anchor given, the anchor read and the gate use it and the local
+    read keeps q: the oracle against the full-history model, across admits."""
+    w = tiny(t0=t0, bank_n=bank_n, steps=steps, ring_full=t0 > 0)
+    seed = 17
+    o, st = make_oracle(w, seed)
+    wg = synth.gate_weights(w, seed)
+    bfs = [BruteForce(w.H, w.G, w.d, w.R, w.N, w.C, w.d ** -0.5, t0,
+                      st["ring_k"][0, b], st["ring_v"][0, b], st["bank_k"][0, b],
+                      st["bank_v"][0, b], st["bscore"][0, b], st["bsrc"][0, b],
+                      st["bank_n"][0, b]) for b in range(w.B)]
+    for s in range(steps):
+        x = synth.step_inputs(w, seed, 0, s)
+        qa = synth.anchor_query(w, seed, 0, s)
+        out = o.decode_step(0, x["q"], x["k"], x["v"], x["ck"], x["cv"], x["cs"], wg[0],
+                            q_anchor=qa)
+        if o.pend_n[0] == o.C:
+            o.admit(0)
+        for b in range(w.B):
+            ref = bfs[b].step(x["q"][b], x["k"][b], x["v"][b], x["ck"][b], x["cv"][b],
+                              x["cs"][b], wg[0], q_anchor=qa[b])
+            np.testing.assert_allclose(out[b], ref, rtol=0, atol=1e-12)
+
+
+def test_anchor_query_equal_to_q_is_the_plain_step():
+    """q_anchor == q reproduces the one-query step exactly (same doubles)."""
+    w = synth.WORKLOADS["layer_b1"].with_(B=2, bank_n=700)
+    seed = 18
+    o1, _ = make_oracle(w, seed)
+    o2 = o1.clone()
+    wg = synth.gate_weights(w, seed)
+    for s in range(3):
+        x = synth.step_inputs(w, seed, 0, s)
+        a = o1.decode_step(0, x["q"], x["k"], x["v"], x["ck"], x["cv"], x["cs"], wg[0])
+        b = o2.decode_step(0, x["q"], x["k"], x["v"], x["ck"], x["cv"], x["cs"], wg[0],
+                           q_anchor=x["q"].copy())
+        assert np.array_equal(a, b)
+
+
+def test_anchor_query_leaves_the_local_read_alone():
+    """With the gate weights zero (or an empty bank), the output is the local
+    read alone, whatever q_anchor is."""
+    for bank_n, zero_gate in ((700, True), (0, False)):
+        w = synth.WORKLOADS["layer_b1"].with_(B=1, bank_n=bank_n)
+        seed = 19
+        o1, _ = make_oracle(w, seed)
+        o2 = o1.clone()
+        wg = synth.gate_weights(w, seed)
+        if zero_gate:
+            wg[:] = 0
+        x = synth.step_inputs(w, seed, 0, 0)
+        a = o1.decode_step(0, x["q"], x["k"], x["v"], x["ck"], x["cv"], x["cs"], wg[0])
+        b = o2.decode_step(0, x["q"], x["k"], x["v"], x["ck"], x["cv"], x["cs"], wg[0],
+                           q_anchor=synth.anchor_query(w, seed, 0, 0))
+        assert np.array_equal(a, b)
+
+
+def test_planted_anchor_key_follows_the_anchor_query():
+    """A bank key equal to lambda*q_anchor takes the anchor read to that
+    record's value, and the gate is tanh(q_anchor . w_g): recovered from two
+    runs (gate weights zero, then random) as (out_b - out_a) / gate."""
+    w = synth.WORKLOADS["sharp_b1"]
+    seed = 20
+    o, st = make_oracle(w, seed)
+    x = synth.step_inputs(w, seed, 0, 0)
+    qa = synth.anchor_query(w, seed, 0, 0)
+    h, g = 6, 1
+    slot = 321
+    o.bank_k[0, 0, g, slot] = synth.bf16_bits(8.0 * synth.bf16_to_f32(qa[0, h]))
+    wg = synth.gate_weights(w, seed)
+    wz = np.zeros_like(wg)
+    out_a = o.clone().decode_step(0, x["q"], x["k"], x["v"], x["ck"], x["cv"], x["cs"], wz[0],
+                                  q_anchor=qa)
+    out_b = o.clone().decode_step(0, x["q"], x["k"], x["v"], x["ck"], x["cv"], x["cs"], wg[0],
+                                  q_anchor=qa)
+    gate = np.tanh(f32(qa[0, h]) @ wg[0, h].astype(np.float64))
+    anchor = (out_b[0, h] - out_a[0, h]) / gate
+    np.testing.assert_allclose(anchor, f32(st["bank_v"][0, 0, g, slot]), rtol=0, atol=1e-6)
+
+
 # ----------------------------------------------------------- invariances
 
 
