@@ -279,6 +279,36 @@ def bench_staggered(S, w, sets, wg, outs, steps):
             "tokens_per_s": round(w.B * steps / (ms * 1e-3), 1)}
 
 
+def bench_anchor_query(S, w, sets, wg, outs, steps):
+    """The headline batch through the per-sequence call with a separate
+    anchor query (the anchor read and the gate use q_anchor; here the q of
+    another input set of the pool), every sequence at the same position."""
+    import torch
+    pos = torch.full((w.B,), S.t[0], dtype=torch.int32, device=S.device)
+    e0, e1 = _event(), _event()
+    ev = [(_event(), _event()) for _ in range(steps * w.L)]
+    torch.cuda.synchronize()
+    e0.record()
+    for s in range(steps):
+        for l in range(w.L):
+            x = sets[l][s % len(sets[l])]
+            qa = sets[l][(s + 1) % len(sets[l])]["q"]
+            ev[s * w.L + l][0].record()
+            S.decode_step_at(l, pos, x["q"], x["k"], x["v"], x["ck"], x["cv"], x["cs"], wg[l],
+                             outs[l], q_anchor=qa)
+            ev[s * w.L + l][1].record()
+        pos += 1
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1)
+    launch_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+    return {"workload": f"{w.name} through rma_decode_step_at with a separate anchor query",
+            "steps": steps, "ms_per_step": round(ms / steps, 4),
+            "tokens_per_s": round(w.B * steps / (ms * 1e-3), 1),
+            "decode_launch_us": round(launch_ms * 1e3, 1),
+            "GBps": round(w.B * w.G * (UNIT_BYTES + 2048) / (launch_ms * 1e-3) / 1e9, 1)}
+
+
 def cpu_baseline(S, w, sets, wg, sample_b: int, seed: int, steps: int = 8):
     """The oracle, timed on the host cores on a bounded sample: `sample_b`
     sequences of the same state, `steps` tokens through all layers."""
@@ -353,6 +383,8 @@ def main():
                     help="batch-1 token steps timed eager and as graph replays (0: skip)")
     ap.add_argument("--staggered-steps", type=int, default=256,
                     help="steps of the per-sequence-position run at the headline batch (0: skip)")
+    ap.add_argument("--anchor-steps", type=int, default=64,
+                    help="steps with a separate anchor query at the headline batch (0: skip)")
     ap.add_argument("--prefill-blocks", type=int, default=4,
                     help="256-token blocks timed per prefill batch size (0: skip)")
     ap.add_argument("--calibration-copy-gib", type=int, default=0,
@@ -482,6 +514,11 @@ def main():
         say(f"[bench] per-sequence positions, {args.staggered_steps} steps")
         result["staggered"] = bench_staggered(S, w, sets, wg, outs, args.staggered_steps)
         say(f"[bench] staggered: {result['staggered']['tokens_per_s']:,.0f} tok/s")
+    if args.anchor_steps > 0:
+        say(f"[bench] separate anchor query, {args.anchor_steps} steps")
+        result["anchor_query"] = bench_anchor_query(S, w, sets, wg, outs, args.anchor_steps)
+        say(f"[bench] anchor query: {result['anchor_query']['tokens_per_s']:,.0f} tok/s, decode "
+            f"launch {result['anchor_query']['decode_launch_us']} us")
     del S, sets, outs
     torch.cuda.empty_cache()
     if args.latency_steps > 0:

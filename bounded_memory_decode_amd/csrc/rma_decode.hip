@@ -147,7 +147,8 @@ __device__ __forceinline__ Seg make_seg(const DecodeArgs& a, int u, bool ring, i
     sg.K4 = reinterpret_cast<const uint4*>(a.bank_k + (size_t)u * a.N * kD);
     sg.V4 = reinterpret_cast<const uint4*>(a.bank_v + (size_t)u * a.N * kD);
   }
-  sg.q4 = reinterpret_cast<const uint4*>(a.q + (size_t)b * a.q_bs + (size_t)g * kHpg * kD);
+  const uint16_t* qsrc = (ring || a.qa == nullptr) ? a.q : a.qa;  // the anchor read's query
+  sg.q4 = reinterpret_cast<const uint4*>(qsrc + (size_t)b * a.q_bs + (size_t)g * kHpg * kD);
   const int ntiles = (sg.count + kTile - 1) / kTile;
   int t1 = t0 + tiles;
   t1 = t1 < ntiles ? t1 : ntiles;
@@ -186,19 +187,21 @@ struct FinOps {
 // Sources of the two auxiliary loads issued when a wave moves to segment
 // `nsub` of the next item: the segment's query rows, except that a
 // whole-unit wave entering the bank segment of the unit it is on (`item`)
-// keeps its query rows and fetches that unit's finish operands instead.
+// keeps its query rows and fetches that unit's finish operands instead
+// (with a separate anchor query, kQA, it fetches the anchor query rows and
+// the finish loads its own operands).
 struct AuxPtrs {
   const uint4* p0;
   const uint4* p1;
 };
 
-template <bool kWhole>
+template <bool kWhole, bool kQA>
 __device__ __forceinline__ AuxPtrs aux_ptrs(const DecodeArgs& a, const Seg& nxt, int nsub,
                                             int item, int lane) {
   AuxPtrs ap;
   ap.p0 = nxt.q4 + 2 * lane;
   ap.p1 = nxt.q4 + 2 * lane + 1;
-  if (kWhole) {
+  if (kWhole && !kQA) {
     const int b = item / a.G, g = item - b * a.G;
     const size_t kvo = (size_t)b * a.kv_bs + (size_t)g * kD;
     const int c32 = lane & 31;
@@ -216,15 +219,21 @@ __device__ __forceinline__ AuxPtrs aux_ptrs(const DecodeArgs& a, const Seg& nxt,
 // out = o_local + tanh(q . w_g) * o_anchor, the ring write and the pending
 // append.  Every read of the unit's ring by this launch is already done:
 // only this wave reads it.
+template <bool kQA>
 __device__ __forceinline__ void finish_unit(const DecodeArgs& a, int u, int lane,
-                                            const uint4* q_w, const float* o_r,
-                                            const float* mr, const float* lr,
-                                            const float* lb, float accb[kHpg][8],
-                                            const FinOps& f) {
+                                            const uint4* q_w, const uint4* qa_w,
+                                            const float* o_r, const float* mr,
+                                            const float* lr, const float* lb,
+                                            float accb[kHpg][8], FinOps f) {
   const int b = u / a.G, g = u - b * a.G;
   const TokPos tp = tok_pos(a, b);
   if (!tp.live) return;
   const int c32 = lane & 31;
+  if (kQA) {  // operands not delivered by the pipeline in this mode
+    const size_t kvo = (size_t)b * a.kv_bs + (size_t)g * kD;
+    f.k_or_v = reinterpret_cast<const uint4*>((lane < 32 ? a.k : a.v) + kvo)[c32];
+    f.ck_or_cv = reinterpret_cast<const uint4*>((lane < 32 ? a.ck : a.cv) + kvo)[c32];
+  }
   // the current K (lanes 0-31, 8 dims each) and V (lanes 32-63)
   const uint4 kv = f.k_or_v;
   // q . k_t over 8 dims in lanes 0-31; q . w_g over 4 dims in all lanes
@@ -241,7 +250,7 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs& a, int u, int lane
     ds = fmaf(bf_lo(q8.w), bf_lo(kv.w), ds);
     ds = fmaf(bf_hi(q8.w), bf_hi(kv.w), ds);
     ds = lane < 32 ? ds : 0.f;
-    const uint2 q2 = reinterpret_cast<const uint2*>(q_w + h * kChunks)[lane];
+    const uint2 q2 = reinterpret_cast<const uint2*>((kQA ? qa_w : q_w) + h * kChunks)[lane];
     const float4 w4 = reinterpret_cast<const float4*>(a.w_g + (size_t)(g * kHpg + h) * kD)[lane];
     float dz = bf_lo(q2.x) * w4.x;
     dz = fmaf(bf_hi(q2.x), w4.y, dz);
@@ -314,7 +323,7 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs& a, int u, int lane
 // for V(i) and P.V(i) never waits for K(i+1): a wave keeps ~64 16-byte
 // loads in flight across tile, segment and item boundaries.  No
 // workgroup barrier: each wave owns its LDS slices.
-template <bool kWhole>
+template <bool kWhole, bool kQA>
 __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a, int items) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -324,6 +333,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a, int item
   int sub = 0;
 
   __shared__ uint4 q_s[kWaves][kHpg * kChunks];  // each wave's 4 query rows
+  __shared__ uint4 qa_s[kQA ? kWaves : 1][kHpg * kChunks];  // anchor query rows (kQA)
   __shared__ float4 p_s[kWaves][kTile];          // per-key probabilities
   __shared__ float or_s[kWhole ? kWaves : 1][kHpg * kD];  // ring result
 
@@ -352,10 +362,15 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a, int item
     if (!kWhole || sub == 0) {
       q_s[wave][2 * lane] = qn0;
       q_s[wave][2 * lane + 1] = qn1;
+    } else if (kQA) {
+      qa_s[kQA ? wave : 0][2 * lane] = qn0;
+      qa_s[kQA ? wave : 0][2 * lane + 1] = qn1;
     } else {
       fin.k_or_v = qn0;
       fin.ck_or_cv = qn1;
     }
+    // query rows of this segment's scores
+    const uint4* qrows = (kWhole && kQA && sub == 1) ? qa_s[kQA ? wave : 0] : q_s[wave];
     __builtin_amdgcn_wave_barrier();
 
     int nitem = item, nsub = sub + 1;
@@ -393,7 +408,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a, int item
         const uint4 kv = kr[c];
 #pragma unroll
         for (int h = 0; h < kHpg; ++h) {
-          const uint4 qv = q_s[wave][h * kChunks + c];
+          const uint4 qv = qrows[h * kChunks + c];
           s[h] = dot2(qv.x, kv.x, s[h]);
           s[h] = dot2(qv.y, kv.y, s[h]);
           s[h] = dot2(qv.z, kv.z, s[h]);
@@ -433,7 +448,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a, int item
         // the ring segment of a unit hands over to its bank segment (same
         // query rows), the operands of the unit's finish
         const uint4* vrow_p = cur.V4 + voff;
-        const AuxPtrs ap = aux_ptrs<kWhole>(a, nxt, nsub, item, lane);
+        const AuxPtrs ap = aux_ptrs<kWhole, kQA>(a, nxt, nsub, item, lane);
         qn0 = *(go_next ? ap.p0 : vrow_p);
         qn1 = *(go_next ? ap.p1 : vrow_p);
         const int ktile = more ? tile + 1 : nxt.ta;
@@ -511,13 +526,14 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a, int item
       }
       __builtin_amdgcn_wave_barrier();
     } else {
-      finish_unit(a, item, lane, q_s[wave], or_s[kWhole ? wave : 0], mr, lr, l, acc, fin);
+      finish_unit<kQA>(a, item, lane, q_s[wave], qa_s[kQA ? wave : 0], or_s[kWhole ? wave : 0],
+                       mr, lr, l, acc, fin);
       __builtin_amdgcn_wave_barrier();
     }
 
     if (!has_next) break;
     if (cur.ta == cur.tb) {  // empty segment: nothing was prefetched for nxt
-      const AuxPtrs ap = aux_ptrs<kWhole>(a, nxt, nsub, item, lane);
+      const AuxPtrs ap = aux_ptrs<kWhole, kQA>(a, nxt, nsub, item, lane);
       qn0 = *ap.p0;
       qn1 = *ap.p1;
       load_k(nxt, nxt.ta);
@@ -564,19 +580,23 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   }
 
   const uint16_t* qb = a.q + (size_t)b * a.q_bs + (size_t)g * kHpg * kD;
+  const uint16_t* qab = (a.qa ? a.qa : a.q) + (size_t)b * a.q_bs + (size_t)g * kHpg * kD;
   const size_t kvo = (size_t)b * a.kv_bs + (size_t)g * kD;
-  float qf[kHpg];
+  float qf[kHpg], qaf[kHpg];
 #pragma unroll
-  for (int h = 0; h < kHpg; ++h) qf[h] = bf1(qb[h * kD + tid]);
+  for (int h = 0; h < kHpg; ++h) {
+    qf[h] = bf1(qb[h * kD + tid]);
+    qaf[h] = bf1(qab[h * kD + tid]);
+  }
   const float kf = bf1(a.k[kvo + tid]);
   const float vf = bf1(a.v[kvo + tid]);
 
-  // q.k_t (current-token score) and q.w_g (gate argument) for the 4 heads
+  // q.k_t (current-token score) and qa.w_g (gate argument) for the 4 heads
   float dts[8];
 #pragma unroll
   for (int h = 0; h < kHpg; ++h) {
     dts[h] = wave_sum(qf[h] * kf);
-    dts[kHpg + h] = wave_sum(qf[h] * a.w_g[(size_t)(g * kHpg + h) * kD + tid]);
+    dts[kHpg + h] = wave_sum(qaf[h] * a.w_g[(size_t)(g * kHpg + h) * kD + tid]);
   }
   if (lane == 0) {
 #pragma unroll
@@ -683,7 +703,7 @@ __global__ void seq_bank_n_kernel(int32_t* bank_n, int L, int B, int G, int firs
 
 // Workgroups of a kernel that are resident at once on the current device
 // (CUs x workgroups per CU), computed once per device.
-template <bool kWhole>
+template <bool kWhole, bool kQA>
 int resident_workgroups() {
   static int cached[64] = {0};
   int dev = 0;
@@ -692,8 +712,8 @@ int resident_workgroups() {
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_attn_kernel<kWhole>, 256,
-                                                     0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_attn_kernel<kWhole, kQA>,
+                                                     256, 0) != hipSuccess ||
         per_cu < 1)
       per_cu = 1;
     cached[dev] = cus * per_cu;
@@ -706,13 +726,17 @@ int resident_workgroups() {
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   // Whole-unit launch when there is at least one unit per resident wave and
   // the last round of units leaves at most 1/8 of the waves idle.
-  const int res_whole = resident_workgroups<true>();
+  const bool qa = a.qa != nullptr;
+  const int res_whole = qa ? resident_workgroups<true, true>() : resident_workgroups<true, false>();
   const int waves = res_whole * kWaves;
   const int rounds = (a.units + waves - 1) / waves;
   if (a.units >= waves && (int64_t)(rounds * waves - a.units) * 8 <= a.units) {
     int grid = (a.units + kWaves - 1) / kWaves;
     if (grid > res_whole) grid = res_whole;
-    hipLaunchKernelGGL(decode_attn_kernel<true>, dim3(grid), dim3(256), 0, s, a, a.units);
+    if (qa)
+      hipLaunchKernelGGL((decode_attn_kernel<true, true>), dim3(grid), dim3(256), 0, s, a, a.units);
+    else
+      hipLaunchKernelGGL((decode_attn_kernel<true, false>), dim3(grid), dim3(256), 0, s, a, a.units);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.pos == nullptr) return e;
     // per-sequence positions: admit the units whose block this token ends
@@ -739,9 +763,9 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   const int S = a.splits_ring + a.splits_bank;
   const int items = a.units * S;
   int grid = (items + kWaves - 1) / kWaves;
-  const int res = resident_workgroups<false>();
+  const int res = resident_workgroups<false, false>();
   if (grid > res) grid = res;
-  hipLaunchKernelGGL(decode_attn_kernel<false>, dim3(grid), dim3(256), 0, s, a, items);
+  hipLaunchKernelGGL((decode_attn_kernel<false, false>), dim3(grid), dim3(256), 0, s, a, items);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_combine_kernel, dim3(a.units), dim3(256), 0, s, a);

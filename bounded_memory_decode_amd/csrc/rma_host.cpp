@@ -128,6 +128,7 @@ rma::DecodeArgs decode_args(const rma_state* st, int32_t layer, int64_t t, const
   const Splits sp = choose_splits(&c, B);
   rma::DecodeArgs a;
   a.q = static_cast<const uint16_t*>(q);
+  a.qa = nullptr;
   a.k = static_cast<const uint16_t*>(k);
   a.v = static_cast<const uint16_t*>(v);
   a.ck = static_cast<const uint16_t*>(ck);
@@ -179,6 +180,7 @@ rma::PrefillArgs prefill_args(const rma_state* st, int32_t layer, int32_t n_toke
   const uint64_t unit0 = (uint64_t)layer * B * G;
   rma::PrefillArgs a;
   a.q = static_cast<const uint16_t*>(q);
+  a.qa = nullptr;
   a.k = static_cast<const uint16_t*>(k);
   a.v = static_cast<const uint16_t*>(v);
   a.ck = static_cast<const uint16_t*>(ck);
@@ -386,36 +388,41 @@ int rma_admit(rma_state* st, int32_t layer, void* stream) {
 }
 
 int rma_decode_step_at(rma_state* st, int32_t layer, const int32_t* pos, const void* q,
-                       const void* k, const void* v, const void* cand_k, const void* cand_v,
-                       const float* cand_score, const float* w_g, void* out, void* stream) {
+                       const void* q_anchor, const void* k, const void* v, const void* cand_k,
+                       const void* cand_v, const float* cand_score, const float* w_g, void* out,
+                       void* stream) {
   int rc = check_state(st, layer);
   if (rc != RMA_OK) return rc;
   if (!aligned4(pos) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(cand_k) ||
-      !aligned16(cand_v) || !cand_score || !w_g || !aligned16(out))
+      !aligned16(cand_v) || !cand_score || !w_g || !aligned16(out) ||
+      (q_anchor && !aligned16(q_anchor)))
     return RMA_E_ARG;
   const rma_config& c = st->cfg;
   const int64_t H = c.q_heads, G = c.kv_groups;
   rma::DecodeArgs a = decode_args(st, layer, 0, q, k, v, cand_k, cand_v, cand_score, w_g, out,
                                   H * kD, G * kD, G, H * kD);
   a.pos = pos;
+  a.qa = static_cast<const uint16_t*>(q_anchor);
   const hipError_t e = rma::launch_decode(a, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(st, e);
   return RMA_OK;
 }
 
 int rma_prefill_block_at(rma_state* st, int32_t layer, int32_t n_tokens, const int32_t* pos,
-                         const void* q, const void* k, const void* v, const void* cand_k,
-                         const void* cand_v, const float* cand_score, const float* w_g,
-                         void* out, void* stream) {
+                         const void* q, const void* q_anchor, const void* k, const void* v,
+                         const void* cand_k, const void* cand_v, const float* cand_score,
+                         const float* w_g, void* out, void* stream) {
   int rc = check_state(st, layer);
   if (rc != RMA_OK) return rc;
   const rma_config& c = st->cfg;
   if (n_tokens < 1 || n_tokens > c.commit) return RMA_E_ARG;
   if (!aligned4(pos) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(cand_k) ||
-      !aligned16(cand_v) || !cand_score || !w_g || !aligned16(out))
+      !aligned16(cand_v) || !cand_score || !w_g || !aligned16(out) ||
+      (q_anchor && !aligned16(q_anchor)))
     return RMA_E_ARG;
-  const rma::PrefillArgs a = prefill_args(st, layer, n_tokens, 0, pos, q, k, v, cand_k, cand_v,
-                                          cand_score, w_g, out);
+  rma::PrefillArgs a = prefill_args(st, layer, n_tokens, 0, pos, q, k, v, cand_k, cand_v,
+                                    cand_score, w_g, out);
+  a.qa = static_cast<const uint16_t*>(q_anchor);
   const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = rma::launch_prefill(a, s);
   // only a full block can complete one (its start is a multiple of C)

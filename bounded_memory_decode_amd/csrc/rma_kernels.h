@@ -26,6 +26,7 @@ __host__ __device__ inline size_t k_chunk_index(int slot, int c, int slots) {
 // One decode token of one layer.
 struct DecodeArgs {
   const uint16_t* q;       // [B][H][D]
+  const uint16_t* qa;      // [B][H][D] query of the anchor read and the gate, or null: q
   const uint16_t* k;       // [B][G][D]
   const uint16_t* v;
   const uint16_t* ck;
@@ -68,6 +69,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 // A chunked-prefill block of one layer.
 struct PrefillArgs {
   const uint16_t* q;       // [B][n][H][D]
+  const uint16_t* qa;      // [B][n][H][D] query of the anchor read and the gate, or null: q
   const uint16_t* k;       // [B][n][G][D]
   const uint16_t* v;
   const uint16_t* ck;

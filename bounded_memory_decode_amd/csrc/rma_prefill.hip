@@ -137,15 +137,17 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_kernel(PrefillArgs a
   __shared__ __attribute__((aligned(16))) unsigned char k_lds[2][kPT * kRowK];
   __shared__ __attribute__((aligned(16))) unsigned char v_lds[2][kPT * kRowV];
 
-  // Q^T as B-operands (column = query): 8 k-steps of 32 dims
+  // Q^T as B-operands (column = query): 8 k-steps of 32 dims; with a
+  // separate anchor query (a.qa) the bank tiles and the gate use its rows
   uint4 qa[8];
-  {
+  auto load_q = [&](const uint16_t* src) {
     const bool ok = q_tok < n;
     const uint4* qrow = reinterpret_cast<const uint4*>(
-        a.q + (((size_t)b * n + (ok ? q_tok : 0)) * a.H + g * kHpg + q_head) * kD);
+        src + (((size_t)b * n + (ok ? q_tok : 0)) * a.H + g * kHpg + q_head) * kD);
 #pragma unroll
     for (int st = 0; st < 8; ++st) qa[st] = ok ? qrow[st * 4 + lg] : make_uint4(0, 0, 0, 0);
-  }
+  };
+  load_q(a.q);
 
   const int R = a.R;
   int64_t P = a.P;
@@ -275,6 +277,7 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_kernel(PrefillArgs a
     int seg, ti;
     seg_of(t, seg, ti);
     const int cnt = seg_count(seg);
+    if (a.qa != nullptr && t == t_loc) load_q(a.qa);  // first bank tile
     // prefetch of tile t + 2, without branches: past the last tile, reload
     // the last one
     const int tn = t + 2 < t_all ? t + 2 : t_all - 1;
@@ -414,7 +417,9 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_kernel(PrefillArgs a
   // anchor read (zero for an empty bank)
   const float inv_b = (t_bank > 0 && l_run > 0.f) ? 1.f / l_run : 0.f;
 
-  // gate argument q . w_g of this lane's query, summed over the 4 k-groups
+  // gate argument qa . w_g of this lane's query (qa = the anchor query if
+  // given, else q), summed over the 4 k-groups
+  if (a.qa != nullptr && t_bank == 0) load_q(a.qa);
   float z = 0.f;
   {
     const float* wrow = a.w_g + (size_t)(g * kHpg + q_head) * kD;

@@ -86,10 +86,10 @@ def lib() -> ctypes.CDLL:
         L.rma_prefill_block.restype = ctypes.c_int
         L.rma_admit.argtypes = [ctypes.POINTER(_State), ctypes.c_int32, _P]
         L.rma_admit.restype = ctypes.c_int
-        L.rma_decode_step_at.argtypes = [ctypes.POINTER(_State), ctypes.c_int32] + [_P] * 10
+        L.rma_decode_step_at.argtypes = [ctypes.POINTER(_State), ctypes.c_int32] + [_P] * 11
         L.rma_decode_step_at.restype = ctypes.c_int
         L.rma_prefill_block_at.argtypes = [ctypes.POINTER(_State), ctypes.c_int32,
-                                           ctypes.c_int32] + [_P] * 10
+                                           ctypes.c_int32] + [_P] * 11
         L.rma_prefill_block_at.restype = ctypes.c_int
         L.rma_seq_reset.argtypes = [ctypes.POINTER(_State), ctypes.c_int32, ctypes.c_int32,
                                     ctypes.c_int32, _P]
@@ -290,26 +290,36 @@ class State:
         return out
 
     def decode_step_at(self, layer: int, pos: torch.Tensor, q, k, v, cand_k, cand_v, cand_score,
-                       w_g, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                       w_g, out: Optional[torch.Tensor] = None,
+                       q_anchor: Optional[torch.Tensor] = None) -> torch.Tensor:
         """Decode with per-sequence positions: `pos` is a device int32
         tensor [batch] (negative: sequence left out, its `out` rows are not
-        written).  Admits the blocks the step completes.  The host counters
-        (t, pend_n, bank_n) are not used or updated."""
+        written).  Admits the blocks the step completes.  `q_anchor` (shape
+        of q), if given, is the query of the anchor read and the gate.  The
+        host counters (t, pend_n, bank_n) are not used or updated."""
         out, ptrs = self._decode_ptrs(q, k, v, cand_k, cand_v, cand_score, w_g, out)
         p = _dev(pos, torch.int32, (self.batch,), "pos", self.device)
-        _check(lib().rma_decode_step_at(ctypes.byref(self._st), int(layer), p, *ptrs,
-                                        _stream_handle(self.device)), "rma_decode_step_at")
+        qa = None if q_anchor is None else _dev(q_anchor, torch.bfloat16, tuple(q.shape),
+                                                "q_anchor", self.device)
+        _check(lib().rma_decode_step_at(ctypes.byref(self._st), int(layer), p, ptrs[0], qa,
+                                        *ptrs[1:], _stream_handle(self.device)),
+               "rma_decode_step_at")
         return out
 
     def prefill_block_at(self, layer: int, pos: torch.Tensor, q, k, v, cand_k, cand_v,
-                         cand_score, w_g, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                         cand_score, w_g, out: Optional[torch.Tensor] = None,
+                         q_anchor: Optional[torch.Tensor] = None) -> torch.Tensor:
         """Prefill block with per-sequence block starts in `pos` (device
         int32 [batch]; sequences whose entry is negative or not a multiple of
-        the commit interval are left out).  A full block is admitted."""
+        the commit interval are left out).  A full block is admitted.
+        `q_anchor` as in decode_step_at, with the token axis."""
         n, out, ptrs = self._prefill_ptrs(q, k, v, cand_k, cand_v, cand_score, w_g, out)
         p = _dev(pos, torch.int32, (self.batch,), "pos", self.device)
-        _check(lib().rma_prefill_block_at(ctypes.byref(self._st), int(layer), int(n), p, *ptrs,
-                                          _stream_handle(self.device)), "rma_prefill_block_at")
+        qa = None if q_anchor is None else _dev(q_anchor, torch.bfloat16, tuple(q.shape),
+                                                "q_anchor", self.device)
+        _check(lib().rma_prefill_block_at(ctypes.byref(self._st), int(layer), int(n), p,
+                                          ptrs[0], qa, *ptrs[1:], _stream_handle(self.device)),
+               "rma_prefill_block_at")
         return out
 
     def seq_reset(self, first: int, count: int = 1, bank_n: int = 0):

@@ -222,21 +222,31 @@ int rma_admit(rma_state* st, int32_t layer, void* stream);
 
 /* Decode one token for every sequence b with pos[b] >= 0, at position
  * pos[b]; tensors as in rma_decode_step.  Then admits the blocks these
- * tokens complete.  Returns RMA_OK, RMA_E_ARG or RMA_E_HIP. */
+ * tokens complete.
+ *   q_anchor  [batch][q_heads][head_dim] bf16, or NULL.  A separate query
+ *             for the anchor read and the gate: o_anchor attends with
+ *             q_anchor[h] and the gate is tanh(q_anchor[h] . w_g[h]); the
+ *             local read keeps q.  NULL: q serves both reads, as in
+ *             rma_decode_step.  (Reading of the model card's "separate RMA
+ *             modules" and query-dependent read, section "How Rock Memory
+ *             Anchors work"; the pages fix neither the query's source nor
+ *             the gate's input.)
+ * Returns RMA_OK, RMA_E_ARG or RMA_E_HIP. */
 int rma_decode_step_at(rma_state* st, int32_t layer, const int32_t* pos, const void* q,
-                       const void* k, const void* v, const void* cand_k, const void* cand_v,
-                       const float* cand_score, const float* w_g, void* out,
+                       const void* q_anchor, const void* k, const void* v, const void* cand_k,
+                       const void* cand_v, const float* cand_score, const float* w_g, void* out,
                        void* stream);
 
 /* A prefill block of n_tokens (1 .. commit) for every sequence b whose
  * pos[b] is >= 0 and a multiple of commit (the block's first position);
- * other sequences are left out.  Tensors as in rma_prefill_block.  A full
- * block (n_tokens == commit) is admitted by the same call.  Returns
- * RMA_OK, RMA_E_ARG or RMA_E_HIP. */
+ * other sequences are left out.  Tensors as in rma_prefill_block;
+ * q_anchor [batch][n][q_heads][head_dim] or NULL, as in
+ * rma_decode_step_at.  A full block (n_tokens == commit) is admitted by
+ * the same call.  Returns RMA_OK, RMA_E_ARG or RMA_E_HIP. */
 int rma_prefill_block_at(rma_state* st, int32_t layer, int32_t n_tokens, const int32_t* pos,
-                         const void* q, const void* k, const void* v, const void* cand_k,
-                         const void* cand_v, const float* cand_score, const float* w_g,
-                         void* out, void* stream);
+                         const void* q, const void* q_anchor, const void* k, const void* v,
+                         const void* cand_k, const void* cand_v, const float* cand_score,
+                         const float* w_g, void* out, void* stream);
 
 /* Give sequences first .. first+count-1 (every layer and group) a bank of
  * `bank_n` committed anchors (0 for a new sequence in a reused batch slot;

@@ -207,13 +207,17 @@ def test_positioned_calls_validation_on_host():
     reset range on the host; nothing is enqueued on failure."""
     L = rma.lib()
     st = _fake_state()
-    P = [FAKE] * 9
+    P = [FAKE] * 10  # q, q_anchor, k, v, cand_k, cand_v, cand_score, w_g, out, stream
     assert L.rma_decode_step_at(ctypes.byref(st), 0, None, *P) == rma.RMA_E_ARG
     assert L.rma_decode_step_at(ctypes.byref(st), 0, FAKE + 2, *P) == rma.RMA_E_ARG
     assert L.rma_decode_step_at(ctypes.byref(st), 8, FAKE, *P) == rma.RMA_E_ARG
     bad = list(P)
-    bad[1] = FAKE + 8  # misaligned k
+    bad[2] = FAKE + 8  # misaligned k
     assert L.rma_decode_step_at(ctypes.byref(st), 0, FAKE, *bad) == rma.RMA_E_ARG
+    bad = list(P)
+    bad[1] = FAKE + 8  # misaligned q_anchor
+    assert L.rma_decode_step_at(ctypes.byref(st), 0, FAKE, *bad) == rma.RMA_E_ARG
+    assert L.rma_prefill_block_at(ctypes.byref(st), 0, 16, FAKE, *bad) == rma.RMA_E_ARG
     assert L.rma_decode_step_at(None, 0, FAKE, *P) == rma.RMA_E_ARG
     assert L.rma_prefill_block_at(ctypes.byref(st), 0, 0, FAKE, *P) == rma.RMA_E_ARG
     assert L.rma_prefill_block_at(ctypes.byref(st), 0, 257, FAKE, *P) == rma.RMA_E_ARG
