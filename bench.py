@@ -7,7 +7,11 @@ ring write and the pending append; plus, every 256 tokens, the admit of
 all layers.  Workload: 512 sequences, state pre-filled as after a 32K
 prompt (ring and bank full), synthetic N(0,1)/16 bf16 inputs from a
 device-resident pool of 16 input sets per layer (the pool changes none of
-the state traffic).  Prints ONE JSON line.
+the state traffic).  Prints ONE JSON line: the headline decode figure with
+its HBM roofline and the CPU oracle beside it, plus the admit round, the
+same batch with per-sequence positions and with a separate anchor query,
+batch-1 token latency (eager and HIP-graph replay) and the MFMA prefill
+block at batch 1 and 8.
 
     python bench.py [--gpus 1] [--steps 1024] [--warmup 16]
 """

@@ -9,13 +9,19 @@
 //   * split (small batch): reads are cut into parts of 64-key tiles spread
 //     over all waves; partials go to scratch and a combine kernel finishes
 //     the token.
+// Positions come from the lockstep arguments or, per sequence, from a
+// device array (TokPos); with per-sequence positions a completed block is
+// admitted right after the token (in the combine workgroup, or by an admit
+// launch after the whole-unit kernel).  kQA instantiates the whole-unit
+// kernel for a separate anchor query (the anchor read and the gate use it).
 //
 // Semantics: EdgeRock model card (ModelScope), "How Rock Memory Anchors
 // work" (local window of 1,024 positions, committed-bank reads, signed gate)
 // and the persistent-history table note (ring of 1,023 preceding positions
 // plus the current token); ai-primer "EdgeRock-4B fixes its attention KV
 // cache at 72 MiB", three-operation list (Write, Retrieve).  Gate reading:
-// out = o_local + tanh(q . w_g) * o_anchor.
+// out = o_local + tanh(qa . w_g) * o_anchor, qa = the anchor query if one
+// is given, else q.
 //
 // Data layout (owned by this library, see include/rma.h): K planes are
 // chunk-major (16-byte chunks of 8 dims), so that a wave loading chunk c of

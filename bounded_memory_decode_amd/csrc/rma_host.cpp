@@ -1,8 +1,9 @@
 // Host side of librma.so: the C ABI declared in include/rma.h.
 //
-// Everything here is argument checking, state bookkeeping (the lockstep
-// position, pending and bank counters of every layer are mirrored on the
-// host) and kernel launches.  No arithmetic of the layer runs on the host.
+// Everything here is argument checking, state bookkeeping (for the
+// lockstep calls the position, pending and bank counters of every layer
+// are mirrored on the host; the per-sequence calls keep no host state) and
+// kernel launches.  No arithmetic of the layer runs on the host.
 #include "rma.h"
 
 #include <cmath>

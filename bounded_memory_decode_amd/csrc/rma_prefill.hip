@@ -47,13 +47,6 @@ constexpr int kPT = 32;          // keys per tile
 constexpr int kRowK = 528;
 constexpr int kRowV = 544;
 
-__device__ __forceinline__ uint16_t to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
-}
-
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
 typedef float f32x2_t __attribute__((ext_vector_type(2)));

@@ -46,8 +46,11 @@
  *   - The library allocates no memory.  The caller owns the rma_state
  *     struct and one device buffer holding the whole state (its size from
  *     rma_state_bytes).
- *   - Batches move in lockstep: all sequences of a layer share the
- *     position t, which the host mirrors in rma_state.
+ *   - The lockstep calls (rma_decode_step, rma_prefill_block, rma_admit)
+ *     move a batch together: all sequences of a layer share the position
+ *     t, which the host mirrors in rma_state.  The per-sequence calls
+ *     (the _at calls below) take each sequence's position from device
+ *     memory instead.
  *   - Kernels support head_dim 256 and 4 query heads per KV group (the
  *     EdgeRock geometry); other shapes return RMA_E_UNSUPPORTED.
  */
