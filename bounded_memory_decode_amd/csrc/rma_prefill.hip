@@ -89,6 +89,10 @@ __device__ __forceinline__ float sum32(float x) {
   return __uint_as_float(r.x) + __uint_as_float(r.y);
 }
 
+// s_waitcnt immediate (gfx9 encoding): vmcnt 0, expcnt and lgkmcnt left
+// at their maxima (no wait).
+constexpr int kWaitVmcnt0 = 0x0F70;
+
 // Key source of one segment (ring, block, bank).
 enum : int { kSegRing = 0, kSegBlock = 1, kSegBank = 2 };
 
@@ -262,20 +266,32 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_kernel(PrefillArgs a
   stage_store(0, 0, stage_load(0, 0));
   if (kParts == 2) stage_store(0, 1, stage_load(0, 1));
   const int t1 = 1 < t_all ? 1 : 0;
-  Stage pf0 = stage_load(t1, 0);
-  Stage pf1 = kParts == 2 ? stage_load(t1, 1) : pf0;
+  Stage x0 = stage_load(t1, 0), x1 = x0, y0 = x0, y1 = x0;
+  if (kParts == 2) x1 = stage_load(t1, 1);
   __syncthreads();
 
-  for (int t = 0; t < t_all; ++t) {
+  // One tile: LDS buffer t & 1 holds tile t, registers `cur` hold tile
+  // t + 1, and tile t + 2 is loaded into `nxt`.  Two register sets that
+  // swap roles from one tile to the next (the loop below takes two tiles
+  // per turn) mean no register copy of loads in flight, which would make
+  // the compiler wait for them at the end of every tile.
+  auto tile_step = [&](int t, const Stage& cur0, const Stage& cur1, Stage& nxt0, Stage& nxt1)
+                       __attribute__((always_inline)) {
     int seg, ti;
     seg_of(t, seg, ti);
     const int cnt = seg_count(seg);
-    if (a.qa != nullptr && t == t_loc) load_q(a.qa);  // first bank tile
+    if (a.qa != nullptr && t == t_loc) {  // first bank tile: the anchor query
+      load_q(a.qa);
+      // wait for these loads here, on this one tile: left pending, they
+      // make the compiler guard the scores of every tile with a wait on
+      // all outstanding loads, the prefetches included
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    }
     // prefetch of tile t + 2, without branches: past the last tile, reload
     // the last one
     const int tn = t + 2 < t_all ? t + 2 : t_all - 1;
-    const Stage next0 = stage_load(tn, 0);
-    const Stage next1 = kParts == 2 ? stage_load(tn, 1) : next0;
+    nxt0 = stage_load(tn, 0);
+    if (kParts == 2) nxt1 = stage_load(tn, 1);
 
     const unsigned char* kl = k_lds[t & 1];
     const unsigned char* vl = v_lds[t & 1];
@@ -395,12 +411,16 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_kernel(PrefillArgs a
       for (int dt = 0; dt < 16; ++dt) oloc[dt] = o[dt] * inv;
       reset();
     }
-    stage_store((t + 1) & 1, 0, pf0);  // tile t + 1
-    if (kParts == 2) stage_store((t + 1) & 1, 1, pf1);
-    pf0 = next0;
-    pf1 = next1;
+    stage_store((t + 1) & 1, 0, cur0);  // tile t + 1
+    if (kParts == 2) stage_store((t + 1) & 1, 1, cur1);
     __syncthreads();
+  };
+  int t = 0;
+  for (; t + 1 < t_all; t += 2) {
+    tile_step(t, x0, x1, y0, y1);
+    tile_step(t + 1, y0, y1, x0, x1);
   }
+  if (t < t_all) tile_step(t, x0, x1, y0, y1);
   if (t_loc == 0) {
     // no visible local key is impossible for a real token (it sees itself)
 #pragma unroll
