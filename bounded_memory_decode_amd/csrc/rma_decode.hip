@@ -609,45 +609,58 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
     for (int j = 0; j < 8; ++j) red[j][wave] = dts[j];
   }
   __syncthreads();
-#pragma unroll
-  for (int j = 0; j < 8; ++j) dts[j] = (red[j][0] + red[j][1]) + (red[j][2] + red[j][3]);
 
+  // Merge weights, once per (head, part) rather than per dimension: wave 0,
+  // lane = 16 h + r, takes ring part r and bank part r of head h; the
+  // 16-lane groups reduce the maxima and sums.  wt[h][sp] is the weight of
+  // part sp (launch order: ring parts, then bank parts, then zeros), that
+  // of a bank part with the gate folded in, so that out = sum_sp wt * o_sp
+  // + wt[h][2 kMaxSplits] * v_t.
+  __shared__ float wt[kHpg][2 * kMaxSplits + 4];
   const int n = scalar_load(a.bank_n + u);
+  if (wave == 0) {
+    const int h = lane >> 4, r = lane & 15;
+    const float dk = (red[h][0] + red[h][1]) + (red[h][2] + red[h][3]);
+    const float dz = (red[kHpg + h][0] + red[kHpg + h][1]) + (red[kHpg + h][2] + red[kHpg + h][3]);
+    const float sc = dk * a.sl2e;
+    // local read: ring parts 0 .. sr-1 plus the current token
+    const float mr = r < sr ? ml[r][h] : -INFINITY;
+    float M = fmaxf(mr, sc);
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+    const float fr = fast_exp2(mr - M);  // m = -inf -> 0
+    float L = r < sr ? ml[r][kHpg + h] * fr : 0.f;
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) L += __shfl_xor(L, o, 64);
+    const float fc = fast_exp2(sc - M);
+    L += fc;
+    // anchor read: bank parts sr .. S-1 (an empty bank reads as zero)
+    const int sb = sr + r;
+    const float mb = sb < S ? ml[sb][h] : -INFINITY;
+    float M2 = mb;
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) M2 = fmaxf(M2, __shfl_xor(M2, o, 64));
+    const float fb = mb == -INFINITY ? 0.f : fast_exp2(mb - M2);
+    float L2 = sb < S ? ml[sb][kHpg + h] * fb : 0.f;
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) L2 += __shfl_xor(L2, o, 64);
+    const float il = 1.f / L;
+    const float ga = (n > 0 && L2 > 0.f) ? tanhf(dz) / L2 : 0.f;
+    // zeros first; the weights below overwrite them (same wave, in order)
+    wt[h][r] = 0.f;
+    wt[h][kMaxSplits + r] = 0.f;
+    if (r < sr) wt[h][r] = fr * il;
+    if (sb < S) wt[h][sb] = fb * ga;
+    if (r == 0) wt[h][2 * kMaxSplits] = fc * il;
+  }
+  __syncthreads();
   uint16_t* outp = a.out + (size_t)b * a.out_bs + (size_t)g * kHpg * kD;
-
 #pragma unroll
   for (int h = 0; h < kHpg; ++h) {
-    // local read: ring parts plus the current token
-    const float sc = dts[h] * a.sl2e;
-    float M = sc;
+    float o = wt[h][2 * kMaxSplits] * vf;
 #pragma unroll
-    for (int sp = 0; sp < 2 * kMaxSplits; ++sp) M = fmaxf(M, sp < sr ? ml[sp][h] : -INFINITY);
-    float L = fast_exp2(sc - M);
-    float o = L * vf;
-#pragma unroll
-    for (int sp = 0; sp < 2 * kMaxSplits; ++sp) {
-      const float f = sp < sr ? fast_exp2(ml[sp][h] - M) : 0.f;  // m = -inf -> 0
-      o = fmaf(po[h][sp], f, o);
-      L = fmaf(ml[sp][kHpg + h], f, L);
-    }
-    const float oloc = o / L;
-
-    // anchor read: bank parts (an empty bank reads as zero)
-    float M2 = -INFINITY;
-#pragma unroll
-    for (int sp = 0; sp < 2 * kMaxSplits; ++sp)
-      M2 = fmaxf(M2, (sp >= sr && sp < S) ? ml[sp][h] : -INFINITY);
-    float o2 = 0.f, L2 = 0.f;
-#pragma unroll
-    for (int sp = 0; sp < 2 * kMaxSplits; ++sp) {
-      const float ms = (sp >= sr && sp < S) ? ml[sp][h] : -INFINITY;
-      const float f = ms == -INFINITY ? 0.f : fast_exp2(ms - M2);
-      o2 = fmaf(po[h][sp], f, o2);
-      L2 = fmaf(ml[sp][kHpg + h], f, L2);
-    }
-    const float oanc = n > 0 ? o2 / L2 : 0.f;
-    const float gate = tanhf(dts[kHpg + h]);
-    outp[(size_t)h * kD + tid] = to_bf16(fmaf(gate, oanc, oloc));
+    for (int sp = 0; sp < 2 * kMaxSplits; ++sp) o = fmaf(po[h][sp], wt[h][sp], o);
+    outp[(size_t)h * kD + tid] = to_bf16(o);
   }
 
   // Write: ring slot t mod R takes the current K/V (after every read of
