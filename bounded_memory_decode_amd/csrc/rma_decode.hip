@@ -550,6 +550,186 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a, int item
   }
 }
 
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// Loads of one 64-key tile for decode_part_kernel, as raw buffer loads:
+// a wave-uniform descriptor per plane, one 32-bit offset register per
+// lane, and the rest of each address in the scalar and immediate offsets
+// (so 64 loads need no 64-bit addresses).  The descriptor's byte bound
+// applies to the whole offset (vector + scalar + immediate) on gfx950:
+// past it a load returns zeros.
+//   K, MFMA A layout: block kb, k-step st = chunk 4 st + l / 16 of key
+//     64 tile + 16 kb + l % 16; bound = the plane.  Keys past the count
+//     read stale slots (their scores are masked).
+//   V rows: key 64 tile + 2 j + half, chunk c32; bound = count rows, so
+//     keys past the count read zeros.
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+constexpr int kBufWord3 = 0x00020000;  // descriptor word 3 for gfx9-family raw buffers
+
+__device__ __forceinline__ void part_load_k(const Seg& sg, int tile, int lane, uint4 (&kr)[32]) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)sg.K4, (short)0, sg.slots * kChunks * 16, kBufWord3);
+  const uint32_t v0 = (uint32_t)(((lane >> 4) * sg.slots + tile * kTile + (lane & 15)) * 16);
+#pragma unroll
+  for (int st = 0; st < 8; ++st)
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+      kr[8 * kb + st] = buf_load16(r, v0 + kb * 256, (uint32_t)(4 * st * sg.slots * 16));
+}
+
+__device__ __forceinline__ void part_load_v(const Seg& sg, int tile, int lane,
+                                            uint4 (&vr)[kTile / 2]) {
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)sg.V4, (short)0, sg.count * kChunks * 16, kBufWord3);
+  const uint32_t v0 = (uint32_t)(((tile * kTile + (lane >> 5)) * kChunks + (lane & 31)) * 16);
+#pragma unroll
+  for (int j = 0; j < kTile / 2; ++j)
+    vr[j] = buf_load16(r, v0 + (j & 3) * 1024, (uint32_t)((j >> 2) * 4096));
+}
+
+// Attention of the split launch when every part is one 64-key tile
+// (small batches).  grid: ceil(items / 4); block: 256 = 4 waves, one part
+// each (item = unit * S + r: tile r of the unit's ring for r <
+// splits_ring, else tile r - splits_ring of its bank), writing the part's
+// partial (o[4][256], m[4], l[4]) for the combine kernel.
+//
+// Latency first: the part's query rows and its K and V are all loaded at
+// the start, so the part costs one memory round trip.  Scores on the
+// matrix cores, per 16-key block kb: S^T (16 keys x 16 columns) = K Q^T
+// with v_mfma_f32_16x16x32_bf16, A = 16 keys x 32 dims (lane l: key
+// l % 16, chunk 4 st + l / 16 of k-step st), B = Q^T (lane l: query row
+// (l % 16) mod 4, same chunk; columns 4-15 repeat rows 0-3 and are
+// ignored); accumulator register r of lane l then holds key 4 (l / 16) + r
+// of the block for query l % 16.  P.V on the vector ALU as in the
+// whole-unit kernel: a half-wave per key, 8 dims per lane, on V rows as
+// stored.
+__global__ __launch_bounds__(256) void decode_part_kernel(DecodeArgs a, int items) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int item = blockIdx.x * kWaves + wave;
+  if (item >= items) return;
+  // per-key probabilities of the 4 heads (float4 per key), then a pad that
+  // takes the stores of lanes without a real query (no branch)
+  __shared__ float4 p_s[kWaves][kTile + 4];
+  const Seg sg = seg_of<false>(a, item, 0);
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int half = lane >> 5, c32 = lane & 31;
+  float* P = a.part + (size_t)item * kPart;
+
+  if (sg.ta == sg.tb) {  // nothing to read: m = -inf, l = 0, o = 0
+    if (lane < 32) {
+#pragma unroll
+      for (int h = 0; h < kHpg; ++h) {
+        float4* dst = reinterpret_cast<float4*>(P + h * kD + 8 * c32);
+        dst[0] = make_float4(0.f, 0.f, 0.f, 0.f);
+        dst[1] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+    if (lane < kHpg) {
+      P[kHpg * kD + lane] = -INFINITY;
+      P[kHpg * kD + kHpg + lane] = 0.f;
+    }
+    return;
+  }
+  const int tile = sg.ta;
+
+  uint4 qb[8];          // B operands (Q^T), k-step st
+  uint4 kr[4 * 8];      // A operands: block kb, k-step st at kr[8 kb + st]
+  uint4 vr[kTile / 2];  // V rows: key 2 j + half, chunk c32
+#pragma unroll
+  for (int st = 0; st < 8; ++st) qb[st] = sg.q4[(l16 & 3) * kChunks + 4 * st + lg];
+  part_load_k(sg, tile, lane, kr);
+  part_load_v(sg, tile, lane, vr);
+  __builtin_amdgcn_sched_barrier(0);
+
+  f32x4_t s[4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    s[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int st = 0; st < 8; ++st)
+      s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[8 * kb + st]),
+                                                      as_bf16x8(qb[st]), s[kb], 0, 0, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);  // scores before anything of P.V
+
+  // softmax of query l16 (log2 domain) over this lane's 16 keys, then over
+  // the 4 lanes l16 + 16 lg; only the lanes of queries 0-3 store
+  const int kbase = tile * kTile + 4 * lg;
+  float mt = -INFINITY;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float v = kbase + kb * 16 + r < sg.count ? s[kb][r] * a.sl2e : -INFINITY;
+      s[kb][r] = v;
+      mt = fmaxf(mt, v);
+    }
+  mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
+  mt = fmaxf(mt, __shfl_xor(mt, 32, 64));  // > -inf: the tile's first key is valid
+  float ps = 0.f;
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float p = fast_exp2(s[kb][r] - mt);
+      ps += p;
+      const int key = l16 < kHpg ? kb * 16 + 4 * lg + r : kTile;
+      reinterpret_cast<float*>(&p_s[wave][key])[l16 & 3] = p;
+    }
+  ps += __shfl_xor(ps, 16, 64);
+  ps += __shfl_xor(ps, 32, 64);
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+
+  float acc[kHpg][8];
+#pragma unroll
+  for (int h = 0; h < kHpg; ++h)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[h][i] = 0.f;
+#pragma unroll
+  for (int j = 0; j < kTile / 2; ++j) {
+    const uint4 vv = vr[j];
+    const float4 pp = p_s[wave][2 * j + half];
+    const float x[8] = {bf_lo(vv.x), bf_hi(vv.x), bf_lo(vv.y), bf_hi(vv.y),
+                        bf_lo(vv.z), bf_hi(vv.z), bf_lo(vv.w), bf_hi(vv.w)};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      acc[0][i] = fmaf(pp.x, x[i], acc[0][i]);
+      acc[1][i] = fmaf(pp.y, x[i], acc[1][i]);
+      acc[2][i] = fmaf(pp.z, x[i], acc[2][i]);
+      acc[3][i] = fmaf(pp.w, x[i], acc[3][i]);
+    }
+  }
+
+  // the partial: o over the two half-waves
+#pragma unroll
+  for (int h = 0; h < kHpg; ++h)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[h][i] += __shfl_xor(acc[h][i], 32, 64);
+  if (lane < 32) {
+#pragma unroll
+    for (int h = 0; h < kHpg; ++h) {
+      float4* dst = reinterpret_cast<float4*>(P + h * kD + 8 * c32);
+      dst[0] = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
+      dst[1] = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
+    }
+  }
+  if (lane < kHpg) {
+    P[kHpg * kD + lane] = mt;
+    P[kHpg * kD + kHpg + lane] = ps;
+  }
+}
+
 // Finish of the split launch.  grid: units; block: 256 (thread =
 // dimension).  Merges the parts of the local read (ring parts plus the
 // current token) and of the anchor read (bank parts), applies the gate,
@@ -781,10 +961,15 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   }
   const int S = a.splits_ring + a.splits_bank;
   const int items = a.units * S;
-  int grid = (items + kWaves - 1) / kWaves;
-  const int res = resident_workgroups<false, false>();
-  if (grid > res) grid = res;
-  hipLaunchKernelGGL((decode_attn_kernel<false, false>), dim3(grid), dim3(256), 0, s, a, items);
+  if (a.tiles_ring == 1 && a.tiles_bank == 1) {  // one tile per part
+    const int grid = (items + kWaves - 1) / kWaves;
+    hipLaunchKernelGGL(decode_part_kernel, dim3(grid), dim3(256), 0, s, a, items);
+  } else {
+    int grid = (items + kWaves - 1) / kWaves;
+    const int res = resident_workgroups<false, false>();
+    if (grid > res) grid = res;
+    hipLaunchKernelGGL((decode_attn_kernel<false, false>), dim3(grid), dim3(256), 0, s, a, items);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(decode_combine_kernel, dim3(a.units), dim3(256), 0, s, a);
