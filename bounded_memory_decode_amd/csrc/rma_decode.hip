@@ -76,6 +76,17 @@ __device__ __forceinline__ float wave_sum_u(float x) {
           __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48)));
 }
 
+__device__ __forceinline__ float wave_max_u(float x) {
+  x = fmaxf(x, dpp<kQuadSwap1>(x));
+  x = fmaxf(x, dpp<kQuadSwap2>(x));
+  x = fmaxf(x, dpp<kRowHalfMirror>(x));
+  x = fmaxf(x, dpp<kRowMirror>(x));
+  return fmaxf(fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0)),
+                     __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16))),
+               fmaxf(__int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32)),
+                     __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48))));
+}
+
 __device__ __forceinline__ float wave_max(float x) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
@@ -597,10 +608,11 @@ __device__ __forceinline__ void part_load_v(const Seg& sg, int tile, int lane,
 }
 
 // Attention of the split launch when every part is one 64-key tile
-// (small batches).  grid: ceil(items / 4); block: 256 = 4 waves, one part
-// each (item = unit * S + r: tile r of the unit's ring for r <
-// splits_ring, else tile r - splits_ring of its bank), writing the part's
-// partial (o[4][256], m[4], l[4]) for the combine kernel.
+// (small batches).  grid: items; block: one wave, one part (item = unit *
+// S + r: tile r of the unit's ring for r < splits_ring, else tile
+// r - splits_ring of its bank), writing the part's partial (o[4][256],
+// m[4], l[4]) for the combine kernel.  One wave per workgroup spreads a
+// small launch over as many CUs as it has parts.
 //
 // Latency first: the part's query rows and its K and V are all loaded at
 // the start, so the part costs one memory round trip.  Scores on the
@@ -612,14 +624,12 @@ __device__ __forceinline__ void part_load_v(const Seg& sg, int tile, int lane,
 // of the block for query l % 16.  P.V on the vector ALU as in the
 // whole-unit kernel: a half-wave per key, 8 dims per lane, on V rows as
 // stored.
-__global__ __launch_bounds__(256) void decode_part_kernel(DecodeArgs a, int items) {
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int lane = threadIdx.x & 63;
-  const int item = blockIdx.x * kWaves + wave;
-  if (item >= items) return;
+__global__ __launch_bounds__(64) void decode_part_kernel(DecodeArgs a) {
+  const int lane = threadIdx.x;
+  const int item = blockIdx.x;
   // per-key probabilities of the 4 heads (float4 per key), then a pad that
   // takes the stores of lanes without a real query (no branch)
-  __shared__ float4 p_s[kWaves][kTile + 4];
+  __shared__ float4 p_s[kTile + 4];
   const Seg sg = seg_of<false>(a, item, 0);
   const int l16 = lane & 15, lg = lane >> 4;
   const int half = lane >> 5, c32 = lane & 31;
@@ -684,7 +694,7 @@ __global__ __launch_bounds__(256) void decode_part_kernel(DecodeArgs a, int item
       const float p = fast_exp2(s[kb][r] - mt);
       ps += p;
       const int key = l16 < kHpg ? kb * 16 + 4 * lg + r : kTile;
-      reinterpret_cast<float*>(&p_s[wave][key])[l16 & 3] = p;
+      reinterpret_cast<float*>(&p_s[key])[l16 & 3] = p;
     }
   ps += __shfl_xor(ps, 16, 64);
   ps += __shfl_xor(ps, 32, 64);
@@ -699,7 +709,7 @@ __global__ __launch_bounds__(256) void decode_part_kernel(DecodeArgs a, int item
 #pragma unroll
   for (int j = 0; j < kTile / 2; ++j) {
     const uint4 vv = vr[j];
-    const float4 pp = p_s[wave][2 * j + half];
+    const float4 pp = p_s[2 * j + half];
     const float x[8] = {bf_lo(vv.x), bf_hi(vv.x), bf_lo(vv.y), bf_hi(vv.y),
                         bf_lo(vv.z), bf_hi(vv.z), bf_lo(vv.w), bf_hi(vv.w)};
 #pragma unroll
@@ -730,136 +740,109 @@ __global__ __launch_bounds__(256) void decode_part_kernel(DecodeArgs a, int item
   }
 }
 
-// Finish of the split launch.  grid: units; block: 256 (thread =
-// dimension).  Merges the parts of the local read (ring parts plus the
-// current token) and of the anchor read (bank parts), applies the gate,
-// writes the output, the ring slot and the pending slot; with per-sequence
-// positions, a token that completes its block is followed by the unit's
-// admit in this same workgroup.  Every part's value for this thread's
-// dimension is loaded before any is used, so the merge costs one memory
-// round trip.
+// Finish of the split launch.  grid: units; block: 256 = 4 waves, wave h
+// = query head h of the unit's group, lane = dims 4 lane .. 4 lane + 3.
+// Merges the parts of the local read (ring parts plus the current token)
+// and of the anchor read (bank parts), applies the gate, writes the
+// output, the ring slot and the pending slot; with per-sequence positions,
+// a token that completes its block is followed by the unit's admit in this
+// same workgroup.  Each wave merges its head alone: lane p holds part p's
+// (m, l), the weights come out of wave reductions, and every part's o for
+// the lane's dims is loaded before any is used (one memory round trip, no
+// barrier).
 __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   const int u = blockIdx.x;
   const int b = u / a.G, g = u - b * a.G;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int h = __builtin_amdgcn_readfirstlane(tid >> 6);
   const TokPos tp = tok_pos(a, b);
   if (!tp.live) return;  // the whole block: no barrier is skipped
-  __shared__ float red[8][kWaves];
-  __shared__ float ml[2 * kMaxSplits][2 * kHpg];  // (m[4], l[4]) of every part
   __shared__ AdmitShared sh;
 
   const int sr = a.splits_ring, S = a.splits_ring + a.splits_bank;
   const float* P = a.part + (size_t)u * S * kPart;
-  // (m, l) of part tid / 8; parts past S read as empty (m = -inf, l = 0)
-  {
-    const int sp = tid >> 3, j = tid & 7;
-    ml[sp][j] = sp < S ? P[(size_t)sp * kPart + kHpg * kD + j] : (j < kHpg ? -INFINITY : 0.f);
-  }
-  // o of every part for this dimension (parts past S re-read part S-1;
-  // their weight is 0)
-  float po[kHpg][2 * kMaxSplits];
+  // o of every part for this head and the lane's 4 dims (parts past S
+  // re-read part S-1; their weight is 0); (m, l) of part `lane`
+  float4 po[2 * kMaxSplits];
 #pragma unroll
   for (int sp = 0; sp < 2 * kMaxSplits; ++sp) {
     const int sc = sp < S ? sp : S - 1;
-#pragma unroll
-    for (int h = 0; h < kHpg; ++h) po[h][sp] = P[(size_t)sc * kPart + h * kD + tid];
+    po[sp] = *reinterpret_cast<const float4*>(P + (size_t)sc * kPart + h * kD + 4 * lane);
   }
+  const bool have = lane < S;
+  const float mp = have ? P[(size_t)lane * kPart + kHpg * kD + h] : -INFINITY;
+  const float lp = have ? P[(size_t)lane * kPart + kHpg * kD + kHpg + h] : 0.f;
 
-  const uint16_t* qb = a.q + (size_t)b * a.q_bs + (size_t)g * kHpg * kD;
-  const uint16_t* qab = (a.qa ? a.qa : a.q) + (size_t)b * a.q_bs + (size_t)g * kHpg * kD;
+  // current token and gate operands for the lane's dims
   const size_t kvo = (size_t)b * a.kv_bs + (size_t)g * kD;
-  float qf[kHpg], qaf[kHpg];
-#pragma unroll
-  for (int h = 0; h < kHpg; ++h) {
-    qf[h] = bf1(qb[h * kD + tid]);
-    qaf[h] = bf1(qab[h * kD + tid]);
-  }
-  const float kf = bf1(a.k[kvo + tid]);
-  const float vf = bf1(a.v[kvo + tid]);
-
-  // q.k_t (current-token score) and qa.w_g (gate argument) for the 4 heads
-  float dts[8];
-#pragma unroll
-  for (int h = 0; h < kHpg; ++h) {
-    dts[h] = wave_sum(qf[h] * kf);
-    dts[kHpg + h] = wave_sum(qaf[h] * a.w_g[(size_t)(g * kHpg + h) * kD + tid]);
-  }
-  if (lane == 0) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) red[j][wave] = dts[j];
-  }
-  __syncthreads();
-
-  // Merge weights, once per (head, part) rather than per dimension: wave 0,
-  // lane = 16 h + r, takes ring part r and bank part r of head h; the
-  // 16-lane groups reduce the maxima and sums.  wt[h][sp] is the weight of
-  // part sp (launch order: ring parts, then bank parts, then zeros), that
-  // of a bank part with the gate folded in, so that out = sum_sp wt * o_sp
-  // + wt[h][2 kMaxSplits] * v_t.
-  __shared__ float wt[kHpg][2 * kMaxSplits + 4];
+  const size_t qo = (size_t)b * a.q_bs + (size_t)(g * kHpg + h) * kD + 4 * lane;
+  const uint2 qv = *reinterpret_cast<const uint2*>(a.q + qo);
+  const uint2 qav = *reinterpret_cast<const uint2*>((a.qa ? a.qa : a.q) + qo);
+  const uint2 kv = *reinterpret_cast<const uint2*>(a.k + kvo + 4 * lane);
+  const uint2 vv = *reinterpret_cast<const uint2*>(a.v + kvo + 4 * lane);
+  const float4 wv = *reinterpret_cast<const float4*>(a.w_g + (size_t)(g * kHpg + h) * kD + 4 * lane);
   const int n = scalar_load(a.bank_n + u);
-  if (wave == 0) {
-    const int h = lane >> 4, r = lane & 15;
-    const float dk = (red[h][0] + red[h][1]) + (red[h][2] + red[h][3]);
-    const float dz = (red[kHpg + h][0] + red[kHpg + h][1]) + (red[kHpg + h][2] + red[kHpg + h][3]);
-    const float sc = dk * a.sl2e;
-    // local read: ring parts 0 .. sr-1 plus the current token
-    const float mr = r < sr ? ml[r][h] : -INFINITY;
-    float M = fmaxf(mr, sc);
+
+  // q.k_t (current-token score) and qa.w_g (gate argument)
+  float dk = bf_lo(qv.x) * bf_lo(kv.x);
+  dk = fmaf(bf_hi(qv.x), bf_hi(kv.x), dk);
+  dk = fmaf(bf_lo(qv.y), bf_lo(kv.y), dk);
+  dk = fmaf(bf_hi(qv.y), bf_hi(kv.y), dk);
+  float dz = bf_lo(qav.x) * wv.x;
+  dz = fmaf(bf_hi(qav.x), wv.y, dz);
+  dz = fmaf(bf_lo(qav.y), wv.z, dz);
+  dz = fmaf(bf_hi(qav.y), wv.w, dz);
+  const float sc = wave_sum_u(dk) * a.sl2e;
+  dz = wave_sum_u(dz);
+
+  // weights: local read = ring parts 0 .. sr-1 plus the current token;
+  // anchor read = bank parts sr .. S-1 (an empty bank reads as zero), the
+  // gate folded into its weights
+  const bool ring = lane < sr, bank = have && !ring;
+  const float M = fmaxf(wave_max_u(ring ? mp : -INFINITY), sc);
+  const float fr = ring ? fast_exp2(mp - M) : 0.f;  // m = -inf -> 0
+  const float fc = fast_exp2(sc - M);
+  const float L = wave_sum_u(lp * fr) + fc;
+  const float M2 = wave_max_u(bank ? mp : -INFINITY);
+  const float fb = (bank && mp != -INFINITY) ? fast_exp2(mp - M2) : 0.f;
+  const float L2 = wave_sum_u(lp * fb);
+  const float il = 1.f / L;
+  const float ga = (n > 0 && L2 > 0.f) ? tanhf(dz) / L2 : 0.f;
+  const float w = ring ? fr * il : fb * ga;  // weight of part `lane`
+  const float wc = fc * il;
+
+  float o[4] = {wc * bf_lo(vv.x), wc * bf_hi(vv.x), wc * bf_lo(vv.y), wc * bf_hi(vv.y)};
 #pragma unroll
-    for (int o = 8; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
-    const float fr = fast_exp2(mr - M);  // m = -inf -> 0
-    float L = r < sr ? ml[r][kHpg + h] * fr : 0.f;
-#pragma unroll
-    for (int o = 8; o > 0; o >>= 1) L += __shfl_xor(L, o, 64);
-    const float fc = fast_exp2(sc - M);
-    L += fc;
-    // anchor read: bank parts sr .. S-1 (an empty bank reads as zero)
-    const int sb = sr + r;
-    const float mb = sb < S ? ml[sb][h] : -INFINITY;
-    float M2 = mb;
-#pragma unroll
-    for (int o = 8; o > 0; o >>= 1) M2 = fmaxf(M2, __shfl_xor(M2, o, 64));
-    const float fb = mb == -INFINITY ? 0.f : fast_exp2(mb - M2);
-    float L2 = sb < S ? ml[sb][kHpg + h] * fb : 0.f;
-#pragma unroll
-    for (int o = 8; o > 0; o >>= 1) L2 += __shfl_xor(L2, o, 64);
-    const float il = 1.f / L;
-    const float ga = (n > 0 && L2 > 0.f) ? tanhf(dz) / L2 : 0.f;
-    // zeros first; the weights below overwrite them (same wave, in order)
-    wt[h][r] = 0.f;
-    wt[h][kMaxSplits + r] = 0.f;
-    if (r < sr) wt[h][r] = fr * il;
-    if (sb < S) wt[h][sb] = fb * ga;
-    if (r == 0) wt[h][2 * kMaxSplits] = fc * il;
+  for (int sp = 0; sp < 2 * kMaxSplits; ++sp) {
+    const float ws = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w), sp));
+    o[0] = fmaf(po[sp].x, ws, o[0]);
+    o[1] = fmaf(po[sp].y, ws, o[1]);
+    o[2] = fmaf(po[sp].z, ws, o[2]);
+    o[3] = fmaf(po[sp].w, ws, o[3]);
   }
-  __syncthreads();
-  uint16_t* outp = a.out + (size_t)b * a.out_bs + (size_t)g * kHpg * kD;
-#pragma unroll
-  for (int h = 0; h < kHpg; ++h) {
-    float o = wt[h][2 * kMaxSplits] * vf;
-#pragma unroll
-    for (int sp = 0; sp < 2 * kMaxSplits; ++sp) o = fmaf(po[h][sp], wt[h][sp], o);
-    outp[(size_t)h * kD + tid] = to_bf16(o);
-  }
+  uint16_t* outp = a.out + (size_t)b * a.out_bs + (size_t)(g * kHpg + h) * kD + 4 * lane;
+  *reinterpret_cast<uint2*>(outp) =
+      make_uint2((uint32_t)to_bf16(o[0]) | ((uint32_t)to_bf16(o[1]) << 16),
+                 (uint32_t)to_bf16(o[2]) | ((uint32_t)to_bf16(o[3]) << 16));
 
   // Write: ring slot t mod R takes the current K/V (after every read of
   // this step, which all finished in the attention kernel), and pending
-  // slot t mod C takes the candidate record and score.
-  if (tid < 32) {
-    uint4* rk = reinterpret_cast<uint4*>(a.ring_k + (size_t)u * a.R * kD);
-    rk[k_chunk_index(tp.ring_slot, tid, a.R)] = reinterpret_cast<const uint4*>(a.k + kvo)[tid];
-  } else if (tid < 64) {
-    uint4* rv = reinterpret_cast<uint4*>(a.ring_v + ((size_t)u * a.R + tp.ring_slot) * kD);
-    rv[tid - 32] = reinterpret_cast<const uint4*>(a.v + kvo)[tid - 32];
-  } else if (tid < 96) {
-    uint4* pk = reinterpret_cast<uint4*>(a.pend_k + ((size_t)u * a.C + tp.pend_slot) * kD);
-    pk[tid - 64] = reinterpret_cast<const uint4*>(a.ck + kvo)[tid - 64];
-  } else if (tid < 128) {
-    uint4* pv = reinterpret_cast<uint4*>(a.pend_v + ((size_t)u * a.C + tp.pend_slot) * kD);
-    pv[tid - 96] = reinterpret_cast<const uint4*>(a.cv + kvo)[tid - 96];
-  } else if (tid == 128) {
-    a.pscore[(size_t)u * a.C + tp.pend_slot] = a.cs[(size_t)b * a.cs_bs + g];
+  // slot t mod C takes the candidate record and score; one wave each.
+  if (lane < 32) {
+    if (h == 0) {
+      uint4* rk = reinterpret_cast<uint4*>(a.ring_k + (size_t)u * a.R * kD);
+      rk[k_chunk_index(tp.ring_slot, lane, a.R)] = reinterpret_cast<const uint4*>(a.k + kvo)[lane];
+    } else if (h == 1) {
+      uint4* rv = reinterpret_cast<uint4*>(a.ring_v + ((size_t)u * a.R + tp.ring_slot) * kD);
+      rv[lane] = reinterpret_cast<const uint4*>(a.v + kvo)[lane];
+    } else if (h == 2) {
+      uint4* pk = reinterpret_cast<uint4*>(a.pend_k + ((size_t)u * a.C + tp.pend_slot) * kD);
+      pk[lane] = reinterpret_cast<const uint4*>(a.ck + kvo)[lane];
+    } else {
+      uint4* pv = reinterpret_cast<uint4*>(a.pend_v + ((size_t)u * a.C + tp.pend_slot) * kD);
+      pv[lane] = reinterpret_cast<const uint4*>(a.cv + kvo)[lane];
+      if (lane == 0) a.pscore[(size_t)u * a.C + tp.pend_slot] = a.cs[(size_t)b * a.cs_bs + g];
+    }
   }
 
   // per-sequence positions: the token completes its block -> admit now
@@ -962,8 +945,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   const int S = a.splits_ring + a.splits_bank;
   const int items = a.units * S;
   if (a.tiles_ring == 1 && a.tiles_bank == 1) {  // one tile per part
-    const int grid = (items + kWaves - 1) / kWaves;
-    hipLaunchKernelGGL(decode_part_kernel, dim3(grid), dim3(256), 0, s, a, items);
+    hipLaunchKernelGGL(decode_part_kernel, dim3(items), dim3(64), 0, s, a);
   } else {
     int grid = (items + kWaves - 1) / kWaves;
     const int res = resident_workgroups<false, false>();
