@@ -85,7 +85,13 @@ int make_layout(const rma_config* c, int32_t batch, rma_layout* L) {
   L->pscore = take(units * C * 4);
   L->bank_n = take(units * 4);
   const Splits sp = choose_splits(c, batch);
+  // split-K partials of the decode launch and, for small batches, of the
+  // split prefill launch (never both at once: calls on a state are ordered)
   L->scratch_bytes = (uint64_t)batch * c->kv_groups * (sp.ring + sp.bank) * kPart * 4;
+  if (rma::prefill_split(batch, c->kv_groups)) {
+    const uint64_t pf = (uint64_t)batch * c->commit * c->q_heads * rma::kPfSplits * rma::kPfPart * 4;
+    L->scratch_bytes = pf > L->scratch_bytes ? pf : L->scratch_bytes;
+  }
   L->scratch = take(L->scratch_bytes);
   L->total_bytes = off;
   L->ring_bytes = units * R * rec_half * 2;
@@ -197,6 +203,7 @@ rma::PrefillArgs prefill_args(const rma_state* st, int32_t layer, int32_t n_toke
   a.pend_k = region<uint16_t>(st, L.pend_k) + unit0 * C * kD;
   a.pend_v = region<uint16_t>(st, L.pend_v) + unit0 * C * kD;
   a.pscore = region<float>(st, L.pscore) + unit0 * C;
+  a.part = region<float>(st, L.scratch);
   a.pos = pos;
   a.B = B;
   a.G = G;

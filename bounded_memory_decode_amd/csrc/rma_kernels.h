@@ -88,11 +88,25 @@ struct PrefillArgs {
   const int32_t* pos;      // [B] block start of each sequence (a sequence
                            // whose entry is < 0 or not a multiple of C is
                            // left out), or null: every sequence at P
+  float* part;             // scratch of the split launch (small batches):
+                           // [B][n][H][kPfSplits][kPfPart]
   int B, G, H, R, N, C;
   int n;                   // tokens in the block (1 .. C)
   int64_t P;               // lockstep: position of the block's first token
   float sl2e;              // scale * log2(e)
 };
+
+// Split prefill launch for small batches: each query row's local read is
+// cut in kPfLocalSplits slices of its tiles and its anchor read in
+// kPfBankSplits, one workgroup per slice, whose partials (o[D], m, l) are
+// merged by a second kernel.  Used iff batch * groups < 32 (fewer than one
+// 32-token workgroup per CU for a full block), a function of the batch
+// only so that the scratch size is known at layout time.
+constexpr int kPfLocalSplits = 2;
+constexpr int kPfBankSplits = 2;
+constexpr int kPfSplits = kPfLocalSplits + kPfBankSplits;
+constexpr int kPfPart = kD + 4;  // floats per partial: o[D], m, l, padding
+inline bool prefill_split(int batch, int groups) { return batch * groups < 32; }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
 

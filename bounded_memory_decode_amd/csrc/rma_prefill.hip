@@ -27,6 +27,10 @@
 //    the row-major V rows.
 //  * Online softmax in the log2 domain; local and anchor reads separately
 //    normalised, then out = o_local + tanh(q . w_g) * o_anchor.
+//  * Small batches (batch * groups < 32, under one 32-token workgroup per
+//    CU): each read is cut into slices of its tiles, one workgroup per
+//    slice, and prefill_merge_kernel merges the slices' partials by their
+//    running maxima and applies the gate.
 #include "rma_kernels.h"
 
 namespace rma {
@@ -100,28 +104,35 @@ enum : int { kSegRing = 0, kSegBlock = 1, kSegBank = 2 };
 // k slot 8 lg + j holds key 4 lg + j (j < 4, first 16-key sub-tile) or key
 // 16 + 4 lg + (j - 4) (second sub-tile), which is where the S^T accumulator
 // of lane group lg keeps them; the V^T operand is read in the same order.
-template <int kWaves>
+// kSplit (small batches): the workgroup reads one slice of one read, part
+// pr of kPfSplits (the local read cut in kPfLocalSplits slices of its tiles,
+// the anchor read in kPfBankSplits), and writes its unnormalised partial
+// (o, running max, sum) per query row to a.part for prefill_merge_kernel.
+template <int kWaves, bool kSplit>
 __global__ __launch_bounds__(64 * kWaves) void prefill_attn_kernel(PrefillArgs a) {
   constexpr int kThreads = 64 * kWaves;
   constexpr int kTokWG = 4 * kWaves;                     // 4 tokens (16 query rows) per wave
   constexpr int kStage = 2 * kPT * kChunks / kThreads;   // K and V chunks staged per thread
-  // Workgroup -> (query tile, sequence, group).  The hardware hands
+  // Workgroup -> (query tile, sequence, group[, part]).  The hardware hands
   // workgroup w to XCD w mod 8, each XCD with its own L2; all query tiles of
-  // one (sequence, group) read the same K/V tiles, so when the number of
-  // (sequence, group) units is a multiple of 8 they are all placed on one
-  // XCD (w mod 8 fixed) and share its L2.
+  // one (sequence, group[, part]) read the same K/V tiles, so when the
+  // number of such units is a multiple of 8 they are all placed on one XCD
+  // (w mod 8 fixed) and share its L2.
   const int nqt = (a.n + kTokWG - 1) / kTokWG;
-  const int units = a.B * a.G;
+  const int units = a.B * a.G * (kSplit ? kPfSplits : 1);
   const int w = blockIdx.x;
-  int qt, u;
+  int qt, vu;
   if ((units & 7) == 0) {
     const int r = w >> 3;
     qt = r % nqt;
-    u = (w & 7) + 8 * (r / nqt);
+    vu = (w & 7) + 8 * (r / nqt);
   } else {
     qt = w % nqt;
-    u = w / nqt;
+    vu = w / nqt;
   }
+  const int u = kSplit ? vu / kPfSplits : vu;
+  const int pr = kSplit ? vu - u * kPfSplits : 0;  // part (kSplit)
+  const bool anchor_part = kSplit && pr >= kPfLocalSplits;
   const int b = u / a.G, g = u - b * a.G;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l16 = lane & 15, lg = lane >> 4;  // MFMA column / k-group
@@ -144,7 +155,7 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_kernel(PrefillArgs a
 #pragma unroll
     for (int st = 0; st < 8; ++st) qa[st] = ok ? qrow[st * 4 + lg] : make_uint4(0, 0, 0, 0);
   };
-  load_q(a.q);
+  load_q(anchor_part && a.qa != nullptr ? a.qa : a.q);
 
   const int R = a.R;
   int64_t P = a.P;
@@ -163,6 +174,18 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_kernel(PrefillArgs a
   const int t_bank = (nb + kPT - 1) / kPT;
   const int t_loc = t_ring + t_blk;
   const int t_all = t_loc + t_bank;
+  // tiles of this workgroup: all, or the slice of its part
+  int ta = 0, tb = t_all;
+  if (kSplit) {
+    if (anchor_part) {
+      const int i = pr - kPfLocalSplits;
+      ta = t_loc + i * t_bank / kPfBankSplits;
+      tb = t_loc + (i + 1) * t_bank / kPfBankSplits;
+    } else {
+      ta = pr * t_loc / kPfLocalSplits;
+      tb = (pr + 1) * t_loc / kPfLocalSplits;
+    }
+  }
   // ring age threshold: slot s holds position P - R + age(s), age(s) =
   // (s - P) mod R; it exists iff age >= R - P
   const int min_age = (int)(R - P > 0 ? R - P : 0);
@@ -261,11 +284,34 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_kernel(PrefillArgs a
   };
   reset();
 
-  // tile 0 into LDS; tile 1 in registers (each tile's loads are issued two
-  // tiles ahead of its use, so they have two tiles of work to land)
-  stage_store(0, 0, stage_load(0, 0));
-  if (kParts == 2) stage_store(0, 1, stage_load(0, 1));
-  const int t1 = 1 < t_all ? 1 : 0;
+  // kSplit: the part's partial of this lane's query row (an empty slice:
+  // m = -inf, l = 0, o = 0)
+  auto write_part = [&](bool empty) {
+    if (q_tok < n) {
+      float* dst = a.part + ((((size_t)b * n + q_tok) * a.H + g * kHpg + q_head) * kPfSplits + pr) *
+                                kPfPart;
+#pragma unroll
+      for (int dt = 0; dt < 16; ++dt)
+        *reinterpret_cast<float4*>(dst + 16 * dt + 4 * lg) =
+            empty ? make_float4(0.f, 0.f, 0.f, 0.f)
+                  : make_float4(o[dt][0], o[dt][1], o[dt][2], o[dt][3]);
+      if (lg == 0) {
+        dst[kD] = empty ? -INFINITY : m_run;
+        dst[kD + 1] = empty ? 0.f : l_run;
+      }
+    }
+  };
+  if (kSplit && ta >= tb) {
+    write_part(true);
+    return;
+  }
+
+  // tile ta into LDS; tile ta + 1 in registers (each tile's loads are
+  // issued two tiles ahead of its use, so they have two tiles of work to
+  // land)
+  stage_store(ta & 1, 0, stage_load(ta, 0));
+  if (kParts == 2) stage_store(ta & 1, 1, stage_load(ta, 1));
+  const int t1 = ta + 1 < tb ? ta + 1 : ta;
   Stage x0 = stage_load(t1, 0), x1 = x0, y0 = x0, y1 = x0;
   if (kParts == 2) x1 = stage_load(t1, 1);
   __syncthreads();
@@ -280,7 +326,7 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_kernel(PrefillArgs a
     int seg, ti;
     seg_of(t, seg, ti);
     const int cnt = seg_count(seg);
-    if (a.qa != nullptr && t == t_loc) {  // first bank tile: the anchor query
+    if (!kSplit && a.qa != nullptr && t == t_loc) {  // first bank tile: the anchor query
       load_q(a.qa);
       // wait for these loads here, on this one tile: left pending, they
       // make the compiler guard the scores of every tile with a wait on
@@ -289,7 +335,7 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_kernel(PrefillArgs a
     }
     // prefetch of tile t + 2, without branches: past the last tile, reload
     // the last one
-    const int tn = t + 2 < t_all ? t + 2 : t_all - 1;
+    const int tn = t + 2 < tb ? t + 2 : tb - 1;
     nxt0 = stage_load(tn, 0);
     if (kParts == 2) nxt1 = stage_load(tn, 1);
 
@@ -405,7 +451,7 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_kernel(PrefillArgs a
     }
 
     // end of the local read: normalise and keep it
-    if (t == t_loc - 1) {
+    if (!kSplit && t == t_loc - 1) {
       const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
 #pragma unroll
       for (int dt = 0; dt < 16; ++dt) oloc[dt] = o[dt] * inv;
@@ -415,12 +461,16 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_kernel(PrefillArgs a
     if (kParts == 2) stage_store((t + 1) & 1, 1, cur1);
     __syncthreads();
   };
-  int t = 0;
-  for (; t + 1 < t_all; t += 2) {
+  int t = ta;
+  for (; t + 1 < tb; t += 2) {
     tile_step(t, x0, x1, y0, y1);
     tile_step(t + 1, y0, y1, x0, x1);
   }
-  if (t < t_all) tile_step(t, x0, x1, y0, y1);
+  if (t < tb) tile_step(t, x0, x1, y0, y1);
+  if (kSplit) {
+    write_part(false);
+    return;
+  }
   if (t_loc == 0) {
     // no visible local key is impossible for a real token (it sees itself)
 #pragma unroll
@@ -500,6 +550,70 @@ __global__ __launch_bounds__(128) void prefill_commit_kernel(PrefillArgs a) {
   }
 }
 
+// Merge of the split launch.  grid: ceil(B n H / 4); block: 256 = 4 waves,
+// one query row (sequence, token, head) per wave, lane = dims 4 lane ..
+// 4 lane + 3.  The local slices and the anchor slices are each merged by
+// their running maxima, then out = o_local + tanh(qa . w_g) * o_anchor (an
+// empty bank reads as zero).
+__global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillArgs a) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);  // (b, token, head)
+  const int lane = threadIdx.x & 63;
+  const int rows = a.B * a.n * a.H;
+  if (row >= rows) return;
+  const int b = row / (a.n * a.H);
+  if (a.pos != nullptr) {  // left-out sequences: no partials, no output
+    const int p = a.pos[b];
+    if (p < 0 || p % a.C != 0) return;
+  }
+  const int hq = row % a.H;
+  const float* pp = a.part + (size_t)row * kPfSplits * kPfPart;
+  float4 o[kPfSplits];
+  float m[kPfSplits], l[kPfSplits];
+#pragma unroll
+  for (int i = 0; i < kPfSplits; ++i) {
+    o[i] = *reinterpret_cast<const float4*>(pp + i * kPfPart + 4 * lane);
+    m[i] = pp[i * kPfPart + kD];
+    l[i] = pp[i * kPfPart + kD + 1];
+  }
+  const uint16_t* qsrc = a.qa != nullptr ? a.qa : a.q;
+  const uint2 qv = *reinterpret_cast<const uint2*>(qsrc + (size_t)row * kD + 4 * lane);
+  const float4 wv = *reinterpret_cast<const float4*>(a.w_g + (size_t)hq * kD + 4 * lane);
+  float z = __uint_as_float(qv.x << 16) * wv.x;
+  z = fmaf(__uint_as_float(qv.x & 0xffff0000u), wv.y, z);
+  z = fmaf(__uint_as_float(qv.y << 16), wv.z, z);
+  z = fmaf(__uint_as_float(qv.y & 0xffff0000u), wv.w, z);
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off, 64);
+  const float gate = tanhf(z);
+
+  // slices [i0, i1) of one read -> (sum of e_i o_i) / (sum of e_i l_i)
+  auto merge = [&](int i0, int i1) {
+    float M = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kPfSplits; ++i)
+      if (i >= i0 && i < i1) M = fmaxf(M, m[i]);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    float L = 0.f;
+#pragma unroll
+    for (int i = 0; i < kPfSplits; ++i) {
+      if (i < i0 || i >= i1) continue;
+      const float e = m[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[i] - M);
+      acc.x = fmaf(e, o[i].x, acc.x);
+      acc.y = fmaf(e, o[i].y, acc.y);
+      acc.z = fmaf(e, o[i].z, acc.z);
+      acc.w = fmaf(e, o[i].w, acc.w);
+      L = fmaf(e, l[i], L);
+    }
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+    return make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  };
+  const float4 ol = merge(0, kPfLocalSplits);
+  const float4 oa = merge(kPfLocalSplits, kPfSplits);
+  uint16_t* orow = a.out + (size_t)row * kD + 4 * lane;
+  *reinterpret_cast<uint2*>(orow) = make_uint2(pack_bf16(fmaf(gate, oa.x, ol.x), fmaf(gate, oa.y, ol.y)),
+                                               pack_bf16(fmaf(gate, oa.z, ol.z), fmaf(gate, oa.w, ol.w)));
+}
+
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
@@ -507,11 +621,18 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
   // when that still gives a workgroup per CU; else 4-wave ones
   const int units = a.B * a.G;
   const int tiles8 = (a.n + 31) / 32;
-  if ((int64_t)tiles8 * units >= 256) {
-    hipLaunchKernelGGL(prefill_attn_kernel<8>, dim3(tiles8 * units), dim3(512), 0, s, a);
+  const int tiles4 = (a.n + 15) / 16;
+  if (prefill_split(a.B, a.G)) {
+    hipLaunchKernelGGL((prefill_attn_kernel<4, true>), dim3(tiles4 * units * kPfSplits), dim3(256),
+                       0, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int rows = a.B * a.n * a.H;
+    hipLaunchKernelGGL(prefill_merge_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, a);
+  } else if ((int64_t)tiles8 * units >= 256) {
+    hipLaunchKernelGGL((prefill_attn_kernel<8, false>), dim3(tiles8 * units), dim3(512), 0, s, a);
   } else {
-    const int tiles4 = (a.n + 15) / 16;
-    hipLaunchKernelGGL(prefill_attn_kernel<4>, dim3(tiles4 * units), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((prefill_attn_kernel<4, false>), dim3(tiles4 * units), dim3(256), 0, s, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

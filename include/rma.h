@@ -108,7 +108,8 @@ typedef struct {
  *   bsrc    [units][N]         i32    source position of each anchor
  *   pscore  [units][C]         f32    score of each pending candidate
  *   bank_n  [units]            i32    committed anchors (dense prefix)
- *   scratch                           split-K partials, library-private
+ *   scratch                           split-K partials of the decode and of the
+ *                                     small-batch prefill, library-private
  */
 typedef struct {
   uint64_t ring_k, ring_v, bank_k, bank_v, pend_k, pend_v;

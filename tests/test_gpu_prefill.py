@@ -147,3 +147,39 @@ def test_long_prompt_start_eight_layers():
         step += 1
     torch.cuda.synchronize()
     gu.check_state(S, o, "long end")
+
+
+@pytest.mark.parametrize("n", [256, 60])
+def test_batch8_launch_paths(n):
+    """Batch 8, above the small-batch split: a full block takes the 8-wave
+    kernel, a 60-token block the 4-wave one.  Sequences at their own
+    block-aligned positions (per-sequence call); two sampled sequences (a
+    full history and an empty one) against one-sequence oracles, outputs
+    and state."""
+    from test_gpu_positions import _rows, _seq_oracles
+    gu.log(f"case prefill batch 8, n={n}")
+    base = synth.WORKLOADS["layer_b1"]
+    specs = [(32768, 1024), (33024, 700), (256, 0), (1024, 1024), (32768, 512), (0, 0),
+             (4096, 1000), (768, 64)]
+    sampled = (0, 5)
+    seed = 56
+    states, oracles = _seq_oracles(base, specs, seed)
+    w = base.with_(B=len(specs))
+    S = gu.assemble_state(w, states)
+    wg = synth.gate_weights(w, seed)
+    wg_dev = gu.to_dev(wg[0])
+    x = synth.block_inputs(w, seed, 0, 0, n)
+    d = gu.inputs_to_dev(x)
+    pos = torch.tensor([t0 for t0, _ in specs], dtype=torch.int32, device=gu.DEV)
+    out = S.prefill_block_at(0, pos, d["q"], d["k"], d["v"], d["ck"], d["cv"], d["cs"], wg_dev)
+    for b in sampled:
+        o = oracles[b]
+        xb = _rows(x, b)
+        vm = gu.vmax(o.ring_v, o.bank_v, xb["v"])
+        ref = o.prefill_block(0, xb["q"], xb["k"], xb["v"], xb["ck"], xb["cv"], xb["cs"], wg[0])
+        if o.pend_n[0] == o.C:
+            o.admit(0)
+        gu.check_out(out[b:b + 1], ref, f"batch 8 prefill n={n} sequence {b}", p_bf16_vmax=vm)
+    torch.cuda.synchronize()
+    for b in sampled:
+        gu.check_seq_state(S, b, oracles[b], f"batch 8 prefill n={n}")
