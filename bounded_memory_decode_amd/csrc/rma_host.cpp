@@ -37,23 +37,20 @@ int check_config(const rma_config* c) {
 }
 
 int ceil_div(int a, int b) { return (a + b - 1) / b; }
+int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Split-K policy: every read (ring, bank) of a (sequence, group) unit is
-// cut into parts of whole 64-key tiles so that there are at least ~1,024
-// parts in a launch (one per wave of the persistent attention kernel on a
-// 256-CU device).  A function of the batch only, so that the scratch size
-// is known before the first call.
+// cut into s parts of whole 64-key tiles for the persistent attention
+// kernel, whose 1,024 waves (256 CUs) take the parts round by round.  The
+// split s (a power of two) minimises rounds x tiles per part, the time of
+// the launch if every part costs its tiles; ties go to the smaller s (fewer
+// partials to merge).  A function of the batch only, so that the scratch
+// size is known before the first call.
 struct Splits {
   int ring, bank, tiles_ring, tiles_bank;
 };
 
-Splits choose_splits(const rma_config* c, int32_t batch) {
-  const int units = batch * c->kv_groups;
-  const int tr = ceil_div(c->window - 1, kTile);
-  const int tb = ceil_div(c->bank_cap, kTile);
-  const int tmax = tr > tb ? tr : tb;
-  int s = 1;
-  while (s < kMaxSplits && units * 2 * s < 1024 && s < tmax) s *= 2;
+Splits split_of(int tr, int tb, int s) {
   Splits r;
   r.tiles_ring = ceil_div(tr, s);
   r.tiles_bank = ceil_div(tb, s);
@@ -61,6 +58,27 @@ Splits choose_splits(const rma_config* c, int32_t batch) {
   r.ring = ceil_div(tr, r.tiles_ring);
   r.bank = ceil_div(tb, r.tiles_bank);
   return r;
+}
+
+Splits choose_splits(const rma_config* c, int32_t batch) {
+  constexpr int64_t kWavesPerLaunch = 1024;
+  const int64_t units = (int64_t)batch * c->kv_groups;
+  const int tr = ceil_div(c->window - 1, kTile);
+  const int tb = ceil_div(c->bank_cap, kTile);
+  const int tmax = tr > tb ? tr : tb;
+  Splits best = split_of(tr, tb, 1);
+  int64_t best_cost = -1;
+  for (int s = 1;; s *= 2) {
+    const Splits r = split_of(tr, tb, s);
+    const int64_t rounds = ceil_div64(units * (r.ring + r.bank), kWavesPerLaunch);
+    const int64_t cost = rounds * (r.tiles_ring > r.tiles_bank ? r.tiles_ring : r.tiles_bank);
+    if (best_cost < 0 || cost < best_cost) {
+      best = r;
+      best_cost = cost;
+    }
+    if (s >= kMaxSplits || s >= tmax) break;
+  }
+  return best;
 }
 
 int make_layout(const rma_config* c, int32_t batch, rma_layout* L) {
