@@ -44,8 +44,8 @@ int64_t ceil_div64(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // kernel, whose 1,024 waves (256 CUs) take the parts round by round.  The
 // split s (a power of two) minimises rounds x tiles per part, the time of
 // the launch if every part costs its tiles; ties go to the smaller s (fewer
-// partials to merge).  A function of the batch only, so that the scratch
-// size is known before the first call.
+// partials to merge) except as noted below.  A function of the batch
+// only, so that the scratch size is known before the first call.
 struct Splits {
   int ring, bank, tiles_ring, tiles_bank;
 };
@@ -72,7 +72,12 @@ Splits choose_splits(const rma_config* c, int32_t batch) {
     const Splits r = split_of(tr, tb, s);
     const int64_t rounds = ceil_div64(units * (r.ring + r.bank), kWavesPerLaunch);
     const int64_t cost = rounds * (r.tiles_ring > r.tiles_bank ? r.tiles_ring : r.tiles_bank);
-    if (best_cost < 0 || cost < best_cost) {
+    // on a tie, one-tile parts (the small-batch part kernel) win while they
+    // fill at most 4 rounds (measured faster up to 128 units, slower from
+    // 256); otherwise the smaller split does
+    const bool one_tile = r.tiles_ring == 1 && r.tiles_bank == 1 &&
+                          units * (r.ring + r.bank) <= 4 * kWavesPerLaunch;
+    if (best_cost < 0 || cost < best_cost || (cost == best_cost && one_tile)) {
       best = r;
       best_cost = cost;
     }
