@@ -344,17 +344,22 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_kernel(PrefillArgs a
 
     // S^T = K Q^T for the tile's two 16-key sub-tiles: A = 16 keys x 32
     // dims (lane: key l16, chunk 4 st + lg), B = Q^T
-    f32x4_t s[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+    // (two accumulators per sub-tile, even and odd k-steps: four independent
+    // MFMA chains instead of two)
+    f32x4_t s4[2][2];
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) s4[sub][0] = s4[sub][1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int st = 0; st < 8; ++st) {
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub) {
         const uint4 ka = *reinterpret_cast<const uint4*>(&kl[(sub * 16 + l16) * kRowK +
                                                               (st * 4 + lg) * 16]);
-        s[sub] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka), as_bf16x8(qa[st]),
-                                                          s[sub], 0, 0, 0);
+        s4[sub][st & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            as_bf16x8(ka), as_bf16x8(qa[st]), s4[sub][st & 1], 0, 0, 0);
       }
     }
+    const f32x4_t s[2] = {s4[0][0] + s4[0][1], s4[1][0] + s4[1][1]};
 
     // Mask.  A tile every key of which is visible to every query of the
     // wave (most ring and bank tiles) skips it; the test is wave-uniform.
