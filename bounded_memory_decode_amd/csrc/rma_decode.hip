@@ -2,13 +2,17 @@
 // the local ring and over the committed anchor bank, the signed gate that
 // merges the two reads, the ring write and the pending append.
 //
-// Two launch shapes of one persistent, wave-pipelined attention kernel:
-//   * whole-unit (large batch): a wave owns a (sequence, group) unit, reads
-//     its ring then its bank, and finishes the token in-wave (current
-//     token, gate, output, ring write, pending append): one launch;
-//   * split (small batch): reads are cut into parts of 64-key tiles spread
-//     over all waves; partials go to scratch and a combine kernel finishes
-//     the token.
+// Three launch shapes:
+//   * whole-unit (large batch): a wave of the persistent, wave-pipelined
+//     attention kernel owns a (sequence, group) unit, reads its ring then
+//     its bank, and finishes the token in-wave (current token, gate,
+//     output, ring write, pending append): one launch;
+//   * split, multi-tile parts (middling batch): reads are cut into parts of
+//     whole 64-key tiles taken by the same persistent kernel; partials go
+//     to scratch and a combine kernel finishes the token;
+//   * split, one-tile parts (small batch): one wave per 64-key tile in
+//     decode_part_kernel (all loads at once, scores on MFMA), then the
+//     combine kernel.
 // Positions come from the lockstep arguments or, per sequence, from a
 // device array (TokPos); with per-sequence positions a completed block is
 // admitted right after the token (in the combine workgroup, or by an admit
