@@ -525,9 +525,15 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_kernel(PrefillArgs a
 
 // The block's writes, after every query of the block has read the ring:
 // token j goes to ring slot (P + j) mod R and pending slot (P + j) mod C.
-// grid: (n, units); block: 128.
-__global__ __launch_bounds__(128) void prefill_commit_kernel(PrefillArgs a) {
-  const int j = blockIdx.x, u = blockIdx.y;
+// grid: (ceil(n / 8), units); block: 256, 8 tokens of one unit.  V,
+// pending and score rows are row-contiguous and copied directly; ring K is
+// chunk-major, so the 8 K rows pass through LDS and each chunk plane gets
+// 8 consecutive slots (128 bytes, contiguous up to the wrap at R) per
+// store instead of 16-byte pieces from separate workgroups.  (64 tokens per
+// workgroup left too few workgroups at small batches.)
+constexpr int kCommitTok = 8;
+__global__ __launch_bounds__(256) void prefill_commit_kernel(PrefillArgs a) {
+  const int j0 = blockIdx.x * kCommitTok, u = blockIdx.y;
   const int b = u / a.G, g = u - b * a.G;
   const int tid = threadIdx.x;
   int64_t P = a.P;
@@ -536,22 +542,34 @@ __global__ __launch_bounds__(128) void prefill_commit_kernel(PrefillArgs a) {
     if (p < 0 || p % a.C != 0) return;
     P = p;
   }
-  const size_t src = (((size_t)b * a.n + j) * a.G + g) * kD;
-  const int rs = (int)((P + j) % a.R), ps = (int)((P + j) % a.C);
-  const int c = tid & 31;
-  if (tid < 32) {
-    uint4* rk = reinterpret_cast<uint4*>(a.ring_k + (size_t)u * a.R * kD);
-    rk[k_chunk_index(rs, c, a.R)] = reinterpret_cast<const uint4*>(a.k + src)[c];
-  } else if (tid < 64) {
-    reinterpret_cast<uint4*>(a.ring_v + ((size_t)u * a.R + rs) * kD)[c] =
-        reinterpret_cast<const uint4*>(a.v + src)[c];
-  } else if (tid < 96) {
-    reinterpret_cast<uint4*>(a.pend_k + ((size_t)u * a.C + ps) * kD)[c] =
-        reinterpret_cast<const uint4*>(a.ck + src)[c];
-  } else {
-    reinterpret_cast<uint4*>(a.pend_v + ((size_t)u * a.C + ps) * kD)[c] =
-        reinterpret_cast<const uint4*>(a.cv + src)[c];
-    if (tid == 96) a.pscore[(size_t)u * a.C + ps] = a.cs[((size_t)b * a.n + j) * a.G + g];
+  const int nt = a.n - j0 < kCommitTok ? a.n - j0 : kCommitTok;
+  __shared__ uint4 kt[kCommitTok][kChunks + 1];  // K rows, one chunk of padding each
+  // thread x = tid + 256 i: token x / 32, chunk x % 32 (rows read whole)
+#pragma unroll
+  for (int i = 0; i < kCommitTok * kChunks / 256; ++i) {
+    const int x = tid + 256 * i, jj = x >> 5, c = x & 31;
+    if (jj < nt) {
+      const int j = j0 + jj;
+      const size_t src = (((size_t)b * a.n + j) * a.G + g) * kD;
+      const int rs = (int)((P + j) % a.R), ps = (int)((P + j) % a.C);
+      kt[jj][c] = reinterpret_cast<const uint4*>(a.k + src)[c];
+      reinterpret_cast<uint4*>(a.ring_v + ((size_t)u * a.R + rs) * kD)[c] =
+          reinterpret_cast<const uint4*>(a.v + src)[c];
+      reinterpret_cast<uint4*>(a.pend_k + ((size_t)u * a.C + ps) * kD)[c] =
+          reinterpret_cast<const uint4*>(a.ck + src)[c];
+      reinterpret_cast<uint4*>(a.pend_v + ((size_t)u * a.C + ps) * kD)[c] =
+          reinterpret_cast<const uint4*>(a.cv + src)[c];
+      if (c == 0) a.pscore[(size_t)u * a.C + ps] = a.cs[((size_t)b * a.n + j) * a.G + g];
+    }
+  }
+  __syncthreads();
+  // ring K: thread x: chunk x / 64, token x % 64 (consecutive lanes write
+  // consecutive slots of one chunk plane)
+  uint4* rk = reinterpret_cast<uint4*>(a.ring_k + (size_t)u * a.R * kD);
+#pragma unroll
+  for (int i = 0; i < kCommitTok * kChunks / 256; ++i) {
+    const int x = tid + 256 * i, c = x / kCommitTok, jj = x % kCommitTok;
+    if (jj < nt) rk[k_chunk_index((int)((P + j0 + jj) % a.R), c, a.R)] = kt[jj][c];
   }
 }
 
@@ -641,7 +659,8 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(prefill_commit_kernel, dim3(a.n, a.B * a.G), dim3(128), 0, s, a);
+  hipLaunchKernelGGL(prefill_commit_kernel, dim3((a.n + kCommitTok - 1) / kCommitTok, a.B * a.G),
+                     dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
