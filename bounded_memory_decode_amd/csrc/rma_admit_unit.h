@@ -14,13 +14,15 @@
 // every NaN ranks below -inf; evicted slots (ascending) take admitted
 // candidates (ascending j); the remainder is appended at n, n+1, ...
 //
-// Selection by rank: each pool entry becomes the 64-bit key
+// Selection by threshold: each pool entry becomes the 64-bit key
 //   (order-preserving image of the score) << 32 | (0xFFFFFFFF - index),
 // so that the order above is the descending order of distinct integers;
-// an entry is kept iff fewer than K = min(N, n + C) keys exceed it.  Every
-// thread counts, for the keys it owns, the keys above them in one pass
-// over the pool in LDS (broadcast reads), so there is no sort and no
-// barrier inside the selection.
+// an entry is kept iff its key is at least the K-th largest key,
+// K = min(N, n + C).  The K-th largest key comes from a radix select,
+// most-significant 8-bit digit first: a 256-bin LDS histogram of the keys
+// that still match the chosen digits, a block scan to find the digit whose
+// bin holds the K-th, until that bin holds a single key (at most 8
+// passes).  No sort and no all-pairs comparison.
 #pragma once
 #include "rma_kernels.h"
 
@@ -44,7 +46,9 @@ struct AdmitUnit {
 };
 
 struct AdmitShared {
-  alignas(16) uint64_t key[kMaxPool + 2];  // + padding for pairwise reads
+  int hist[256];      // radix-select histogram
+  int sel[3];         // chosen digit, keys above it, keys in its bin
+  uint64_t kth;       // the K-th largest key, once found
   int evicted[256];
   int admitted[256];
   int lds4[4];
@@ -88,25 +92,51 @@ __device__ __forceinline__ int admit_block_scan(int v, int* total, int* lds4) {
   return before + x - v;
 }
 
-// ranks of keys tid, tid + 256, ... (kR of them): keys of the pool greater
-// than each, counted over key[0 .. P) (key[P], key[P+1] are 0).
-template <int kR>
-__device__ __forceinline__ void admit_ranks(const uint64_t* key, int P, int* rank) {
+// The k-th largest (1 <= k <= valid keys) of the keys kv[r] held by the
+// block's threads (entry i = r * 256 + tid, valid iff i < P; keys are
+// distinct), by a radix select over 8-bit digits, most significant first.
+__device__ inline uint64_t admit_kth_largest(const uint64_t (&kv)[9], int P, int k,
+                                             AdmitShared& sh) {
   const int tid = threadIdx.x;
-  uint64_t mine[kR];
+  uint64_t prefix = 0;  // the digits chosen so far
+  for (int shift = 56; shift >= 0; shift -= 8) {
+    sh.hist[tid] = 0;
+    __syncthreads();
+    const uint64_t above_mask = shift == 56 ? 0ull : (~0ull << (shift + 8));
 #pragma unroll
-  for (int r = 0; r < kR; ++r) {
-    const int i = r * kAdmitThreads + tid;
-    mine[r] = i < P ? key[i] : ~0ull;  // past the pool: never counted as kept
-    rank[r] = 0;
-  }
-  const ulonglong2* k2 = reinterpret_cast<const ulonglong2*>(key);
-#pragma unroll 8
-  for (int j = 0; j < (P + 1) / 2; ++j) {
-    const ulonglong2 kk = k2[j];
+    for (int r = 0; r < 9; ++r) {
+      const int i = r * kAdmitThreads + tid;
+      if (i < P && (kv[r] & above_mask) == prefix)
+        atomicAdd(&sh.hist[(int)((kv[r] >> shift) & 255u)], 1);
+    }
+    __syncthreads();
+    // bins in descending digit order: thread tid holds digit 255 - tid
+    const int cnt = sh.hist[255 - tid];
+    int tot = 0;
+    const int above = admit_block_scan(cnt, &tot, sh.lds4);  // keys with a larger digit
+    if (above < k && k <= above + cnt) {
+      sh.sel[0] = 255 - tid;
+      sh.sel[1] = above;
+      sh.sel[2] = cnt;
+    }
+    __syncthreads();
+    k -= sh.sel[1];
+    prefix |= (uint64_t)sh.sel[0] << shift;
+    if (sh.sel[2] == 1) {  // one key left with these digits: it is the k-th
+      const uint64_t mask = ~0ull << shift;
 #pragma unroll
-    for (int r = 0; r < kR; ++r) rank[r] += (int)(kk.x > mine[r]) + (int)(kk.y > mine[r]);
+      for (int r = 0; r < 9; ++r) {
+        const int i = r * kAdmitThreads + tid;
+        if (i < P && (kv[r] & mask) == prefix) sh.kth = kv[r];
+      }
+      __syncthreads();
+      const uint64_t t = sh.kth;
+      __syncthreads();  // every thread has read sel and kth before they change
+      return t;
+    }
+    __syncthreads();  // every thread has read sel before the next pass writes it
   }
+  return prefix;
 }
 
 __device__ inline void admit_unit(const AdmitUnit& a, AdmitShared& sh) {
@@ -117,13 +147,13 @@ __device__ inline void admit_unit(const AdmitUnit& a, AdmitShared& sh) {
   const int K = P < N ? P : N;
   const int R = (P + kAdmitThreads - 1) / kAdmitThreads;  // keys per thread, <= 8
 
-  // rank of every pool entry (P <= N: everything is kept, no ranking)
-  int rank[8];
-#pragma unroll
-  for (int r = 0; r < 8; ++r) rank[r] = 0;
+  // the pool's keys, entry i = r * 256 + tid (past the pool: 0, below every
+  // real key); P <= N keeps everything, with no selection
+  uint64_t kv[9];
+  uint64_t thr = 0;  // kept iff key >= thr
   if (P > N) {
-    // all score loads first (one memory round trip): entry i = r*256 + tid
-    // (past the pool: a clamped re-read, replaced by the padding key 0)
+    // all score loads first (one memory round trip); past the pool: a
+    // clamped re-read, replaced by the key 0
     float sv[9];
 #pragma unroll
     for (int r = 0; r < 9; ++r) {
@@ -135,21 +165,13 @@ __device__ inline void admit_unit(const AdmitUnit& a, AdmitShared& sh) {
 #pragma unroll
     for (int r = 0; r < 9; ++r) {
       const int i = r * kAdmitThreads + tid;
-      if (i < P + 2)
-        sh.key[i] = i < n ? admit_pool_key(sv[r], (uint32_t)i)
-                          : (i < P ? admit_pool_key(sv[r], (uint32_t)(N + (i - n))) : 0ull);
+      kv[r] = i < n ? admit_pool_key(sv[r], (uint32_t)i)
+                    : (i < P ? admit_pool_key(sv[r], (uint32_t)(N + (i - n))) : 0ull);
     }
-    __syncthreads();
-    switch (R) {
-      case 1: admit_ranks<1>(sh.key, P, rank); break;
-      case 2: admit_ranks<2>(sh.key, P, rank); break;
-      case 3: admit_ranks<3>(sh.key, P, rank); break;
-      case 4: admit_ranks<4>(sh.key, P, rank); break;
-      case 5: admit_ranks<5>(sh.key, P, rank); break;
-      case 6: admit_ranks<6>(sh.key, P, rank); break;
-      case 7: admit_ranks<7>(sh.key, P, rank); break;
-      default: admit_ranks<8>(sh.key, P, rank); break;
-    }
+    thr = admit_kth_largest(kv, P, K, sh);
+  } else {
+#pragma unroll
+    for (int r = 0; r < 9; ++r) kv[r] = 0;
   }
 
   // evicted anchors and admitted candidates, both ascending: pool entry
@@ -158,10 +180,10 @@ __device__ inline void admit_unit(const AdmitUnit& a, AdmitShared& sh) {
   int ne = 0, na = 0;
   for (int r = 0; r < R; ++r) {
     const int i = r * kAdmitThreads + tid;
-    int rr = rank[0];
+    uint64_t key = kv[0];
 #pragma unroll
-    for (int x = 1; x < 8; ++x) rr = r == x ? rank[x] : rr;
-    const bool kept = rr < K;
+    for (int x = 1; x < 9; ++x) key = r == x ? kv[x] : key;
+    const bool kept = key >= thr;
     const int ev = (i < n && !kept) ? 1 : 0;
     const int ad = (i >= n && i < P && kept) ? 1 : 0;
     int tot = 0;
