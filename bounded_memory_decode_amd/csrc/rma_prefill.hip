@@ -43,12 +43,11 @@ typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef short v8i16_t __attribute__((ext_vector_type(8)));
 
 constexpr int kPT = 32;          // keys per tile
-// Bytes per staged row.  A 16-byte LDS read serves 16 lanes per pass and
-// an 8-byte one 32: K rows (16-byte operand reads of 16 consecutive keys)
-// are 132 dwords apart (4 mod 64 banks), V rows (8-byte transposed reads of
-// 4 lane groups x 4 keys) 136 dwords apart (8 mod 64), so that neither read
-// nor the row-wise staging writes have bank conflicts.
-constexpr int kRowK = 528;
+// Bytes per staged row (padding against LDS bank conflicts).  Chosen by
+// measurement of the batch-8 prefill over 16-byte multiples: K rows 544
+// (136 dwords) and V rows 544 ran fastest (K rows of 528: +5%, 576: +10%;
+// V rows of 528 or 560: +2-4%).
+constexpr int kRowK = 544;
 constexpr int kRowV = 544;
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
