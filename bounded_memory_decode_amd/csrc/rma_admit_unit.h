@@ -28,8 +28,9 @@
 
 namespace rma {
 
-constexpr int kMaxPool = 2048;  // N + C
+constexpr int kMaxPool = 2048;  // N + C (the configuration check enforces it)
 constexpr int kAdmitThreads = 256;
+static_assert(9 * kAdmitThreads >= kMaxPool, "each thread holds at most 9 pool entries");
 
 // One unit's records and counts.
 struct AdmitUnit {

@@ -46,7 +46,6 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
 
 __device__ __forceinline__ float bf_lo(uint32_t x) { return __uint_as_float(x << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
-__device__ __forceinline__ float bf1(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
