@@ -28,21 +28,14 @@
 // is given, else q.
 //
 // Data layout (owned by this library, see include/rma.h): K planes are
-// chunk-major (16-byte chunks of 8 dims), so that a wave loading chunk c of
-// 64 consecutive slots reads 1 KiB of contiguous memory with one key per
-// lane; V planes are row-major so that a half-wave loads one 512-byte row.
-// Neither read needs an LDS transpose.
+// chunk-major (16-byte chunks of 8 dims), so that one load of a score
+// MFMA's A operand (16 consecutive slots x 4 consecutive chunks) reads four
+// contiguous 256-byte runs; V planes are row-major so that a half-wave
+// loads one 512-byte row.  Neither read needs an LDS transpose.
 #include "rma_admit_unit.h"
 
 namespace rma {
 namespace {
-
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-
-__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
-                                          __builtin_bit_cast(bf16x2_t, b), c, false);
-}
 
 __device__ __forceinline__ float bf_lo(uint32_t x) { return __uint_as_float(x << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t x) { return __uint_as_float(x & 0xffff0000u); }
@@ -90,17 +83,35 @@ __device__ __forceinline__ float wave_max_u(float x) {
                      __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48))));
 }
 
-__device__ __forceinline__ float wave_max(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o, 64));
-  return x;
+// Max / sum over lanes l and l ^ 16 (resp. l ^ 32), in every lane:
+// v_permlane16_swap / v_permlane32_swap with the value in both operands
+// leave the lane's own value in one result and its partner's in the other.
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float max16(float x) {
+  const unsigned u = __float_as_uint(x);
+  const u32x2_t r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r.x), __uint_as_float(r.y));
+}
+__device__ __forceinline__ float max32(float x) {
+  const unsigned u = __float_as_uint(x);
+  const u32x2_t r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r.x), __uint_as_float(r.y));
+}
+__device__ __forceinline__ float sum16(float x) {
+  const unsigned u = __float_as_uint(x);
+  const u32x2_t r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+  return __uint_as_float(r.x) + __uint_as_float(r.y);
+}
+__device__ __forceinline__ float sum32(float x) {
+  const unsigned u = __float_as_uint(x);
+  const u32x2_t r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r.x) + __uint_as_float(r.y);
 }
 
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o, 64);
-  return x;
-}
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
 // fp32 -> bf16, round to nearest, ties to even.
 __device__ __forceinline__ uint16_t to_bf16(float f) {
@@ -333,6 +344,55 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs& a, int u, int lane
   }
 }
 
+// Raw buffer loads: a wave-uniform descriptor per plane, one 32-bit offset
+// register per lane, and the rest of each address in the scalar and
+// immediate offsets (so a tile's 64 loads need no 64-bit addresses).  The
+// descriptor's byte bound applies to the whole offset (vector + scalar +
+// immediate) on gfx950: past it a load returns zeros.
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+constexpr int kBufWord3 = 0x00020000;  // descriptor word 3 for gfx9-family raw buffers
+
+// K of one 64-key tile for decode_attn_kernel, as the A operands of its
+// score MFMAs: kr[8 kb + st] = chunk 4 st + l / 16 of key 64 tile + 16 kb +
+// l % 16 of a chunk-major plane of `slots` slots; a key past `hi` re-reads
+// key hi, so every load stays inside the plane.  Raw buffer loads: the
+// plane's descriptor, one offset register per 16-key block, the k-step in
+// the scalar offset.  With `idle` (nothing left to fetch) the descriptor's
+// range is empty: the loads are still issued, so the loop has no
+// conditional loads, but they touch no memory and return zeros.
+__device__ __forceinline__ void load_k_tile(const uint4* base, int slots, int hi, int tile,
+                                            int lane, bool idle, uint4 (&kr)[kChunks]) {
+  // the descriptor and the scalar offset are wave-uniform; readfirstlane
+  // tells the compiler so (else it wraps each load in a waterfall loop)
+  const uint64_t bp = reinterpret_cast<uint64_t>(base);
+  // (the builtin returns int: each word goes back through uint32_t, or the
+  // low word's bit 31 would sign-extend over the high word)
+  const uint32_t bp_lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)bp);
+  const uint32_t bp_hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(bp >> 32));
+  const uint64_t bu = ((uint64_t)bp_hi << 32) | bp_lo;
+  const uint32_t bytes =
+      (uint32_t)__builtin_amdgcn_readfirstlane(idle ? 0 : slots * kChunks * 16);
+  const __amdgpu_buffer_rsrc_t r =
+      __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(bu), (short)0, bytes, kBufWord3);
+  uint32_t vo[4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    const int key = tile * kTile + 16 * kb + (lane & 15);
+    vo[kb] = idle ? 0u : (uint32_t)(((lane >> 4) * slots + (key < hi ? key : hi)) * 16);
+  }
+  const uint32_t sst = (uint32_t)__builtin_amdgcn_readfirstlane(idle ? 0 : 4 * slots * 16);
+#pragma unroll
+  for (int st = 0; st < 8; ++st)
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) kr[8 * kb + st] = buf_load16(r, vo[kb], st * sst);
+}
+
 // Persistent attention kernel.  grid: at most the resident workgroups;
 // block: 256 = 4 independent waves.  Wave gw takes items gw, gw + W, ...
 // (W = all waves) and walks their segments.  Per tile i, in issue order:
@@ -343,6 +403,10 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs& a, int u, int lane
 // for V(i) and P.V(i) never waits for K(i+1): a wave keeps ~64 16-byte
 // loads in flight across tile, segment and item boundaries.  No
 // workgroup barrier: each wave owns its LDS slices.
+// QK runs on the matrix cores (v_mfma_f32_16x16x32_bf16, K as loaded by
+// load_k_tile as the A operand, the 4 query rows as B columns, repeated
+// over the 16 columns); P.V runs on the vector ALU, a half-wave per key
+// and 8 dims per lane, on V rows as stored.
 template <bool kWhole, bool kQA>
 __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a, int items) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -354,10 +418,14 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a, int item
 
   __shared__ uint4 q_s[kWaves][kHpg * kChunks];  // each wave's 4 query rows
   __shared__ uint4 qa_s[kQA ? kWaves : 1][kHpg * kChunks];  // anchor query rows (kQA)
-  __shared__ float4 p_s[kWaves][kTile];          // per-key probabilities
+  // per-key probabilities of the 4 heads, then a pad that takes the stores
+  // of the lanes that hold copies (no branch)
+  __shared__ float4 p_s[kWaves][2 * kTile];
   __shared__ float or_s[kWhole ? kWaves : 1][kHpg * kD];  // ring result
 
   const int half = lane >> 5, c32 = lane & 31;
+  const int l16 = lane & 15, lg = lane >> 4;
+  uint4 qb[8];  // B operands of the score MFMAs (the segment's query rows)
   uint4 kr[kChunks];
   uint4 vr[kTile / 2];
   uint4 qn0, qn1;  // auxiliary loads for the next segment (2 x 16 B per lane)
@@ -365,18 +433,9 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a, int item
   float mr[kHpg], lr[kHpg];  // whole-unit: the ring result
 
   Seg cur = seg_of<kWhole>(a, item, sub);
-  // K of one tile: chunk c of the lane's key (keys past the count re-read
-  // the last valid key)
-  auto load_k = [&](const Seg& sg, int tile) {
-    const int key = tile * kTile + lane;
-    const int hi = sg.count > 0 ? sg.count - 1 : 0;
-    const int ks = key < hi ? key : hi;
-#pragma unroll
-    for (int c = 0; c < kChunks; ++c) kr[c] = sg.K4[k_chunk_index(ks, c, sg.slots)];
-  };
   qn0 = cur.q4[2 * lane];
   qn1 = cur.q4[2 * lane + 1];
-  load_k(cur, cur.ta);
+  load_k_tile(cur.K4, cur.slots, cur.count > 0 ? cur.count - 1 : 0, cur.ta, lane, false, kr);
 
   for (;;) {
     if (!kWhole || sub == 0) {
@@ -392,6 +451,10 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a, int item
     // query rows of this segment's scores
     const uint4* qrows = (kWhole && kQA && sub == 1) ? qa_s[kQA ? wave : 0] : q_s[wave];
     __builtin_amdgcn_wave_barrier();
+    // B operand of k-step st: column n takes query row n mod 4, chunk
+    // 4 st + l / 16 (columns 4-15 repeat rows 0-3)
+#pragma unroll
+    for (int st = 0; st < 8; ++st) qb[st] = qrows[(lane & 3) * kChunks + 4 * st + lg];
 
     int nitem = item, nsub = sub + 1;
     if (!kWhole || nsub == 2) {
@@ -403,16 +466,13 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a, int item
 
     float m[kHpg], l[kHpg], acc[kHpg][8];
 #pragma unroll
-    for (int h = 0; h < kHpg; ++h) {
-      m[h] = -INFINITY;
-      l[h] = 0.f;
+    for (int h = 0; h < kHpg; ++h)
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[h][i] = 0.f;
-    }
+    float mq = -INFINITY, lq = 0.f;  // running max and sum of head lane % 4
 
     for (int tile = cur.ta; tile < cur.tb; ++tile) {
       const int tbase = tile * kTile;
-      const bool valid = tbase + lane < cur.count;
 
 #pragma unroll
       for (int j = 0; j < kTile / 2; ++j) {
@@ -421,42 +481,63 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a, int item
       }
       __builtin_amdgcn_sched_barrier(0);  // keep the V loads ahead of QK
 
-      // scores of this lane's key against the 4 heads
-      float s[kHpg] = {0.f, 0.f, 0.f, 0.f};
+      // Scores on the matrix cores, per 16-key block kb: S^T (16 keys x 16
+      // columns) = K Q^T with v_mfma_f32_16x16x32_bf16 over the 8 k-steps;
+      // register r of lane l then holds key 16 kb + 4 (l / 16) + r against
+      // head l mod 4 (lanes l, l ^ 4, l ^ 8, l ^ 12 hold the same scores).
+      f32x4_t d[4];
 #pragma unroll
-      for (int c = 0; c < kChunks; ++c) {
-        const uint4 kv = kr[c];
+      for (int kb = 0; kb < 4; ++kb) d[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int h = 0; h < kHpg; ++h) {
-          const uint4 qv = qrows[h * kChunks + c];
-          s[h] = dot2(qv.x, kv.x, s[h]);
-          s[h] = dot2(qv.y, kv.y, s[h]);
-          s[h] = dot2(qv.z, kv.z, s[h]);
-          s[h] = dot2(qv.w, kv.w, s[h]);
-        }
-      }
+      for (int st = 0; st < 8; ++st)
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb)
+          d[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[8 * kb + st]),
+                                                          as_bf16x8(qb[st]), d[kb], 0, 0, 0);
 
-      // online softmax update (log2 domain)
-      float p[kHpg];
+      // online softmax update of head lane mod 4 (log2 domain): the max over
+      // the lane's 16 keys, then over lanes l ^ 16 and l ^ 32
+      const int k0 = tbase + 4 * lg;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          d[kb][r] = k0 + 16 * kb + r < cur.count ? d[kb][r] * a.sl2e : -INFINITY;
+          mx = fmaxf(mx, d[kb][r]);
+        }
+      mx = max32(max16(mx));
+      const float mn = fmaxf(mq, mx);
+      const float al = fast_exp2(mq - mn);
+      float ps = 0.f;
+      float* pw = reinterpret_cast<float*>(&p_s[wave][(l16 < kHpg ? 0 : kTile) + 4 * lg]) +
+                  (lane & 3);
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float p = fast_exp2(d[kb][r] - mn);
+          ps += p;
+          pw[4 * (16 * kb + r)] = p;
+        }
+      lq = lq * al + ps;
+      mq = mn;
+      // rescale the P.V accumulators of every head (lane h holds head h)
 #pragma unroll
       for (int h = 0; h < kHpg; ++h) {
-        const float sv = valid ? s[h] * a.sl2e : -INFINITY;
-        const float mn = fmaxf(m[h], wave_max(sv));
-        const float al = fast_exp2(m[h] - mn);
-        p[h] = fast_exp2(sv - mn);
-        l[h] = l[h] * al + p[h];
-        m[h] = mn;
+        const float ah = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(al), h));
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[h][i] *= al;
+        for (int i = 0; i < 8; ++i) acc[h][i] *= ah;
       }
-      p_s[wave][lane] = make_float4(p[0], p[1], p[2], p[3]);
       __builtin_amdgcn_wave_barrier();
 
       // prefetch: the next tile of this segment, else the next segment's
-      // first tile and query rows.  Loads with nothing to fetch (the query
-      // rows while the segment continues, K after the last segment) re-read
-      // the V row this lane loaded above, a cache hit; base and stride are
-      // selected on the scalar unit, so the loop stays free of branches.
+      // first tile and query rows.  Loads with nothing to fetch are still
+      // issued, so the loop stays free of branches: the query-row loads
+      // while the segment continues re-read the V row this lane loaded
+      // above (a cache hit), and K after the last segment goes through an
+      // empty descriptor range.  Bases and strides are selected on the
+      // scalar unit.
       {
         const bool more = tile + 1 < cur.tb;
         const bool go_next = !more && has_next;
@@ -473,13 +554,8 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a, int item
         qn1 = *(go_next ? ap.p1 : vrow_p);
         const int ktile = more ? tile + 1 : nxt.ta;
         const int kcount = more ? cur.count : nxt.count;
-        const uint4* kb = idle ? cur.V4 : (more ? cur.K4 : nxt.K4);
-        const int kstride = idle ? 0 : (more ? cur.slots : nxt.slots);
-        const int key = ktile * kTile + lane;
-        const int hi = kcount > 0 ? kcount - 1 : 0;
-        const int koff = idle ? voff : (key < hi ? key : hi);
-#pragma unroll
-        for (int c = 0; c < kChunks; ++c) kr[c] = kb[(size_t)c * kstride + koff];
+        load_k_tile(more ? cur.K4 : nxt.K4, more ? cur.slots : nxt.slots,
+                    kcount > 0 ? kcount - 1 : 0, ktile, lane, idle, kr);
       }
       __builtin_amdgcn_sched_barrier(0);  // keep the prefetch ahead of P.V
 
@@ -501,10 +577,13 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a, int item
       __builtin_amdgcn_wave_barrier();
     }
 
-    // segment result: l over all lanes, o over the two half-waves
+    // segment result: m and l of each head (l summed over lanes l, l ^ 16,
+    // l ^ 32, l ^ 48; lane h holds head h), o over the two half-waves
+    lq = sum32(sum16(lq));
 #pragma unroll
     for (int h = 0; h < kHpg; ++h) {
-      l[h] = wave_sum(l[h]);
+      m[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mq), h));
+      l[h] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lq), h));
 #pragma unroll
       for (int i = 0; i < 8; ++i) acc[h][i] += __shfl_xor(acc[h][i], 32, 64);
     }
@@ -556,7 +635,7 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a, int item
       const AuxPtrs ap = aux_ptrs<kWhole, kQA>(a, nxt, nsub, item, lane);
       qn0 = *ap.p0;
       qn1 = *ap.p1;
-      load_k(nxt, nxt.ta);
+      load_k_tile(nxt.K4, nxt.slots, nxt.count > 0 ? nxt.count - 1 : 0, nxt.ta, lane, false, kr);
     }
     cur = nxt;
     item = nitem;
@@ -564,31 +643,13 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a, int item
   }
 }
 
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
-
-// Loads of one 64-key tile for decode_part_kernel, as raw buffer loads:
-// a wave-uniform descriptor per plane, one 32-bit offset register per
-// lane, and the rest of each address in the scalar and immediate offsets
-// (so 64 loads need no 64-bit addresses).  The descriptor's byte bound
-// applies to the whole offset (vector + scalar + immediate) on gfx950:
-// past it a load returns zeros.
+// Loads of one 64-key tile for decode_part_kernel:
 //   K, MFMA A layout: block kb, k-step st = chunk 4 st + l / 16 of key
 //     64 tile + 16 kb + l % 16; bound = the plane.  Keys past the count
 //     read stale slots (their scores are masked).
 //   V rows: key 64 tile + 2 j + half, chunk c32; bound = count rows, so
 //     keys past the count read zeros.
-typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
-  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
-  return make_uint4(v.x, v.y, v.z, v.w);
-}
-
-constexpr int kBufWord3 = 0x00020000;  // descriptor word 3 for gfx9-family raw buffers
-
 __device__ __forceinline__ void part_load_k(const Seg& sg, int tile, int lane, uint4 (&kr)[32]) {
   const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
       (void*)sg.K4, (short)0, sg.slots * kChunks * 16, kBufWord3);

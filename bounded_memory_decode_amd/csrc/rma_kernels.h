@@ -8,17 +8,16 @@ namespace rma {
 
 constexpr int kD = 256;       // head dimension the kernels are built for
 constexpr int kHpg = 4;       // query heads per KV group
-constexpr int kTile = 64;     // keys per wave tile (one key per lane)
+constexpr int kTile = 64;     // keys per wave tile
 constexpr int kChunks = kD / 8;  // 16-byte chunks per K/V row
 constexpr int kPart = kHpg * kD + 2 * kHpg;  // floats per split partial
 constexpr int kMaxSplits = 16;  // split-K parts per read (ring, bank)
 
 // K planes are chunk-major: the 16-byte chunk c (dims 8c .. 8c+7) of slot
-// s of a plane with `slots` slots lives at uint4 index c * slots + s, so a
-// wave loading chunk c of 64 consecutive slots (one key per lane) reads
-// 1 KiB of contiguous memory, and the 32 chunk loads of a tile spread over
-// 32 regions of the plane (measured faster on MI355X than a contiguous
-// 32 KiB tile block, which concentrates a wave's loads on fewer channels).
+// s of a plane with `slots` slots lives at uint4 index c * slots + s.  A
+// tile's K then spreads over 32 regions of the plane, one 1 KiB run per
+// chunk (measured faster on MI355X than a contiguous 32 KiB tile block,
+// which concentrates a wave's loads on fewer channels).
 __host__ __device__ inline size_t k_chunk_index(int slot, int c, int slots) {
   return (size_t)c * slots + slot;
 }
