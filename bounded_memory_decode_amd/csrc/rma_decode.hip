@@ -113,6 +113,34 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
+// One of two wave-uniform pointers, chosen per lane.  The pointers go
+// through readfirstlane first: a per-lane select between two fields of the
+// kernel-argument struct otherwise becomes a dynamically indexed private
+// copy of the struct (scratch memory, and a scratch load plus a full
+// vector-memory wait wherever it is read).
+template <typename T>
+__device__ __forceinline__ T* pick(bool first, T* p0, T* p1) {
+  const uint64_t u0 = reinterpret_cast<uint64_t>(p0), u1 = reinterpret_cast<uint64_t>(p1);
+  const uint64_t v0 = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(u0 >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)u0);
+  const uint64_t v1 = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(u1 >> 32)) << 32) |
+                      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)u1);
+  return reinterpret_cast<T*>(first ? v0 : v1);
+}
+
+// 16-byte accesses through the global address space: a generic (flat)
+// access could also reach LDS, and the compiler then waits for every
+// outstanding vector-memory access at its next wait instead of for the one
+// it needs.
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store16(void* p, uint4 v) {
+  *(__attribute__((address_space(1))) u32x4_t*)p = u32x4_t{v.x, v.y, v.z, v.w};
+}
+__device__ __forceinline__ uint4 load16(const void* p) {
+  const u32x4_t v = *(const __attribute__((address_space(1))) u32x4_t*)p;
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
 // fp32 -> bf16, round to nearest, ties to even.
 __device__ __forceinline__ uint16_t to_bf16(float f) {
   uint32_t u = __float_as_uint(f);
@@ -236,8 +264,8 @@ __device__ __forceinline__ AuxPtrs aux_ptrs(const DecodeArgs& a, const Seg& nxt,
     const int b = item / a.G, g = item - b * a.G;
     const size_t kvo = (size_t)b * a.kv_bs + (size_t)g * kD;
     const int c32 = lane & 31;
-    const uint4* fk = reinterpret_cast<const uint4*>((lane < 32 ? a.k : a.v) + kvo) + c32;
-    const uint4* fc = reinterpret_cast<const uint4*>((lane < 32 ? a.ck : a.cv) + kvo) + c32;
+    const uint4* fk = reinterpret_cast<const uint4*>(pick(lane < 32, a.k, a.v) + kvo) + c32;
+    const uint4* fc = reinterpret_cast<const uint4*>(pick(lane < 32, a.ck, a.cv) + kvo) + c32;
     ap.p0 = nsub == 1 ? fk : ap.p0;
     ap.p1 = nsub == 1 ? fc : ap.p1;
   }
@@ -262,8 +290,8 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs& a, int u, int lane
   const int c32 = lane & 31;
   if (kQA) {  // operands not delivered by the pipeline in this mode
     const size_t kvo = (size_t)b * a.kv_bs + (size_t)g * kD;
-    f.k_or_v = reinterpret_cast<const uint4*>((lane < 32 ? a.k : a.v) + kvo)[c32];
-    f.ck_or_cv = reinterpret_cast<const uint4*>((lane < 32 ? a.ck : a.cv) + kvo)[c32];
+    f.k_or_v = load16(reinterpret_cast<const uint4*>(pick(lane < 32, a.k, a.v) + kvo) + c32);
+    f.ck_or_cv = load16(reinterpret_cast<const uint4*>(pick(lane < 32, a.ck, a.cv) + kvo) + c32);
   }
   // the current K (lanes 0-31, 8 dims each) and V (lanes 32-63)
   const uint4 kv = f.k_or_v;
@@ -322,25 +350,22 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs& a, int u, int lane
       pk.y = (uint32_t)o16[2] | ((uint32_t)o16[3] << 16);
       pk.z = (uint32_t)o16[4] | ((uint32_t)o16[5] << 16);
       pk.w = (uint32_t)o16[6] | ((uint32_t)o16[7] << 16);
-      *reinterpret_cast<uint4*>(outp + (size_t)h * kD) = pk;
+      store16(outp + (size_t)h * kD, pk);
     }
   }
   // Write: ring slot t mod R (K chunks from lanes 0-31, the V row from
   // lanes 32-63), pending slot t mod C likewise.
-  if (lane < 32) {
-    uint4* rk = reinterpret_cast<uint4*>(a.ring_k + (size_t)u * a.R * kD);
-    rk[k_chunk_index(tp.ring_slot, c32, a.R)] = kv;
-    uint4* pk = reinterpret_cast<uint4*>(a.pend_k + ((size_t)u * a.C + tp.pend_slot) * kD);
-    pk[c32] = f.ck_or_cv;
-  } else {
-    uint4* rv = reinterpret_cast<uint4*>(a.ring_v + ((size_t)u * a.R + tp.ring_slot) * kD);
-    rv[c32] = kv;
-    uint4* pv = reinterpret_cast<uint4*>(a.pend_v + ((size_t)u * a.C + tp.pend_slot) * kD);
-    pv[c32] = f.ck_or_cv;
+  {
+    const bool kside = lane < 32;
+    const size_t ro = kside ? (size_t)u * a.R * kChunks + k_chunk_index(tp.ring_slot, c32, a.R)
+                            : ((size_t)u * a.R + tp.ring_slot) * kChunks + c32;
+    store16(reinterpret_cast<uint4*>(pick(kside, a.ring_k, a.ring_v)) + ro, kv);
+    const size_t po = ((size_t)u * a.C + tp.pend_slot) * kChunks + c32;
+    store16(reinterpret_cast<uint4*>(pick(kside, a.pend_k, a.pend_v)) + po, f.ck_or_cv);
   }
   if (lane == 0) {
     const float cs = *(const __attribute__((address_space(4))) float*)(a.cs + (size_t)b * a.cs_bs + g);
-    a.pscore[(size_t)u * a.C + tp.pend_slot] = cs;
+    *(__attribute__((address_space(1))) float*)(a.pscore + (size_t)u * a.C + tp.pend_slot) = cs;
   }
 }
 
@@ -349,8 +374,6 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs& a, int u, int lane
 // immediate offsets (so a tile's 64 loads need no 64-bit addresses).  The
 // descriptor's byte bound applies to the whole offset (vector + scalar +
 // immediate) on gfx950: past it a load returns zeros.
-typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
-
 __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
   const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
   return make_uint4(v.x, v.y, v.z, v.w);
@@ -550,8 +573,8 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a, int item
         // query rows), the operands of the unit's finish
         const uint4* vrow_p = cur.V4 + voff;
         const AuxPtrs ap = aux_ptrs<kWhole, kQA>(a, nxt, nsub, item, lane);
-        qn0 = *(go_next ? ap.p0 : vrow_p);
-        qn1 = *(go_next ? ap.p1 : vrow_p);
+        qn0 = load16(go_next ? ap.p0 : vrow_p);
+        qn1 = load16(go_next ? ap.p1 : vrow_p);
         const int ktile = more ? tile + 1 : nxt.ta;
         const int kcount = more ? cur.count : nxt.count;
         load_k_tile(more ? cur.K4 : nxt.K4, more ? cur.slots : nxt.slots,
@@ -633,8 +656,8 @@ __global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a, int item
     if (!has_next) break;
     if (cur.ta == cur.tb) {  // empty segment: nothing was prefetched for nxt
       const AuxPtrs ap = aux_ptrs<kWhole, kQA>(a, nxt, nsub, item, lane);
-      qn0 = *ap.p0;
-      qn1 = *ap.p1;
+      qn0 = load16(ap.p0);
+      qn1 = load16(ap.p1);
       load_k_tile(nxt.K4, nxt.slots, nxt.count > 0 ? nxt.count - 1 : 0, nxt.ta, lane, false, kr);
     }
     cur = nxt;
