@@ -148,6 +148,7 @@ def _event():
 # 2 flop per multiply-add over 256 dims.
 PREFILL_FLOP_PER_GROUP = 1024 * (1024 + 1024) * 256 * 2 * 2   # 2.147 GFLOP
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+EVENT_EVERY = 8  # headline loop: steps between two steps with per-launch events
 
 
 def bench_prefill(device, seed, batch, blocks):
@@ -437,8 +438,13 @@ def main():
     K = args.steps
     runs = []
     step0 = args.warmup
+    # Per-launch events on every EVENT_EVERY-th step only: each event is a
+    # marker packet on the stream, and events around all 8 launches of
+    # every step cost about 0.9% of the step time on MI355X (measured).
+    sampled = [s for s in range(K) if s % EVENT_EVERY == 0]
     for r in range(max(1, args.repeats)):
-        ev = [[(_event(), _event()) for _ in range(w.L)] for _ in range(K)]
+        ev = [[(_event(), _event()) for _ in range(w.L)] if s % EVENT_EVERY == 0 else None
+              for s in range(K)]
         start, stop = _event(), _event()
         say(f"[bench] timing {K} steps (run {r + 1})")
         admits = 0
@@ -453,7 +459,7 @@ def main():
         wall = time.perf_counter() - t_wall
         step0 += K
         ms_total = start.elapsed_time(stop)
-        dec_ms = [ev[s][l][0].elapsed_time(ev[s][l][1]) for s in range(K) for l in range(w.L)]
+        dec_ms = [ev[s][l][0].elapsed_time(ev[s][l][1]) for s in sampled for l in range(w.L)]
         runs.append({"ms_total": ms_total, "dec_avg_ms": sum(dec_ms) / len(dec_ms),
                      "admits": admits, "admit_ev": admit_ev, "wall": wall})
         say(f"[bench] run {r + 1}: {w.B * K / (ms_total * 1e-3):,.0f} tok/s, decode launch "
@@ -498,6 +504,7 @@ def main():
                      "kernel": "decode_attn_kernel<true, false>: the whole decode step of one layer "
                                "(one launch at this batch)",
                      "avg_launch_ms": round(dec_avg_ms, 5),
+                     "launches_timed": len(sampled) * w.L,
                      "bytes_per_launch": launch_bytes,
                      "kernel_sources_sha": sha},
         "cpu_baseline": None,
