@@ -111,8 +111,9 @@ int make_layout(const rma_config* c, int32_t batch, rma_layout* L) {
   // split-K partials of the decode launch and, for small batches, of the
   // split prefill launch (never both at once: calls on a state are ordered)
   L->scratch_bytes = (uint64_t)batch * c->kv_groups * (sp.ring + sp.bank) * kPart * 4;
-  if (rma::prefill_split(batch, c->kv_groups)) {
-    const uint64_t pf = (uint64_t)batch * c->commit * c->q_heads * rma::kPfSplits * rma::kPfPart * 4;
+  const rma::PrefillPlan pp = rma::prefill_plan(batch, c->kv_groups);
+  if (pp.split()) {
+    const uint64_t pf = (uint64_t)batch * c->commit * c->q_heads * pp.parts() * rma::kPfPart * 4;
     L->scratch_bytes = pf > L->scratch_bytes ? pf : L->scratch_bytes;
   }
   L->scratch = take(L->scratch_bytes);
@@ -228,6 +229,9 @@ rma::PrefillArgs prefill_args(const rma_state* st, int32_t layer, int32_t n_toke
   a.pscore = region<float>(st, L.pscore) + unit0 * C;
   a.part = region<float>(st, L.scratch);
   a.pos = pos;
+  const rma::PrefillPlan plan = rma::prefill_plan(B, G);
+  a.pf_loc = plan.loc;
+  a.pf_bank = plan.bank;
   a.B = B;
   a.G = G;
   a.H = c.q_heads;

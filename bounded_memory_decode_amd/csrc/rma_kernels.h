@@ -88,24 +88,35 @@ struct PrefillArgs {
                            // whose entry is < 0 or not a multiple of C is
                            // left out), or null: every sequence at P
   float* part;             // scratch of the split launch (small batches):
-                           // [B][n][H][kPfSplits][kPfPart]
+                           // [B][n][H][pf_loc + pf_bank][kPfPart]
+  int pf_loc, pf_bank;     // split launch: slices of the local and anchor reads
   int B, G, H, R, N, C;
   int n;                   // tokens in the block (1 .. C)
   int64_t P;               // lockstep: position of the block's first token
   float sl2e;              // scale * log2(e)
 };
 
-// Split prefill launch for small batches: each query row's local read is
-// cut in kPfLocalSplits slices of its tiles and its anchor read in
-// kPfBankSplits, one workgroup per slice, whose partials (o[D], m, l) are
-// merged by a second kernel.  Used iff batch * groups < 32 (fewer than one
-// 32-token workgroup per CU for a full block), a function of the batch
-// only so that the scratch size is known at layout time.
-constexpr int kPfLocalSplits = 2;
-constexpr int kPfBankSplits = 2;
-constexpr int kPfSplits = kPfLocalSplits + kPfBankSplits;
+// Launch plan of a prefill block.  A full block of one (sequence, group)
+// is 8 query tiles of 32 tokens (one 8-wave workgroup each); when the batch
+// gives fewer than 256 such workgroups (one per CU), each query tile's
+// local read is cut in `loc` slices of its tiles and its anchor read in
+// `bank`, one workgroup per slice, whose partials (o[D], m, l) are merged
+// by a second kernel.  A function of the batch only, so that the scratch
+// size is known at layout time.
+constexpr int kPfMaxSplits = 8;
 constexpr int kPfPart = kD + 4;  // floats per partial: o[D], m, l, padding
-inline bool prefill_split(int batch, int groups) { return batch * groups < 32; }
+struct PrefillPlan {
+  int loc, bank;  // slices of the local and anchor reads; 0, 0: no split
+  int parts() const { return loc + bank; }
+  bool split() const { return loc > 0; }
+};
+inline PrefillPlan prefill_plan(int batch, int groups) {
+  const int units = batch * groups;
+  if (units <= 4) return {4, 4};
+  if (units <= 8) return {2, 2};
+  if (units <= 16) return {1, 1};
+  return {0, 0};
+}
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s);
 

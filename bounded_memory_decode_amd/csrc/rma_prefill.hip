@@ -14,7 +14,7 @@
 // The block is a dense contraction, so it runs on MFMA:
 // v_mfma_f32_16x16x32_bf16 (A: lane l holds row l%16, k = 8*(l/16)+j;
 // B: column l%16, same k; D: register i holds row 4*(l/16)+i, column l%16).
-// One workgroup per (sequence, group, tile of 16 or 32 tokens); each wave
+// One 8-wave workgroup per (sequence, group, tile of 32 tokens); each wave
 // owns 16 queries (4 tokens x 4 heads), one per MFMA column, so a lane
 // holds one query throughout.
 //  * Scores are computed transposed, S^T = K Q^T (A = 16 keys x 32 dims of
@@ -27,8 +27,9 @@
 //    the row-major V rows.
 //  * Online softmax in the log2 domain; local and anchor reads separately
 //    normalised, then out = o_local + tanh(q . w_g) * o_anchor.
-//  * Small batches (batch * groups < 32, under one 32-token workgroup per
-//    CU): each read is cut into slices of its tiles, one workgroup per
+//  * Small batches (batch * groups <= 16, where the query tiles alone fill
+//    at most half the CUs): each query tile's local and anchor reads are
+//    cut into slices of their tiles (prefill_plan), one workgroup per
 //    slice, and prefill_merge_kernel merges the slices' partials by their
 //    running maxima and applies the gate.
 #include "rma_kernels.h"
@@ -104,8 +105,8 @@ enum : int { kSegRing = 0, kSegBlock = 1, kSegBank = 2 };
 // 16 + 4 lg + (j - 4) (second sub-tile), which is where the S^T accumulator
 // of lane group lg keeps them; the V^T operand is read in the same order.
 // kSplit (small batches): the workgroup reads one slice of one read, part
-// pr of kPfSplits (the local read cut in kPfLocalSplits slices of its tiles,
-// the anchor read in kPfBankSplits), and writes its unnormalised partial
+// pr of a.pf_loc + a.pf_bank (the local read cut in a.pf_loc slices of its
+// tiles, the anchor read in a.pf_bank), and writes its unnormalised partial
 // (o, running max, sum) per query row to a.part for prefill_merge_kernel.
 template <int kWaves, bool kSplit>
 __global__ __launch_bounds__(64 * kWaves) void prefill_attn_kernel(PrefillArgs a) {
@@ -118,7 +119,8 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_kernel(PrefillArgs a
   // number of such units is a multiple of 8 they are all placed on one XCD
   // (w mod 8 fixed) and share its L2.
   const int nqt = (a.n + kTokWG - 1) / kTokWG;
-  const int units = a.B * a.G * (kSplit ? kPfSplits : 1);
+  const int parts = kSplit ? a.pf_loc + a.pf_bank : 1;
+  const int units = a.B * a.G * parts;
   const int w = blockIdx.x;
   int qt, vu;
   if ((units & 7) == 0) {
@@ -129,9 +131,9 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_kernel(PrefillArgs a
     qt = w % nqt;
     vu = w / nqt;
   }
-  const int u = kSplit ? vu / kPfSplits : vu;
-  const int pr = kSplit ? vu - u * kPfSplits : 0;  // part (kSplit)
-  const bool anchor_part = kSplit && pr >= kPfLocalSplits;
+  const int u = kSplit ? vu / parts : vu;
+  const int pr = kSplit ? vu - u * parts : 0;  // part (kSplit)
+  const bool anchor_part = kSplit && pr >= a.pf_loc;
   const int b = u / a.G, g = u - b * a.G;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int l16 = lane & 15, lg = lane >> 4;  // MFMA column / k-group
@@ -177,12 +179,12 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_kernel(PrefillArgs a
   int ta = 0, tb = t_all;
   if (kSplit) {
     if (anchor_part) {
-      const int i = pr - kPfLocalSplits;
-      ta = t_loc + i * t_bank / kPfBankSplits;
-      tb = t_loc + (i + 1) * t_bank / kPfBankSplits;
+      const int i = pr - a.pf_loc;
+      ta = t_loc + i * t_bank / a.pf_bank;
+      tb = t_loc + (i + 1) * t_bank / a.pf_bank;
     } else {
-      ta = pr * t_loc / kPfLocalSplits;
-      tb = (pr + 1) * t_loc / kPfLocalSplits;
+      ta = pr * t_loc / a.pf_loc;
+      tb = (pr + 1) * t_loc / a.pf_loc;
     }
   }
   // ring age threshold: slot s holds position P - R + age(s), age(s) =
@@ -287,7 +289,7 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_kernel(PrefillArgs a
   // m = -inf, l = 0, o = 0)
   auto write_part = [&](bool empty) {
     if (q_tok < n) {
-      float* dst = a.part + ((((size_t)b * n + q_tok) * a.H + g * kHpg + q_head) * kPfSplits + pr) *
+      float* dst = a.part + ((((size_t)b * n + q_tok) * a.H + g * kHpg + q_head) * parts + pr) *
                                 kPfPart;
 #pragma unroll
       for (int dt = 0; dt < 16; ++dt)
@@ -588,14 +590,19 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillArgs a) {
     if (p < 0 || p % a.C != 0) return;
   }
   const int hq = row % a.H;
-  const float* pp = a.part + (size_t)row * kPfSplits * kPfPart;
-  float4 o[kPfSplits];
-  float m[kPfSplits], l[kPfSplits];
+  const int parts = a.pf_loc + a.pf_bank;
+  const float* pp = a.part + (size_t)row * parts * kPfPart;
+  // every slice's partial is loaded before any is used (one memory round
+  // trip); slices past `parts` read as empty
+  float4 o[kPfMaxSplits];
+  float m[kPfMaxSplits], l[kPfMaxSplits];
 #pragma unroll
-  for (int i = 0; i < kPfSplits; ++i) {
-    o[i] = *reinterpret_cast<const float4*>(pp + i * kPfPart + 4 * lane);
-    m[i] = pp[i * kPfPart + kD];
-    l[i] = pp[i * kPfPart + kD + 1];
+  for (int i = 0; i < kPfMaxSplits; ++i) {
+    const bool on = i < parts;
+    const float* pi = pp + (on ? i : 0) * kPfPart;
+    o[i] = *reinterpret_cast<const float4*>(pi + 4 * lane);
+    m[i] = on ? pi[kD] : -INFINITY;
+    l[i] = on ? pi[kD + 1] : 0.f;
   }
   const uint16_t* qsrc = a.qa != nullptr ? a.qa : a.q;
   const uint2 qv = *reinterpret_cast<const uint2*>(qsrc + (size_t)row * kD + 4 * lane);
@@ -612,12 +619,12 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillArgs a) {
   auto merge = [&](int i0, int i1) {
     float M = -INFINITY;
 #pragma unroll
-    for (int i = 0; i < kPfSplits; ++i)
+    for (int i = 0; i < kPfMaxSplits; ++i)
       if (i >= i0 && i < i1) M = fmaxf(M, m[i]);
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     float L = 0.f;
 #pragma unroll
-    for (int i = 0; i < kPfSplits; ++i) {
+    for (int i = 0; i < kPfMaxSplits; ++i) {
       if (i < i0 || i >= i1) continue;
       const float e = m[i] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m[i] - M);
       acc.x = fmaf(e, o[i].x, acc.x);
@@ -629,8 +636,8 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillArgs a) {
     const float inv = L > 0.f ? 1.f / L : 0.f;
     return make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
   };
-  const float4 ol = merge(0, kPfLocalSplits);
-  const float4 oa = merge(kPfLocalSplits, kPfSplits);
+  const float4 ol = merge(0, a.pf_loc);
+  const float4 oa = merge(a.pf_loc, parts);
   uint16_t* orow = a.out + (size_t)row * kD + 4 * lane;
   *reinterpret_cast<uint2*>(orow) = make_uint2(pack_bf16(fmaf(gate, oa.x, ol.x), fmaf(gate, oa.y, ol.y)),
                                                pack_bf16(fmaf(gate, oa.z, ol.z), fmaf(gate, oa.w, ol.w)));
@@ -639,22 +646,20 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillArgs a) {
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
-  // 8-wave workgroups (32 tokens: twice the reuse of every staged tile)
-  // when that still gives a workgroup per CU; else 4-wave ones
+  // 8-wave workgroups (32 tokens: twice the reuse of every staged tile);
+  // small batches split each query tile's reads into slices (a.pf_loc,
+  // a.pf_bank from prefill_plan)
   const int units = a.B * a.G;
   const int tiles8 = (a.n + 31) / 32;
-  const int tiles4 = (a.n + 15) / 16;
-  if (prefill_split(a.B, a.G)) {
-    hipLaunchKernelGGL((prefill_attn_kernel<4, true>), dim3(tiles4 * units * kPfSplits), dim3(256),
-                       0, s, a);
+  if (a.pf_loc > 0) {
+    hipLaunchKernelGGL((prefill_attn_kernel<8, true>),
+                       dim3(tiles8 * units * (a.pf_loc + a.pf_bank)), dim3(512), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int rows = a.B * a.n * a.H;
     hipLaunchKernelGGL(prefill_merge_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, a);
-  } else if ((int64_t)tiles8 * units >= 256) {
-    hipLaunchKernelGGL((prefill_attn_kernel<8, false>), dim3(tiles8 * units), dim3(512), 0, s, a);
   } else {
-    hipLaunchKernelGGL((prefill_attn_kernel<4, false>), dim3(tiles4 * units), dim3(256), 0, s, a);
+    hipLaunchKernelGGL((prefill_attn_kernel<8, false>), dim3(tiles8 * units), dim3(512), 0, s, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

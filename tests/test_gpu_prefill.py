@@ -150,18 +150,22 @@ def test_long_prompt_start_eight_layers():
 
 
 @pytest.mark.parametrize("n", [256, 60])
-def test_batch8_launch_paths(n):
-    """Batch 8, above the small-batch split: a full block takes the 8-wave
-    kernel, a 60-token block the 4-wave one.  Sequences at their own
+@pytest.mark.parametrize("B", [2, 4, 8])
+def test_launch_plans(B, n):
+    """The launch plans above batch 1: batch 2 splits each query tile's
+    local and anchor reads in 2 slices each, batch 4 in 1 each (one
+    workgroup per read), batch 8 runs unsplit; a full block and a 60-token
+    one (its last query tile partial).  Sequences at their own
     block-aligned positions (per-sequence call); two sampled sequences (a
-    full history and an empty one) against one-sequence oracles, outputs
-    and state."""
+    full history and an empty or short one) against one-sequence oracles,
+    outputs and state."""
     from test_gpu_positions import _rows, _seq_oracles
-    gu.log(f"case prefill batch 8, n={n}")
+    gu.log(f"case prefill batch {B}, n={n}")
     base = synth.WORKLOADS["layer_b1"]
     specs = [(32768, 1024), (33024, 700), (256, 0), (1024, 1024), (32768, 512), (0, 0),
              (4096, 1000), (768, 64)]
-    sampled = (0, 5)
+    specs = specs[:B] if B >= 6 else [specs[0], specs[5], specs[1], specs[7]][:B]
+    sampled = (0, 5) if B >= 6 else (0, 1)
     seed = 56
     states, oracles = _seq_oracles(base, specs, seed)
     w = base.with_(B=len(specs))
@@ -179,7 +183,7 @@ def test_batch8_launch_paths(n):
         ref = o.prefill_block(0, xb["q"], xb["k"], xb["v"], xb["ck"], xb["cv"], xb["cs"], wg[0])
         if o.pend_n[0] == o.C:
             o.admit(0)
-        gu.check_out(out[b:b + 1], ref, f"batch 8 prefill n={n} sequence {b}", p_bf16_vmax=vm)
+        gu.check_out(out[b:b + 1], ref, f"batch {B} prefill n={n} sequence {b}", p_bf16_vmax=vm)
     torch.cuda.synchronize()
     for b in sampled:
-        gu.check_seq_state(S, b, oracles[b], f"batch 8 prefill n={n}")
+        gu.check_seq_state(S, b, oracles[b], f"batch {B} prefill n={n}")
