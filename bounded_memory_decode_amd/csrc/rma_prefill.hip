@@ -526,15 +526,15 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_kernel(PrefillArgs a
 
 // The block's writes, after every query of the block has read the ring:
 // token j goes to ring slot (P + j) mod R and pending slot (P + j) mod C.
-// grid: (ceil(n / 8), units); block: 256, 8 tokens of one unit.  V,
+// Workgroup (bx, u) of (ceil(n / 8), units): 256 threads, 8 tokens of one unit.  V,
 // pending and score rows are row-contiguous and copied directly; ring K is
 // chunk-major, so the 8 K rows pass through LDS and each chunk plane gets
 // 8 consecutive slots (128 bytes, contiguous up to the wrap at R) per
 // store instead of 16-byte pieces from separate workgroups.  (64 tokens per
 // workgroup left too few workgroups at small batches.)
 constexpr int kCommitTok = 8;
-__global__ __launch_bounds__(256) void prefill_commit_kernel(PrefillArgs a) {
-  const int j0 = blockIdx.x * kCommitTok, u = blockIdx.y;
+__device__ __forceinline__ void commit_tokens(const PrefillArgs& a, int bx, int u) {
+  const int j0 = bx * kCommitTok;
   const int b = u / a.G, g = u - b * a.G;
   const int tid = threadIdx.x;
   int64_t P = a.P;
@@ -574,13 +574,17 @@ __global__ __launch_bounds__(256) void prefill_commit_kernel(PrefillArgs a) {
   }
 }
 
-// Merge of the split launch.  grid: ceil(B n H / 4); block: 256 = 4 waves,
-// one query row (sequence, token, head) per wave, lane = dims 4 lane ..
+__global__ __launch_bounds__(256) void prefill_commit_kernel(PrefillArgs a) {
+  commit_tokens(a, blockIdx.x, blockIdx.y);
+}
+
+// Merge of the split launch, workgroup bx of ceil(B n H / 4): 4 waves, one
+// query row (sequence, token, head) per wave, lane = dims 4 lane ..
 // 4 lane + 3.  The local slices and the anchor slices are each merged by
 // their running maxima, then out = o_local + tanh(qa . w_g) * o_anchor (an
 // empty bank reads as zero).
-__global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillArgs a) {
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);  // (b, token, head)
+__device__ __forceinline__ void merge_rows(const PrefillArgs& a, int bx) {
+  const int row = bx * 4 + (threadIdx.x >> 6);  // (b, token, head)
   const int lane = threadIdx.x & 63;
   const int rows = a.B * a.n * a.H;
   if (row >= rows) return;
@@ -643,6 +647,20 @@ __global__ __launch_bounds__(256) void prefill_merge_kernel(PrefillArgs a) {
                                                pack_bf16(fmaf(gate, oa.z, ol.z), fmaf(gate, oa.w, ol.w)));
 }
 
+// After the split attention kernel, one launch for both: workgroups
+// [0, merge_wgs) merge query rows, the rest commit the block's tokens (the
+// two touch disjoint memory, and both must follow every read of the ring).
+__global__ __launch_bounds__(256) void prefill_merge_commit_kernel(PrefillArgs a, int merge_wgs,
+                                                                   int commit_x) {
+  const int w = blockIdx.x;
+  if (w < merge_wgs) {
+    merge_rows(a, w);
+  } else {
+    const int c = w - merge_wgs;
+    commit_tokens(a, c % commit_x, c / commit_x);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
@@ -656,14 +674,16 @@ hipError_t launch_prefill(const PrefillArgs& a, hipStream_t s) {
                        dim3(tiles8 * units * (a.pf_loc + a.pf_bank)), dim3(512), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int rows = a.B * a.n * a.H;
-    hipLaunchKernelGGL(prefill_merge_kernel, dim3((rows + 3) / 4), dim3(256), 0, s, a);
-  } else {
-    hipLaunchKernelGGL((prefill_attn_kernel<8, false>), dim3(tiles8 * units), dim3(512), 0, s, a);
+    const int merge_wgs = (a.B * a.n * a.H + 3) / 4;
+    const int commit_x = (a.n + kCommitTok - 1) / kCommitTok;
+    hipLaunchKernelGGL(prefill_merge_commit_kernel, dim3(merge_wgs + commit_x * units), dim3(256),
+                       0, s, a, merge_wgs, commit_x);
+    return hipGetLastError();
   }
+  hipLaunchKernelGGL((prefill_attn_kernel<8, false>), dim3(tiles8 * units), dim3(512), 0, s, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(prefill_commit_kernel, dim3((a.n + kCommitTok - 1) / kCommitTok, a.B * a.G),
+  hipLaunchKernelGGL(prefill_commit_kernel, dim3((a.n + kCommitTok - 1) / kCommitTok, units),
                      dim3(256), 0, s, a);
   return hipGetLastError();
 }
