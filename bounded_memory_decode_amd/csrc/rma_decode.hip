@@ -993,13 +993,19 @@ int resident_workgroups() {
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
-  // Whole-unit launch when there is at least one unit per resident wave and
-  // the last round of units leaves at most 1/8 of the waves idle.
+  // Whole-unit launch when the last round of units (the only one, below
+  // one unit per resident wave) occupies at least 5/8 of the waves; else
+  // the split launch.  Measured on MI355X (1,024 waves, 1 layer, per token):
+  // whole-unit wins from batch 160 (640 units: 237 against 250 us) up to
+  // 255, and at batch 448 (a last round of 768: 649 against 673 us); the
+  // split wins at batch 128 (512 units: 194 against 210 us) and 288-384
+  // (last rounds of 128-512 units).
   const bool qa = a.qa != nullptr;
   const int res_whole = qa ? resident_workgroups<true, true>() : resident_workgroups<true, false>();
   const int waves = res_whole * kWaves;
   const int rounds = (a.units + waves - 1) / waves;
-  if (a.units >= waves && (int64_t)(rounds * waves - a.units) * 8 <= a.units) {
+  const int last = a.units - (rounds - 1) * waves;
+  if ((int64_t)last * 8 >= (int64_t)waves * 5) {
     int grid = (a.units + kWaves - 1) / kWaves;
     if (grid > res_whole) grid = res_whole;
     if (qa)
