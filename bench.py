@@ -501,7 +501,7 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": traffic,
-                     "kernel": "decode_attn_kernel<true, false>: the whole decode step of one layer "
+                     "kernel": "decode_attn_kernel<true, false, 1>: the whole decode step of one layer "
                                "(one launch at this batch)",
                      "avg_launch_ms": round(dec_avg_ms, 5),
                      "launches_timed": len(sampled) * w.L,

@@ -149,7 +149,7 @@ __device__ __forceinline__ uint16_t to_bf16(float f) {
   return (uint16_t)(u >> 16);
 }
 
-constexpr int kWaves = 4;
+constexpr int kWaves = 4;  // waves per workgroup of the split launch's persistent kernel
 
 // Where the token of sequence b sits: the valid ring slots (positions
 // max(0, t-R) .. t-1), the ring slot and pending slot it writes, and
@@ -430,21 +430,21 @@ __device__ __forceinline__ void load_k_tile(const uint4* base, int slots, int hi
 // load_k_tile as the A operand, the 4 query rows as B columns, repeated
 // over the 16 columns); P.V runs on the vector ALU, a half-wave per key
 // and 8 dims per lane, on V rows as stored.
-template <bool kWhole, bool kQA>
-__global__ __launch_bounds__(256) void decode_attn_kernel(DecodeArgs a, int items) {
+template <bool kWhole, bool kQA, int kW>
+__global__ __launch_bounds__(64 * kW) void decode_attn_kernel(DecodeArgs a, int items) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
-  const int W = gridDim.x * kWaves;
-  int item = blockIdx.x * kWaves + wave;
+  const int W = gridDim.x * kW;
+  int item = blockIdx.x * kW + wave;
   if (item >= items) return;
   int sub = 0;
 
-  __shared__ uint4 q_s[kWaves][kHpg * kChunks];  // each wave's 4 query rows
-  __shared__ uint4 qa_s[kQA ? kWaves : 1][kHpg * kChunks];  // anchor query rows (kQA)
+  __shared__ uint4 q_s[kW][kHpg * kChunks];  // each wave's 4 query rows
+  __shared__ uint4 qa_s[kQA ? kW : 1][kHpg * kChunks];  // anchor query rows (kQA)
   // per-key probabilities of the 4 heads, then a pad that takes the stores
   // of the lanes that hold copies (no branch)
-  __shared__ float4 p_s[kWaves][2 * kTile];
-  __shared__ float or_s[kWhole ? kWaves : 1][kHpg * kD];  // ring result
+  __shared__ float4 p_s[kW][2 * kTile];
+  __shared__ float or_s[kWhole ? kW : 1][kHpg * kD];  // ring result
 
   const int half = lane >> 5, c32 = lane & 31;
   const int l16 = lane & 15, lg = lane >> 4;
@@ -972,7 +972,7 @@ __global__ void seq_bank_n_kernel(int32_t* bank_n, int L, int B, int G, int firs
 
 // Workgroups of a kernel that are resident at once on the current device
 // (CUs x workgroups per CU), computed once per device.
-template <bool kWhole, bool kQA>
+template <bool kWhole, bool kQA, int kW>
 int resident_workgroups() {
   static int cached[64] = {0};
   int dev = 0;
@@ -981,13 +981,23 @@ int resident_workgroups() {
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_attn_kernel<kWhole, kQA>,
-                                                     256, 0) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_attn_kernel<kWhole, kQA, kW>,
+                                                     64 * kW, 0) != hipSuccess ||
         per_cu < 1)
       per_cu = 1;
     cached[dev] = cus * per_cu;
   }
   return cached[dev];
+}
+
+template <bool kQA, int kW>
+hipError_t launch_whole(const DecodeArgs& a, hipStream_t s) {
+  int grid = (a.units + kW - 1) / kW;
+  const int res = resident_workgroups<true, kQA, kW>();
+  if (grid > res) grid = res;
+  hipLaunchKernelGGL((decode_attn_kernel<true, kQA, kW>), dim3(grid), dim3(64 * kW), 0, s, a,
+                     a.units);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -997,22 +1007,22 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   // one unit per resident wave) occupies at least 5/8 of the waves; else
   // the split launch.  Measured on MI355X (1,024 waves, 1 layer, per token):
   // whole-unit wins from batch 160 (640 units: 237 against 250 us) up to
-  // 255, and at batch 448 (a last round of 768: 649 against 673 us); the
-  // split wins at batch 128 (512 units: 194 against 210 us) and 288-384
-  // (last rounds of 128-512 units).
+  // 255, and at batch 448 (a last round of 768: 637-649 against 673 us);
+  // the split wins at batch 128 (512 units: 194 against 210 us) and
+  // 288-384 (last rounds of 128-512 units).  With at least one unit per
+  // wave, one-wave workgroups (the dispatcher then places every wave on its
+  // own): 704 against 713 us per launch at batch 512, 637 against 651 at
+  // 448; below that, four-wave ones, which fill fewer CUs completely (237
+  // against 241 us at batch 160, 272 against 281 at 192).
   const bool qa = a.qa != nullptr;
-  const int res_whole = qa ? resident_workgroups<true, true>() : resident_workgroups<true, false>();
-  const int waves = res_whole * kWaves;
+  const int waves = kWaves * (qa ? resident_workgroups<true, true, kWaves>()
+                                 : resident_workgroups<true, false, kWaves>());
   const int rounds = (a.units + waves - 1) / waves;
   const int last = a.units - (rounds - 1) * waves;
   if ((int64_t)last * 8 >= (int64_t)waves * 5) {
-    int grid = (a.units + kWaves - 1) / kWaves;
-    if (grid > res_whole) grid = res_whole;
-    if (qa)
-      hipLaunchKernelGGL((decode_attn_kernel<true, true>), dim3(grid), dim3(256), 0, s, a, a.units);
-    else
-      hipLaunchKernelGGL((decode_attn_kernel<true, false>), dim3(grid), dim3(256), 0, s, a, a.units);
-    hipError_t e = hipGetLastError();
+    const bool full = a.units >= waves;
+    hipError_t e = qa ? (full ? launch_whole<true, 1>(a, s) : launch_whole<true, kWaves>(a, s))
+                      : (full ? launch_whole<false, 1>(a, s) : launch_whole<false, kWaves>(a, s));
     if (e != hipSuccess || a.pos == nullptr) return e;
     // per-sequence positions: admit the units whose block this token ends
     AdmitArgs ad;
@@ -1041,9 +1051,10 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
     hipLaunchKernelGGL(decode_part_kernel, dim3(items), dim3(64), 0, s, a);
   } else {
     int grid = (items + kWaves - 1) / kWaves;
-    const int res = resident_workgroups<false, false>();
+    const int res = resident_workgroups<false, false, kWaves>();
     if (grid > res) grid = res;
-    hipLaunchKernelGGL((decode_attn_kernel<false, false>), dim3(grid), dim3(256), 0, s, a, items);
+    hipLaunchKernelGGL((decode_attn_kernel<false, false, kWaves>), dim3(grid), dim3(64 * kWaves), 0,
+                       s, a, items);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
