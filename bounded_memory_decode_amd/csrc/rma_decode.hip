@@ -1004,25 +1004,31 @@ hipError_t launch_whole(const DecodeArgs& a, hipStream_t s) {
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   // Whole-unit launch when the last round of units (the only one, below
-  // one unit per resident wave) occupies at least 5/8 of the waves; else
-  // the split launch.  Measured on MI355X (1,024 waves, 1 layer, per token):
-  // whole-unit wins from batch 160 (640 units: 237 against 250 us) up to
-  // 255, and at batch 448 (a last round of 768: 637-649 against 673 us);
-  // the split wins at batch 128 (512 units: 194 against 210 us) and
-  // 288-384 (last rounds of 128-512 units).  With at least one unit per
-  // wave, one-wave workgroups (the dispatcher then places every wave on its
-  // own): 704 against 713 us per launch at batch 512, 637 against 651 at
-  // 448; below that, four-wave ones, which fill fewer CUs completely (237
-  // against 241 us at batch 160, 272 against 281 at 192).
+  // one unit per resident wave) occupies at least 5/8 of the waves, or a
+  // single round at least 3/8; else the split launch.  Measured on MI355X
+  // (1,024 waves, 1 layer, per token): whole-unit wins from batch 96 (384
+  // units) up to 255 (at 144: 232 against 243 us; at 160: 237 against
+  // 250) and at batch 448 (a last round of 768: 637-649 against 673 us);
+  // the split wins at batch 64 (101 against 130 us) and 288-384 (last
+  // rounds of 128-512 units).  With at least one unit per wave, one-wave
+  // workgroups (704 against 713 us per launch at batch 512, 637 against
+  // 651 at 448); for a single round of 5/8 or more, four-wave ones, which
+  // fill fewer CUs completely (237 against 241 us at batch 160, 272
+  // against 281 at 192); below 5/8, one-wave ones again (232 against 240
+  // at 144).
   const bool qa = a.qa != nullptr;
   const int waves = kWaves * (qa ? resident_workgroups<true, true, kWaves>()
                                  : resident_workgroups<true, false, kWaves>());
   const int rounds = (a.units + waves - 1) / waves;
   const int last = a.units - (rounds - 1) * waves;
-  if ((int64_t)last * 8 >= (int64_t)waves * 5) {
-    const bool full = a.units >= waves;
-    hipError_t e = qa ? (full ? launch_whole<true, 1>(a, s) : launch_whole<true, kWaves>(a, s))
-                      : (full ? launch_whole<false, 1>(a, s) : launch_whole<false, kWaves>(a, s));
+  const bool wide = (int64_t)last * 8 >= (int64_t)waves * 5;  // last round >= 5/8 of the waves
+  const bool mid = rounds == 1 && (int64_t)last * 8 >= (int64_t)waves * 3;  // one round >= 3/8
+  if (wide || mid) {
+    // one-wave workgroups with at least one unit per wave, and for a
+    // single round of 3/8 to 5/8 of the waves; four-wave ones above 5/8
+    const bool one = a.units >= waves || !wide;
+    hipError_t e = qa ? (one ? launch_whole<true, 1>(a, s) : launch_whole<true, kWaves>(a, s))
+                      : (one ? launch_whole<false, 1>(a, s) : launch_whole<false, kWaves>(a, s));
     if (e != hipSuccess || a.pos == nullptr) return e;
     // per-sequence positions: admit the units whose block this token ends
     AdmitArgs ad;
