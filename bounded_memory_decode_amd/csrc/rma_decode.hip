@@ -10,8 +10,9 @@
 //   * split, multi-tile parts (middling batch): reads are cut into parts of
 //     whole 64-key tiles taken by the same persistent kernel; partials go
 //     to scratch and a combine kernel finishes the token;
-//   * split, one-tile parts (small batch): one wave per 64-key tile in
-//     decode_part_kernel (all loads at once, scores on MFMA), then the
+//   * split, one-tile parts (small batch): one four-wave workgroup per
+//     64-key tile in decode_part_kernel (all loads at once, a 16-key block
+//     per wave, scores on MFMA), then the
 //     combine kernel.
 // Positions come from the lockstep arguments or, per sequence, from a
 // device array (TokPos); with per-sequence positions a completed block is
@@ -667,126 +668,102 @@ __global__ __launch_bounds__(64 * kW) void decode_attn_kernel(DecodeArgs a, int 
 }
 
 
-// Loads of one 64-key tile for decode_part_kernel:
-//   K, MFMA A layout: block kb, k-step st = chunk 4 st + l / 16 of key
-//     64 tile + 16 kb + l % 16; bound = the plane.  Keys past the count
-//     read stale slots (their scores are masked).
-//   V rows: key 64 tile + 2 j + half, chunk c32; bound = count rows, so
-//     keys past the count read zeros.
-__device__ __forceinline__ void part_load_k(const Seg& sg, int tile, int lane, uint4 (&kr)[32]) {
-  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)sg.K4, (short)0, sg.slots * kChunks * 16, kBufWord3);
-  const uint32_t v0 = (uint32_t)(((lane >> 4) * sg.slots + tile * kTile + (lane & 15)) * 16);
-#pragma unroll
-  for (int st = 0; st < 8; ++st)
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-      kr[8 * kb + st] = buf_load16(r, v0 + kb * 256, (uint32_t)(4 * st * sg.slots * 16));
-}
-
-__device__ __forceinline__ void part_load_v(const Seg& sg, int tile, int lane,
-                                            uint4 (&vr)[kTile / 2]) {
-  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)sg.V4, (short)0, sg.count * kChunks * 16, kBufWord3);
-  const uint32_t v0 = (uint32_t)(((tile * kTile + (lane >> 5)) * kChunks + (lane & 31)) * 16);
-#pragma unroll
-  for (int j = 0; j < kTile / 2; ++j)
-    vr[j] = buf_load16(r, v0 + (j & 3) * 1024, (uint32_t)((j >> 2) * 4096));
-}
-
 // Attention of the split launch when every part is one 64-key tile
-// (small batches).  grid: items; block: one wave, one part (item = unit *
-// S + r: tile r of the unit's ring for r < splits_ring, else tile
+// (small batches).  grid: items; block: 256 = 4 waves, one part (item =
+// unit * S + r: tile r of the unit's ring for r < splits_ring, else tile
 // r - splits_ring of its bank), writing the part's partial (o[4][256],
-// m[4], l[4]) for the combine kernel.  One wave per workgroup spreads a
-// small launch over as many CUs as it has parts.
+// m[4], l[4]) for the combine kernel.
 //
-// Latency first: the part's query rows and its K and V are all loaded at
-// the start, so the part costs one memory round trip.  Scores on the
-// matrix cores, per 16-key block kb: S^T (16 keys x 16 columns) = K Q^T
-// with v_mfma_f32_16x16x32_bf16, A = 16 keys x 32 dims (lane l: key
-// l % 16, chunk 4 st + l / 16 of k-step st), B = Q^T (lane l: query row
+// Latency first: wave w takes the part's 16-key block w, loads its query
+// rows, its K and its V rows all at once (one memory round trip; raw
+// buffer loads: a wave-uniform descriptor per plane, the k-step or row in
+// the immediate and scalar offsets, and the descriptor's byte bound, which
+// on gfx950 applies to the whole offset, returns zeros for V rows past the
+// count), then computes that block's scores, softmax and P.V; the four
+// blocks' (m, l, o) are merged in LDS into the part's partial.  Scores on
+// the matrix cores: S^T (16 keys x 16 columns) = K Q^T with
+// v_mfma_f32_16x16x32_bf16, A = 16 keys x 32 dims (lane l: key l % 16,
+// chunk 4 st + l / 16 of k-step st), B = Q^T (lane l: query row
 // (l % 16) mod 4, same chunk; columns 4-15 repeat rows 0-3 and are
-// ignored); accumulator register r of lane l then holds key 4 (l / 16) + r
-// of the block for query l % 16.  P.V on the vector ALU as in the
-// whole-unit kernel: a half-wave per key, 8 dims per lane, on V rows as
-// stored.
-__global__ __launch_bounds__(64) void decode_part_kernel(DecodeArgs a) {
-  const int lane = threadIdx.x;
+// ignored).  P.V on the vector ALU as in the whole-unit kernel: a half-wave
+// per key, 8 dims per lane, on V rows as stored.  Four waves per part
+// rather than one take a quarter of the loads and of the P.V each, which
+// shortens the part's chain (batch 1: 91 against 102 us per 8-layer token
+// as a graph replay).
+__global__ __launch_bounds__(256) void decode_part_kernel(DecodeArgs a) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // 16-key block of the tile
   const int item = blockIdx.x;
-  // per-key probabilities of the 4 heads (float4 per key), then a pad that
-  // takes the stores of lanes without a real query (no branch)
-  __shared__ float4 p_s[kTile + 4];
+  __shared__ float4 p_s[4][20];            // per wave: 16 keys' probabilities, then a pad
+  __shared__ float o_s[4][kHpg * kD];      // per wave: its block's o
+  __shared__ float ml_s[4][2 * kHpg];      // per wave: its block's m and l of each head
   const Seg sg = seg_of<false>(a, item, 0);
   const int l16 = lane & 15, lg = lane >> 4;
   const int half = lane >> 5, c32 = lane & 31;
   float* P = a.part + (size_t)item * kPart;
 
   if (sg.ta == sg.tb) {  // nothing to read: m = -inf, l = 0, o = 0
-    if (lane < 32) {
-#pragma unroll
-      for (int h = 0; h < kHpg; ++h) {
-        float4* dst = reinterpret_cast<float4*>(P + h * kD + 8 * c32);
-        dst[0] = make_float4(0.f, 0.f, 0.f, 0.f);
-        dst[1] = make_float4(0.f, 0.f, 0.f, 0.f);
-      }
-    }
-    if (lane < kHpg) {
-      P[kHpg * kD + lane] = -INFINITY;
-      P[kHpg * kD + kHpg + lane] = 0.f;
+    const int h = w;
+    reinterpret_cast<float4*>(P + h * kD)[lane] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (lane == 0) {
+      P[kHpg * kD + h] = -INFINITY;
+      P[kHpg * kD + kHpg + h] = 0.f;
     }
     return;
   }
   const int tile = sg.ta;
 
-  uint4 qb[8];          // B operands (Q^T), k-step st
-  uint4 kr[4 * 8];      // A operands: block kb, k-step st at kr[8 kb + st]
-  uint4 vr[kTile / 2];  // V rows: key 2 j + half, chunk c32
+  uint4 qb[8];  // B operands (Q^T), k-step st
+  uint4 kr[8];  // A operands of block w, k-step st
+  uint4 vr[8];  // V rows: key 16 w + 2 j + half, chunk c32
 #pragma unroll
   for (int st = 0; st < 8; ++st) qb[st] = sg.q4[(l16 & 3) * kChunks + 4 * st + lg];
-  part_load_k(sg, tile, lane, kr);
-  part_load_v(sg, tile, lane, vr);
+  {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)sg.K4, (short)0, sg.slots * kChunks * 16, kBufWord3);
+    const uint32_t v0 = (uint32_t)((lg * sg.slots + tile * kTile + 16 * w + l16) * 16);
+#pragma unroll
+    for (int st = 0; st < 8; ++st) kr[st] = buf_load16(r, v0, (uint32_t)(4 * st * sg.slots * 16));
+  }
+  {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)sg.V4, (short)0, sg.count * kChunks * 16, kBufWord3);
+    const uint32_t v0 = (uint32_t)(((tile * kTile + 16 * w + half) * kChunks + c32) * 16);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) vr[j] = buf_load16(r, v0 + j * 1024, 0u);
+  }
   __builtin_amdgcn_sched_barrier(0);
 
-  f32x4_t s[4];
+  // scores: register r of lane l holds key 16 w + 4 (l / 16) + r for query
+  // l % 16 (columns 4-15 repeat rows 0-3)
+  f32x4_t sc = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb) {
-    s[kb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int st = 0; st < 8; ++st)
-      s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[8 * kb + st]),
-                                                      as_bf16x8(qb[st]), s[kb], 0, 0, 0);
-  }
-  __builtin_amdgcn_sched_barrier(0);  // scores before anything of P.V
+  for (int st = 0; st < 8; ++st)
+    sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(kr[st]), as_bf16x8(qb[st]), sc, 0, 0, 0);
+  __builtin_amdgcn_sched_barrier(0);
 
-  // softmax of query l16 (log2 domain) over this lane's 16 keys, then over
-  // the 4 lanes l16 + 16 lg; only the lanes of queries 0-3 store
-  const int kbase = tile * kTile + 4 * lg;
+  // the block's softmax (log2 domain); a block past the count has m = -inf
+  const int kbase = tile * kTile + 16 * w + 4 * lg;
   float mt = -INFINITY;
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float v = kbase + kb * 16 + r < sg.count ? s[kb][r] * a.sl2e : -INFINITY;
-      s[kb][r] = v;
-      mt = fmaxf(mt, v);
-    }
+  for (int r = 0; r < 4; ++r) {
+    sc[r] = kbase + r < sg.count ? sc[r] * a.sl2e : -INFINITY;
+    mt = fmaxf(mt, sc[r]);
+  }
   mt = fmaxf(mt, __shfl_xor(mt, 16, 64));
-  mt = fmaxf(mt, __shfl_xor(mt, 32, 64));  // > -inf: the tile's first key is valid
+  mt = fmaxf(mt, __shfl_xor(mt, 32, 64));
+  const float mref = mt == -INFINITY ? 0.f : mt;
   float ps = 0.f;
 #pragma unroll
-  for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const float p = fast_exp2(s[kb][r] - mt);
-      ps += p;
-      const int key = l16 < kHpg ? kb * 16 + 4 * lg + r : kTile;
-      reinterpret_cast<float*>(&p_s[key])[l16 & 3] = p;
-    }
+  for (int r = 0; r < 4; ++r) {
+    const float p = fast_exp2(sc[r] - mref);
+    ps += p;
+    const int key = l16 < kHpg ? 4 * lg + r : 16;
+    reinterpret_cast<float*>(&p_s[w][key])[l16 & 3] = p;
+  }
   ps += __shfl_xor(ps, 16, 64);
   ps += __shfl_xor(ps, 32, 64);
   __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_sched_barrier(0);
 
   float acc[kHpg][8];
 #pragma unroll
@@ -794,9 +771,9 @@ __global__ __launch_bounds__(64) void decode_part_kernel(DecodeArgs a) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) acc[h][i] = 0.f;
 #pragma unroll
-  for (int j = 0; j < kTile / 2; ++j) {
+  for (int j = 0; j < 8; ++j) {
     const uint4 vv = vr[j];
-    const float4 pp = p_s[2 * j + half];
+    const float4 pp = p_s[w][2 * j + half];
     const float x[8] = {bf_lo(vv.x), bf_hi(vv.x), bf_lo(vv.y), bf_hi(vv.y),
                         bf_lo(vv.z), bf_hi(vv.z), bf_lo(vv.w), bf_hi(vv.w)};
 #pragma unroll
@@ -807,8 +784,6 @@ __global__ __launch_bounds__(64) void decode_part_kernel(DecodeArgs a) {
       acc[3][i] = fmaf(pp.w, x[i], acc[3][i]);
     }
   }
-
-  // the partial: o over the two half-waves
 #pragma unroll
   for (int h = 0; h < kHpg; ++h)
 #pragma unroll
@@ -816,14 +791,41 @@ __global__ __launch_bounds__(64) void decode_part_kernel(DecodeArgs a) {
   if (lane < 32) {
 #pragma unroll
     for (int h = 0; h < kHpg; ++h) {
-      float4* dst = reinterpret_cast<float4*>(P + h * kD + 8 * c32);
+      float4* dst = reinterpret_cast<float4*>(&o_s[w][h * kD + 8 * c32]);
       dst[0] = make_float4(acc[h][0], acc[h][1], acc[h][2], acc[h][3]);
       dst[1] = make_float4(acc[h][4], acc[h][5], acc[h][6], acc[h][7]);
     }
   }
-  if (lane < kHpg) {
-    P[kHpg * kD + lane] = mt;
-    P[kHpg * kD + kHpg + lane] = ps;
+  if (lane < kHpg) {  // lane h holds head h's m and l
+    ml_s[w][lane] = mt;
+    ml_s[w][kHpg + lane] = ps;
+  }
+  __syncthreads();
+
+  // merge of the four blocks: wave h takes head h, lane dims 4 lane .. 4 lane + 3
+  const int h = w;
+  float mb[4], M = -INFINITY;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    mb[b] = ml_s[b][h];
+    M = fmaxf(M, mb[b]);
+  }
+  float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+  float L = 0.f;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const float e = mb[b] == -INFINITY ? 0.f : fast_exp2(mb[b] - M);
+    const float4 ob = reinterpret_cast<const float4*>(&o_s[b][h * kD])[lane];
+    o.x = fmaf(e, ob.x, o.x);
+    o.y = fmaf(e, ob.y, o.y);
+    o.z = fmaf(e, ob.z, o.z);
+    o.w = fmaf(e, ob.w, o.w);
+    L = fmaf(e, ml_s[b][kHpg + h], L);
+  }
+  reinterpret_cast<float4*>(P + h * kD)[lane] = o;
+  if (lane == 0) {
+    P[kHpg * kD + h] = M;
+    P[kHpg * kD + kHpg + h] = L;
   }
 }
 
@@ -1054,7 +1056,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   const int S = a.splits_ring + a.splits_bank;
   const int items = a.units * S;
   if (a.tiles_ring == 1 && a.tiles_bank == 1) {  // one tile per part
-    hipLaunchKernelGGL(decode_part_kernel, dim3(items), dim3(64), 0, s, a);
+    hipLaunchKernelGGL(decode_part_kernel, dim3(items), dim3(256), 0, s, a);
   } else {
     int grid = (items + kWaves - 1) / kWaves;
     const int res = resident_workgroups<false, false, kWaves>();
