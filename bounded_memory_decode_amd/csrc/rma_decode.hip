@@ -2,18 +2,19 @@
 // the local ring and over the committed anchor bank, the signed gate that
 // merges the two reads, the ring write and the pending append.
 //
-// Three launch shapes:
-//   * whole-unit (large batch): a wave of the persistent, wave-pipelined
-//     attention kernel owns a (sequence, group) unit, reads its ring then
-//     its bank, and finishes the token in-wave (current token, gate,
-//     output, ring write, pending append): one launch;
-//   * split, multi-tile parts (middling batch): reads are cut into parts of
-//     whole 64-key tiles taken by the same persistent kernel; partials go
-//     to scratch and a combine kernel finishes the token;
-//   * split, one-tile parts (small batch): one four-wave workgroup per
+// Three launch shapes (launch_decode picks one per batch):
+//   * whole-unit (batch 96 and up, except where the last round of units
+//     would leave most waves idle): a wave of the persistent,
+//     wave-pipelined attention kernel owns a (sequence, group) unit, reads
+//     its ring then its bank, and finishes the token in-wave (current
+//     token, gate, output, ring write, pending append): one launch;
+//   * split, multi-tile parts (batch 33-95 and a few larger ones): reads
+//     are cut into parts of whole 64-key tiles taken by the same persistent
+//     kernel; partials go to scratch and a combine kernel finishes the
+//     token;
+//   * split, one-tile parts (batch 1-32): one four-wave workgroup per
 //     64-key tile in decode_part_kernel (all loads at once, a 16-key block
-//     per wave, scores on MFMA), then the
-//     combine kernel.
+//     per wave, scores on MFMA), then the combine kernel.
 // Positions come from the lockstep arguments or, per sequence, from a
 // device array (TokPos); with per-sequence positions a completed block is
 // admitted right after the token (in the combine workgroup, or by an admit
