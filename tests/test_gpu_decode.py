@@ -55,6 +55,22 @@ def _run_trajectory(w, seed, steps, check_every=1, state_at_admit=True, out_batc
     return worst
 
 
+@pytest.mark.parametrize("B,kind", [(300, "split, two rounds of parts"),
+                                     (448, "whole-unit, a partial second round")])
+def test_launch_shapes_large_batch(B, kind):
+    """Launch shapes that depend only on the number of units, run on a small
+    geometry (ring 63, bank 64, commit 16) so that every sequence's state
+    and outputs can be checked: batch 300 (1,200 units; the last round of
+    whole units would leave most waves idle, so the split launch) and 448
+    (1,792 units: whole units in one-wave workgroups, the second round
+    partial).  40 steps across three block ends; every output every 4th step,
+    the whole state at each admit and at the end."""
+    gu.log(f"case launch shape B={B} ({kind})")
+    w = synth.WORKLOADS["layer_b1"].with_(name=f"shape_b{B}", B=B, R=63, N=64, C=16,
+                                          t0=64 * 16 + 5, bank_n=64, steps=40)
+    _run_trajectory(w, 9, 40, check_every=4)
+
+
 def test_layer_b1_512_steps_two_admits():
     """One layer, batch 1, ring and bank full, 512 decode steps with two
     admits; every output and the whole state after each admit."""
