@@ -701,7 +701,9 @@ __global__ __launch_bounds__(64 * kW) void decode_attn_kernel(DecodeArgs a, int 
 // per key, 8 dims per lane, on V rows as stored.  Four waves per part
 // rather than one take a quarter of the loads and of the P.V each, which
 // shortens the part's chain (batch 1: 91 against 102 us per 8-layer token
-// as a graph replay).
+// as a graph replay).  kNT: non-temporal loads, used at batch 1 only
+// (88 against 91 us per token there; at batches 16 and 32 they cost 15%).
+template <bool kNT>
 __global__ __launch_bounds__(256) void decode_part_kernel(DecodeArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // 16-key block of the tile
@@ -735,14 +737,17 @@ __global__ __launch_bounds__(256) void decode_part_kernel(DecodeArgs a) {
         (void*)sg.K4, (short)0, sg.slots * kChunks * 16, kBufWord3);
     const uint32_t v0 = (uint32_t)((lg * sg.slots + tile * kTile + 16 * w + l16) * 16);
 #pragma unroll
-    for (int st = 0; st < 8; ++st) kr[st] = buf_load16(r, v0, (uint32_t)(4 * st * sg.slots * 16));
+    for (int st = 0; st < 8; ++st)
+      kr[st] = kNT ? buf_load16_nt(r, v0, (uint32_t)(4 * st * sg.slots * 16))
+                   : buf_load16(r, v0, (uint32_t)(4 * st * sg.slots * 16));
   }
   {
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
         (void*)sg.V4, (short)0, sg.count * kChunks * 16, kBufWord3);
     const uint32_t v0 = (uint32_t)(((tile * kTile + 16 * w + half) * kChunks + c32) * 16);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) vr[j] = buf_load16(r, v0 + j * 1024, 0u);
+    for (int j = 0; j < 8; ++j)
+      vr[j] = kNT ? buf_load16_nt(r, v0 + j * 1024, 0u) : buf_load16(r, v0 + j * 1024, 0u);
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -1068,7 +1073,10 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   const int S = a.splits_ring + a.splits_bank;
   const int items = a.units * S;
   if (a.tiles_ring == 1 && a.tiles_bank == 1) {  // one tile per part
-    hipLaunchKernelGGL(decode_part_kernel, dim3(items), dim3(256), 0, s, a);
+    if (a.units <= 4)
+      hipLaunchKernelGGL(decode_part_kernel<true>, dim3(items), dim3(256), 0, s, a);
+    else
+      hipLaunchKernelGGL(decode_part_kernel<false>, dim3(items), dim3(256), 0, s, a);
   } else {
     int grid = (items + kWaves - 1) / kWaves;
     const int res = resident_workgroups<false, false, kWaves>();
