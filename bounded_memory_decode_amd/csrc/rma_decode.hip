@@ -199,8 +199,8 @@ __device__ __forceinline__ Seg make_seg(const DecodeArgs& a, int u, bool ring, i
   Seg sg;
   if (ring) {
     sg.count = tp.ring_count;
-    sg.slots = a.R;
-    sg.K4 = reinterpret_cast<const uint4*>(a.ring_k + (size_t)u * a.R * kD);
+    sg.slots = a.Rk;
+    sg.K4 = reinterpret_cast<const uint4*>(a.ring_k + (size_t)u * a.Rk * kD);
     sg.V4 = reinterpret_cast<const uint4*>(a.ring_v + (size_t)u * a.R * kD);
   } else {
     sg.count = tp.live ? scalar_load(a.bank_n + u) : 0;
@@ -359,7 +359,7 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs& a, int u, int lane
   // lanes 32-63), pending slot t mod C likewise.
   {
     const bool kside = lane < 32;
-    const size_t ro = kside ? (size_t)u * a.R * kChunks + k_chunk_index(tp.ring_slot, c32, a.R)
+    const size_t ro = kside ? (size_t)u * a.Rk * kChunks + k_chunk_index(tp.ring_slot, c32, a.Rk)
                             : ((size_t)u * a.R + tp.ring_slot) * kChunks + c32;
     store16(reinterpret_cast<uint4*>(pick(kside, a.ring_k, a.ring_v)) + ro, kv);
     const size_t po = ((size_t)u * a.C + tp.pend_slot) * kChunks + c32;
@@ -936,8 +936,8 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   // slot t mod C takes the candidate record and score; one wave each.
   if (lane < 32) {
     if (h == 0) {
-      uint4* rk = reinterpret_cast<uint4*>(a.ring_k + (size_t)u * a.R * kD);
-      rk[k_chunk_index(tp.ring_slot, lane, a.R)] = reinterpret_cast<const uint4*>(a.k + kvo)[lane];
+      uint4* rk = reinterpret_cast<uint4*>(a.ring_k + (size_t)u * a.Rk * kD);
+      rk[k_chunk_index(tp.ring_slot, lane, a.Rk)] = reinterpret_cast<const uint4*>(a.k + kvo)[lane];
     } else if (h == 1) {
       uint4* rv = reinterpret_cast<uint4*>(a.ring_v + ((size_t)u * a.R + tp.ring_slot) * kD);
       rv[lane] = reinterpret_cast<const uint4*>(a.v + kvo)[lane];

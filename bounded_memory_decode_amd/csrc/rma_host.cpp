@@ -97,7 +97,7 @@ int make_layout(const rma_config* c, int32_t batch, rma_layout* L) {
     off = align_up(off + bytes);
     return at;
   };
-  L->ring_k = take(units * R * rec_half);
+  L->ring_k = take(units * (uint64_t)rma::ring_k_slots((int)R) * rec_half);
   L->ring_v = take(units * R * rec_half);
   L->bank_k = take(units * N * rec_half);
   L->bank_v = take(units * N * rec_half);
@@ -118,6 +118,7 @@ int make_layout(const rma_config* c, int32_t batch, rma_layout* L) {
   }
   L->scratch = take(L->scratch_bytes);
   L->total_bytes = off;
+  L->ring_k_slots = (uint64_t)rma::ring_k_slots((int)R);
   L->ring_bytes = units * R * rec_half * 2;
   L->bank_bytes = units * N * rec_half * 2;
   L->pend_bytes = units * C * rec_half * 2;
@@ -167,7 +168,7 @@ rma::DecodeArgs decode_args(const rma_state* st, int32_t layer, int64_t t, const
   a.cs = cs;
   a.w_g = w_g;
   a.out = static_cast<uint16_t*>(out);
-  a.ring_k = region<uint16_t>(st, L.ring_k) + unit0 * R * kD;
+  a.ring_k = region<uint16_t>(st, L.ring_k) + unit0 * rma::ring_k_slots(R) * kD;
   a.ring_v = region<uint16_t>(st, L.ring_v) + unit0 * R * kD;
   a.bank_k = region<uint16_t>(st, L.bank_k) + unit0 * N * kD;
   a.bank_v = region<uint16_t>(st, L.bank_v) + unit0 * N * kD;
@@ -187,6 +188,7 @@ rma::DecodeArgs decode_args(const rma_state* st, int32_t layer, int64_t t, const
   a.G = G;
   a.H = c.q_heads;
   a.R = R;
+  a.Rk = rma::ring_k_slots(R);
   a.N = N;
   a.C = C;
   a.ring_count = (int)(t < R ? t : R);
@@ -219,7 +221,7 @@ rma::PrefillArgs prefill_args(const rma_state* st, int32_t layer, int32_t n_toke
   a.cs = cs;
   a.w_g = w_g;
   a.out = static_cast<uint16_t*>(out);
-  a.ring_k = region<uint16_t>(st, L.ring_k) + unit0 * R * kD;
+  a.ring_k = region<uint16_t>(st, L.ring_k) + unit0 * rma::ring_k_slots(R) * kD;
   a.ring_v = region<uint16_t>(st, L.ring_v) + unit0 * R * kD;
   a.bank_k = region<uint16_t>(st, L.bank_k) + unit0 * N * kD;
   a.bank_v = region<uint16_t>(st, L.bank_v) + unit0 * N * kD;
@@ -236,6 +238,7 @@ rma::PrefillArgs prefill_args(const rma_state* st, int32_t layer, int32_t n_toke
   a.G = G;
   a.H = c.q_heads;
   a.R = R;
+  a.Rk = rma::ring_k_slots(R);
   a.N = N;
   a.C = C;
   a.n = n_tokens;

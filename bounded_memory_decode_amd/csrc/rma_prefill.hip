@@ -192,7 +192,7 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_kernel(PrefillArgs a
   const int min_age = (int)(R - P > 0 ? R - P : 0);
   const int p_mod = (int)(P % R);
 
-  const uint16_t* ring_k = a.ring_k + (size_t)u * R * kD;
+  const uint16_t* ring_k = a.ring_k + (size_t)u * a.Rk * kD;
   const uint16_t* ring_v = a.ring_v + (size_t)u * R * kD;
   const uint16_t* bank_k = a.bank_k + (size_t)u * a.N * kD;
   const uint16_t* bank_v = a.bank_v + (size_t)u * a.N * kD;
@@ -226,7 +226,7 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_kernel(PrefillArgs a
     sr.v = ring ? reinterpret_cast<const uint4*>(ring_v)
                 : (blk ? vblk : reinterpret_cast<const uint4*>(bank_v));
     sr.kks = blk ? a.G * kChunks : 1;
-    sr.kcs = ring ? R : (blk ? 1 : a.N);
+    sr.kcs = ring ? a.Rk : (blk ? 1 : a.N);
     sr.vks = blk ? a.G * kChunks : kChunks;
     sr.cnt = seg_count(seg);
     sr.ti = ti;
@@ -566,11 +566,11 @@ __device__ __forceinline__ void commit_tokens(const PrefillArgs& a, int bx, int 
   __syncthreads();
   // ring K: thread x: chunk x / 64, token x % 64 (consecutive lanes write
   // consecutive slots of one chunk plane)
-  uint4* rk = reinterpret_cast<uint4*>(a.ring_k + (size_t)u * a.R * kD);
+  uint4* rk = reinterpret_cast<uint4*>(a.ring_k + (size_t)u * a.Rk * kD);
 #pragma unroll
   for (int i = 0; i < kCommitTok * kChunks / 256; ++i) {
     const int x = tid + 256 * i, c = x / kCommitTok, jj = x % kCommitTok;
-    if (jj < nt) rk[k_chunk_index((int)((P + j0 + jj) % a.R), c, a.R)] = kt[jj][c];
+    if (jj < nt) rk[k_chunk_index((int)((P + j0 + jj) % a.R), c, a.Rk)] = kt[jj][c];
   }
 }
 

@@ -47,7 +47,7 @@ class Layout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in (
         "ring_k", "ring_v", "bank_k", "bank_v", "pend_k", "pend_v", "bscore", "bsrc",
         "pscore", "bank_n", "scratch", "scratch_bytes", "total_bytes", "ring_bytes",
-        "bank_bytes", "pend_bytes", "meta_bytes")]
+        "bank_bytes", "pend_bytes", "meta_bytes", "ring_k_slots")]
 
 
 class _State(ctypes.Structure):
@@ -200,14 +200,16 @@ class State:
     def region_view(self, name: str) -> torch.Tensor:
         """A view of one region in its stored layout (int16 for bf16 bits):
         ring_k/bank_k [L][B][G][slots*d] (16-byte chunks, chunk-major, see
-        include/rma.h), ring_v/bank_v [L][B][G][slots][d],
+        include/rma.h; a ring K plane has layout.ring_k_slots slots, the
+        ring's R rounded up to a multiple of 64), ring_v/bank_v
+        [L][B][G][slots][d],
         pend_k/pend_v [L][B][G][C][d], bscore/bsrc [L][B][G][N],
         pscore [L][B][G][C], bank_n [L][B][G]."""
         c = self.cfg
         L, B, G, d = c.layers, self.batch, c.kv_groups, c.head_dim
         R, N, C = c.window - 1, c.bank_cap, c.commit
         shapes = {
-            "ring_k": ((L, B, G, R * d), torch.int16),
+            "ring_k": ((L, B, G, int(self.layout.ring_k_slots) * d), torch.int16),
             "ring_v": ((L, B, G, R, d), torch.int16),
             "bank_k": ((L, B, G, N * d), torch.int16),
             "bank_v": ((L, B, G, N, d), torch.int16),
@@ -231,6 +233,11 @@ class State:
         if name in ("ring_k", "bank_k"):
             dst = v[layers, batch]
             src = _as_bits(value).to(self.device).reshape(*dst.shape[:3], -1, self.cfg.head_dim)
+            slots = dst.shape[-1] // self.cfg.head_dim
+            if src.shape[-2] < slots:  # ring K plane padding slots
+                pad = torch.zeros((*src.shape[:-2], slots - src.shape[-2], src.shape[-1]),
+                                  dtype=src.dtype, device=src.device)
+                src = torch.cat([src, pad], dim=-2)
             dst.copy_(_k_to_stored(src))
         else:
             dst = v[layers, batch]
@@ -243,7 +250,10 @@ class State:
     def read(self, name: str, layers=slice(None), batch=slice(None)) -> torch.Tensor:
         """Copy of region `name` in the natural layout (bf16 bits as int16)."""
         v = self.region_view(name)
-        if name in ("ring_k", "bank_k"):
+        if name == "ring_k":  # without the plane's padding slots
+            nat = _k_to_natural(v[layers, batch], self.cfg.head_dim)
+            return nat[..., :self.cfg.window - 1, :].contiguous()
+        if name == "bank_k":
             return _k_to_natural(v[layers, batch], self.cfg.head_dim)
         return v[layers, batch].clone()
 

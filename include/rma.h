@@ -96,9 +96,13 @@ typedef struct {
  * indexed by unit u = (layer * batch + b) * kv_groups + g first, and is
  * 256-byte aligned.  R = window-1, N = bank_cap, C = commit, d = head_dim.
  *
- *   ring_k  [units][d/8][R][8] bf16   K, split in 16-byte chunks of 8 dims,
+ *   ring_k  [units][d/8][Rk][8] bf16  K, split in 16-byte chunks of 8 dims,
  *                                     chunk-major: chunk c of slot s is at
- *                                     uint4 index c*R + s of the unit's plane
+ *                                     uint4 index c*Rk + s of the unit's
+ *                                     plane; Rk = R rounded up to a multiple
+ *                                     of 64 (ring_k_slots below; slots R ..
+ *                                     Rk-1 are alignment padding, never read
+ *                                     or written)
  *   ring_v  [units][R][d]      bf16   V rows
  *   bank_k  [units][d/8][N][8] bf16   as ring_k with N slots
  *   bank_v  [units][N][d]      bf16
@@ -116,7 +120,9 @@ typedef struct {
   uint64_t bscore, bsrc, pscore, bank_n, scratch;
   uint64_t scratch_bytes;
   uint64_t total_bytes;
-  uint64_t ring_bytes, bank_bytes, pend_bytes, meta_bytes; /* K+V+metadata totals */
+  uint64_t ring_bytes, bank_bytes, pend_bytes, meta_bytes; /* K+V+metadata totals
+                                                             (records, without padding) */
+  uint64_t ring_k_slots;        /* Rk: slots of a ring K plane */
 } rma_layout;
 
 /* Caller-owned state handle.  Plain data; copy it to snapshot the host

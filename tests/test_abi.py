@@ -70,6 +70,10 @@ def test_layout_matches_the_pages_memory_table():
     for name in ("ring_k", "ring_v", "bank_k", "bank_v", "pend_k", "pend_v", "bscore", "bsrc",
                  "pscore", "bank_n", "scratch"):
         assert getattr(L512, name) % 256 == 0
+    # ring K planes are padded to 1,024 slots (1 KiB-aligned chunk planes);
+    # the padding is alignment, not records
+    assert L.ring_k_slots == 1024
+    assert L512.ring_v - L512.ring_k >= 512 * 4 * 8 * 1024 * 512
     # regions do not overlap and are in order
     offs = [L512.ring_k, L512.ring_v, L512.bank_k, L512.bank_v, L512.pend_k, L512.pend_v,
             L512.bscore, L512.bsrc, L512.pscore, L512.bank_n, L512.scratch]
