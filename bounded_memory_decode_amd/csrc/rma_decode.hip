@@ -1022,15 +1022,16 @@ hipError_t launch_whole(const DecodeArgs& a, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
-  // Whole-unit launch when the last round of units (the only one, below
-  // one unit per resident wave) occupies at least 3/8 of the waves; else
-  // the split launch.  Measured on MI355X
-  // (1,024 waves, 1 layer, per token): whole-unit wins from batch 96 (384
-  // units) up to 255 (at 144: 232 against 243 us; at 160: 237 against
-  // 250) and at batch 448 (a last round of 768: 637-649 against 673 us);
-  // the split wins at batch 64 (94 against 129 us with non-temporal loads)
-  // and 288-320 (last rounds of 128-256 units: 455 against 466 us at 320);
-  // at 352 (a last round of 384) whole units win, 491 against 518 us.  With at least one unit per wave, one-wave
+  // Whole-unit launch when the last round of units occupies at least 5/8
+  // of the waves, or 3/8 when it follows full rounds; else the split
+  // launch.  Measured on MI355X
+  // (1,024 waves, 1 layer, per token, non-temporal loads, padded ring K
+  // planes): whole-unit wins from batch 160 (640 units) up to 255 and at
+  // batch 448 (a last round of 768: 594 against 673 us); the split wins
+  // below 160 (at 96: 142 against 153 us; at 128: 178 against 190; at 112
+  // whole units win by 3%) and at 288-320 (last rounds of 128-256 units:
+  // 455 against 466 us at 320); at 352 (a last round of 384 after a full
+  // one) whole units win, 491 against 518 us.  With at least one unit per wave, one-wave
   // workgroups (704 against 713 us per launch at batch 512, 637 against
   // 651 at 448); for a single round of 5/8 or more, four-wave ones, which
   // fill fewer CUs completely (237 against 241 us at batch 160, 272
@@ -1042,11 +1043,10 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   const int rounds = (a.units + waves - 1) / waves;
   const int last = a.units - (rounds - 1) * waves;
   const bool wide = (int64_t)last * 8 >= (int64_t)waves * 5;  // last round >= 5/8 of the waves
-  const bool mid = (int64_t)last * 8 >= (int64_t)waves * 3;  // last round >= 3/8
+  const bool mid = rounds > 1 && (int64_t)last * 8 >= (int64_t)waves * 3;  // later round >= 3/8
   if (wide || mid) {
-    // one-wave workgroups with at least one unit per wave, and for a
-    // single round of 3/8 to 5/8 of the waves; four-wave ones for a single
-    // round above 5/8
+    // one-wave workgroups with at least one unit per wave; four-wave ones
+    // for a single round (5/8 of the waves or more)
     const bool one = a.units >= waves || !wide;
     hipError_t e = qa ? (one ? launch_whole<true, 1>(a, s) : launch_whole<true, kWaves>(a, s))
                       : (one ? launch_whole<false, 1>(a, s) : launch_whole<false, kWaves>(a, s));

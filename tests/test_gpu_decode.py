@@ -173,11 +173,11 @@ def test_pending_full_is_reported_and_state_unchanged():
                                          (144, [0, 77, 143]), (160, [0, 77, 159])])
 def test_launch_shapes(B, out_batch):
     """Batch sizes whose launch differs from the other tests: 16 (the
-    one-tile part kernel with 2,048 parts), 64 (8-tile parts of the
-    persistent kernel), 144 and 160 (the whole-unit kernel with 576 and 640
-    units, fewer than its resident waves, in one-wave and four-wave
-    workgroups).  40 steps across a block end; sampled outputs every 5th
-    step, the whole state at the admit and at the end."""
+    one-tile part kernel with 2,048 parts), 64 and 144 (8-tile and 2-tile
+    parts of the persistent kernel) and 160 (the whole-unit kernel with 640
+    units, fewer than its resident waves, in four-wave workgroups).  40
+    steps across a block end; sampled outputs every 5th step, the whole
+    state at the admit and at the end."""
     gu.log(f"case launch shape B={B}")
     w = synth.WORKLOADS["layer_b1"].with_(name=f"split_b{B}", B=B, t0=32768 + 230, steps=40)
     _run_trajectory(w, 7, 40, check_every=5, out_batch=out_batch)
