@@ -36,6 +36,8 @@
 // loads one 512-byte row.  Neither read needs an LDS transpose.
 #include "rma_admit_unit.h"
 
+#include <atomic>
+
 namespace rma {
 namespace {
 
@@ -990,13 +992,15 @@ __global__ void seq_bank_n_kernel(int32_t* bank_n, int L, int B, int G, int firs
 
 
 // Workgroups of a kernel that are resident at once on the current device
-// (CUs x workgroups per CU), computed once per device.
+// (CUs x workgroups per CU), computed once per device (host threads may
+// race to fill an entry: each computes and stores the same value).
 template <bool kWhole, bool kQA, int kW>
 int resident_workgroups() {
-  static int cached[64] = {0};
+  static std::atomic<int> cached[64];  // zero-initialised (static storage)
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cached[dev] == 0) {
+  int r = cached[dev].load(std::memory_order_relaxed);
+  if (r == 0) {
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       cus = 256;
@@ -1004,9 +1008,10 @@ int resident_workgroups() {
                                                      64 * kW, 0) != hipSuccess ||
         per_cu < 1)
       per_cu = 1;
-    cached[dev] = cus * per_cu;
+    r = cus * per_cu;
+    cached[dev].store(r, std::memory_order_relaxed);
   }
-  return cached[dev];
+  return r;
 }
 
 template <bool kQA, int kW>
