@@ -46,6 +46,11 @@
  *   - The library allocates no memory.  The caller owns the rma_state
  *     struct and one device buffer holding the whole state (its size from
  *     rma_state_bytes).
+ *   - Calls on one state must be ordered: issue them from one host
+ *     thread, on one stream (or order the streams with events).  They
+ *     share the state's scratch region and the host mirror in rma_state,
+ *     so calls on one state that overlap race.  Distinct states are
+ *     independent.
  *   - The lockstep calls (rma_decode_step, rma_prefill_block, rma_admit)
  *     move a batch together: all sequences of a layer share the position
  *     t, which the host mirrors in rma_state.  The per-sequence calls
