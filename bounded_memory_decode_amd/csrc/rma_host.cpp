@@ -31,8 +31,12 @@ int check_config(const rma_config* c) {
       !std::isfinite(c->scale) || c->q_heads % c->kv_groups != 0)
     return RMA_E_ARG;
   if (c->head_dim != kD || c->q_heads != kHpg * c->kv_groups) return RMA_E_UNSUPPORTED;
-  if (c->window > 8193 || c->commit > 256 || c->bank_cap + c->commit > 2048)
+  if (c->window > 4097 || c->commit > 256 || c->bank_cap + c->commit > 2048)
     return RMA_E_UNSUPPORTED;
+  // A block's tokens must land in distinct ring slots, and each query of a
+  // prefill block must have its whole local window inside the ring plus
+  // the block's earlier tokens: the block is at most window - 1 tokens.
+  if (c->commit > c->window - 1) return RMA_E_UNSUPPORTED;
   return RMA_OK;
 }
 

@@ -31,8 +31,9 @@
  *   the bank see an admitted record only from the next block on.
  *
  * The gate form, the tie-break and the compaction order are readings of
- * the pages (which only say "query-dependent signed gate", "highest
- * priority", "retained records remain separate and unchanged").
+ * the pages: they name a query-dependent signed gate, keep the records of
+ * highest priority and leave kept records as they are, without fixing
+ * these details (model card, "How Rock Memory Anchors work").
  *
  * Conventions for every call:
  *   - bf16 tensors are passed as `const void*` to 16-bit IEEE bfloat16
@@ -85,7 +86,8 @@ extern "C" {
  * table; Rock Matrix models page spec list; head_dim from the card's
  * persistent-history MiB table).  Limits: 1 <= layers <= RMA_MAX_LAYERS,
  * q_heads == 4 * kv_groups, head_dim == 256, 2 <= window <= 4097,
- * 1 <= bank_cap, 1 <= commit <= 256, bank_cap + commit <= 2048. */
+ * 1 <= bank_cap, 1 <= commit <= 256, commit <= window - 1 (a block's
+ * tokens take distinct ring slots), bank_cap + commit <= 2048. */
 typedef struct {
   int32_t layers;
   int32_t q_heads;
@@ -157,16 +159,28 @@ int rma_config_default(rma_config* cfg);
  * batch < 1. */
 size_t rma_state_bytes(const rma_config* cfg, int32_t batch);
 
-/* Region offsets for `batch` sequences.  Returns RMA_OK, RMA_E_ARG or
- * RMA_E_UNSUPPORTED. */
+/* Region offsets for `batch` sequences: where the ring, bank, pending and
+ * metadata records of every (layer, sequence, group) sit in the state
+ * buffer (the record sizes are those of the model card's persistent-history
+ * table, section "Constant history and GPU memory": 31.97 MiB of local KV,
+ * 32.00 MiB of anchors, 8.00 MiB of pending candidates per sequence, plus
+ * metadata).  Fills *out; the caller owns it.  Returns RMA_OK, RMA_E_ARG
+ * (null out, batch < 1) or RMA_E_UNSUPPORTED; *out is unspecified on
+ * error. */
 int rma_state_layout(const rma_config* cfg, int32_t batch, rma_layout* out);
 
 /* Bind `dev_buf` (at least rma_state_bytes bytes, 256-byte aligned) to
  * *st and start every layer at position `start_pos` with `bank_n`
  * committed anchors (0 <= bank_n <= bank_cap) and start_pos % commit
- * pending candidates.  Enqueues a write of the device bank counts; record
- * contents, scores and source positions are left as they are (the caller
- * fills them through the layout, or starts from an empty history). */
+ * pending candidates.  The history's memory is fixed before inference and
+ * allocated once (tpsreport, "What this means"): this call takes the
+ * caller's buffer and nothing is allocated later.  Enqueues a write of the
+ * device bank counts; record contents, scores and source positions are
+ * left as they are (the caller fills them through the layout, or starts
+ * from an empty history).  The caller keeps ownership of dev_buf and *st.
+ * Returns RMA_OK, RMA_E_ARG (null pointer, misaligned or short buffer,
+ * bad position or bank count; *st unchanged), RMA_E_UNSUPPORTED, or
+ * RMA_E_HIP (the count write failed to launch; st->hip_error set). */
 int rma_state_init(rma_state* st, const rma_config* cfg, int32_t batch,
                    void* dev_buf, size_t bytes, int64_t start_pos,
                    int32_t bank_n, void* stream);
@@ -190,7 +204,10 @@ int rma_decode_step(rma_state* st, int32_t layer, const void* q, const void* k,
  * of layer `layer`, starting at a block boundary (no candidates pending).
  * Same result as that many rma_decode_step calls: each query attends to
  * its causal local window over the ring and the earlier tokens of the
- * block, and to the bank committed before the block.  Shapes as in
+ * block, and to the bank committed before the block; the block's own
+ * candidates are readable only after the admit at its end (model card,
+ * "How Rock Memory Anchors work": reads use the committed bank, and new
+ * selections become visible in the next block).  Shapes as in
  * rma_decode_step with a token axis after the batch axis:
  *   q [batch][n][q_heads][d], k/v/cand_k/cand_v [batch][n][kv_groups][d],
  *   cand_score [batch][n][kv_groups], out [batch][n][q_heads][d].

@@ -89,6 +89,8 @@ def test_layout_matches_the_pages_memory_table():
     ("layers", 65, rma.RMA_E_ARG),
     ("window", 1, rma.RMA_E_ARG),
     ("commit", 512, rma.RMA_E_UNSUPPORTED),
+    ("window", 4098, rma.RMA_E_UNSUPPORTED),
+    ("window", 256, rma.RMA_E_UNSUPPORTED),   # commit 256 > ring 255
     ("bank_cap", 1900, rma.RMA_E_UNSUPPORTED),
     ("scale", float("nan"), rma.RMA_E_ARG),
 ])

@@ -546,6 +546,118 @@ def test_new_anchor_invisible_until_next_block():
     np.testing.assert_array_equal(a[0, :4], b[0, :4])
 
 
+# ------------------------------------------------------------ prefill block
+
+
+def _prefill_geometry(history):
+    """Tiny heads (d = 16) with the real block length: C = 256 pending
+    slots, so a block of 1, 17 or 256 tokens fits, and a ring of 300 slots
+    that a full block wraps part of the way round."""
+    full = history == "full"
+    return tiny(B=3, H=8, G=2, d=16, R=300, N=40, C=256, t0=512 if full else 0,
+                bank_n=40 if full else 0, ring_full=full)
+
+
+@pytest.mark.parametrize("anchor_query", [False, True], ids=["q", "q_anchor"])
+@pytest.mark.parametrize("history", ["empty", "full"])
+@pytest.mark.parametrize("n", [1, 17, 256])
+def test_prefill_block_equals_bruteforce_and_decode_steps(n, history, anchor_query):
+    """A prompt block is its tokens in order, each reading its causal local
+    window and the bank committed before the block; the block's candidates
+    become readable only after the admit at its end (model card, "How Rock
+    Memory Anchors work": reads use the committed bank, new selections are
+    visible from the next block).
+
+    Two blocks from an empty or a full history, 3 sequences, with and
+    without a separate anchor query.  Each prefill block is checked
+      - output by output against the full-history brute force, which keeps
+        every token by position and admits only at a block end;
+      - state bit for bit against the same tokens fed one at a time to the
+        decode step (the test slices the [B][n] inputs itself);
+      - for a bank left untouched by the block.
+    A short block is completed by decode steps (also against the brute
+    force) before the admit."""
+    w = _prefill_geometry(history)
+    seed = 61 + n
+    o, st = make_oracle(w, seed)
+    wg = synth.gate_weights(w, seed)
+    bfs = [BruteForce(w.H, w.G, w.d, w.R, w.N, w.C, w.d ** -0.5, w.t0, st["ring_k"][0, b],
+                      st["ring_v"][0, b], st["bank_k"][0, b], st["bank_v"][0, b],
+                      st["bscore"][0, b], st["bsrc"][0, b], st["bank_n"][0, b])
+           for b in range(w.B)]
+    step = 0
+    for blk in range(2):
+        x = synth.block_inputs(w, seed, 0, step, n)
+        qa = synth.block_anchor_query(w, seed, 0, step, n) if anchor_query else None
+        per_token = o.clone()
+        bank_before = {k: getattr(o, k).copy() for k in ("bank_k", "bank_v", "bscore", "bsrc",
+                                                         "bank_n")}
+        out = o.prefill_block(0, x["q"], x["k"], x["v"], x["ck"], x["cv"], x["cs"], wg[0],
+                              q_anchor=qa)
+        assert out.shape == (w.B, n, w.H, w.d)
+        for i in range(n):
+            xi = {k: np.ascontiguousarray(v[:, i]) for k, v in x.items()}
+            qai = None if qa is None else np.ascontiguousarray(qa[:, i])
+            ref_i = per_token.decode_step(0, xi["q"], xi["k"], xi["v"], xi["ck"], xi["cv"],
+                                          xi["cs"], wg[0], q_anchor=qai)
+            np.testing.assert_array_equal(out[:, i], ref_i)
+            for b in range(w.B):
+                bf = bfs[b].step(xi["q"][b], xi["k"][b], xi["v"][b], xi["ck"][b], xi["cv"][b],
+                                 xi["cs"][b], wg[0], q_anchor=None if qai is None else qai[b])
+                np.testing.assert_allclose(out[b, i], bf, rtol=0, atol=1e-12,
+                                           err_msg=f"block {blk} token {i} sequence {b}")
+        for name in OracleState.ARRAYS:
+            np.testing.assert_array_equal(getattr(o, name), getattr(per_token, name),
+                                          err_msg=name)
+        for name, before in bank_before.items():
+            np.testing.assert_array_equal(getattr(o, name), before, err_msg=name)
+        assert o.t[0] == w.t0 + step + n and o.pend_n[0] == n
+        step += n
+        while o.pend_n[0] < w.C:
+            xs = synth.step_inputs(w, seed, 0, step)
+            qs = synth.anchor_query(w, seed, 0, step) if anchor_query else None
+            outd = o.decode_step(0, xs["q"], xs["k"], xs["v"], xs["ck"], xs["cv"], xs["cs"],
+                                 wg[0], q_anchor=qs)
+            for b in range(w.B):
+                bf = bfs[b].step(xs["q"][b], xs["k"][b], xs["v"][b], xs["ck"][b], xs["cv"][b],
+                                 xs["cs"][b], wg[0], q_anchor=None if qs is None else qs[b])
+                np.testing.assert_allclose(outd[b], bf, rtol=0, atol=1e-12)
+            step += 1
+        o.admit(0)
+        for b in range(w.B):
+            for g in range(w.G):
+                nb = o.bank_n[0, b, g]
+                assert sorted(o.bsrc[0, b, g, :nb].tolist()) == bfs[b].bank_positions(g)
+
+
+def test_prefill_block_reads_only_the_committed_bank():
+    """A candidate planted early in a prompt block with a huge score and a
+    key along a later query of the same block changes none of that block's
+    outputs (bitwise), and changes the first output of the next block."""
+    w = _prefill_geometry("full").with_(B=1)
+    seed = 71
+    base, _ = make_oracle(w, seed)
+    plant = base.clone()
+    wg = synth.gate_weights(w, seed)
+    x = synth.block_inputs(w, seed, 0, 0, w.C)
+    xp = {k: v.copy() for k, v in x.items()}
+    h, g, late = 5, 1, 200
+    xp["ck"][0, 2, g] = synth.bf16_bits(64.0 * synth.bf16_to_f32(x["q"][0, late, h]))
+    xp["cs"][0, 2, g] = 1e30
+    a = base.prefill_block(0, x["q"], x["k"], x["v"], x["ck"], x["cv"], x["cs"], wg[0])
+    b = plant.prefill_block(0, xp["q"], xp["k"], xp["v"], xp["ck"], xp["cv"], xp["cs"], wg[0])
+    np.testing.assert_array_equal(a, b)
+    base.admit(0)
+    plant.admit(0)
+    assert (plant.bsrc[0, 0, g] == w.t0 + 2).sum() == 1
+    nxt = synth.block_inputs(w, seed, 0, w.C, 1)
+    nxt["q"][0, 0, h] = x["q"][0, late, h]
+    a = base.prefill_block(0, nxt["q"], nxt["k"], nxt["v"], nxt["ck"], nxt["cv"], nxt["cs"], wg[0])
+    b = plant.prefill_block(0, nxt["q"], nxt["k"], nxt["v"], nxt["ck"], nxt["cv"], nxt["cs"],
+                            wg[0])
+    assert np.abs(a[0, 0, h] - b[0, 0, h]).max() > 1e-3
+
+
 # ------------------------------------------------------------ error codes
 
 
