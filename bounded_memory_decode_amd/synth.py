@@ -272,3 +272,25 @@ def torch_scores(shape, w: Workload, seed: int, device, generator_key: Sequence[
 def _torch_seed(seed: int, key: Sequence[int]) -> int:
     ss = np.random.SeedSequence(seed, spawn_key=tuple(int(k) for k in key))
     return int(ss.generate_state(1, dtype=np.uint64)[0] & ((1 << 63) - 1))
+
+
+def torch_block_inputs(w: Workload, seed: int, layer: int, block: int, device,
+                       n: Optional[int] = None, sets: int = 3):
+    """Inputs of n (default C) consecutive tokens of one layer, drawn on
+    `device`: q [B][n][H][d], k, v, ck, cv [B][n][G][d] bf16 and cs [B][n][G]
+    f32, one torch.Generator per (layer, block, tensor).  `block` names the
+    draw (the long prompt uses the index of the 256-token block, decode
+    continues the count); `sets` separates this family of draws from the
+    bench's other torch streams.  Used where a prompt of 131,072 tokens
+    makes the per-token numpy streams too slow."""
+    n = w.C if n is None else int(n)
+    B, H, G, d = w.B, w.H, w.G, w.d
+
+    def key(kind):
+        return (w.wid, KIND[kind], layer, block, sets)
+
+    out = {"q": torch_normal_bf16((B, n, H, d), w.qkv_std, seed, device, key("q"))}
+    for kind in ("k", "v", "ck", "cv"):
+        out[kind] = torch_normal_bf16((B, n, G, d), w.qkv_std, seed, device, key(kind))
+    out["cs"] = torch_scores((B, n, G), w, seed, device, key("cs"))
+    return out

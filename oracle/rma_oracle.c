@@ -1,8 +1,9 @@
 /*
  * RMA layer-step oracle: TEST INFRASTRUCTURE ONLY (see rma_oracle.h).
  *
- * Plain C, double arithmetic, OpenMP only over independent
- * (sequence, group) pairs.  Written from the EdgeRock pages; each
+ * Plain C, double arithmetic, OpenMP only over independent items: the
+ * (sequence, group, head) reads of a token and the (sequence, group)
+ * admits.  Written from the EdgeRock pages; each
  * function names the passage it follows.  Readings of points the pages
  * leave open are marked "Reading:".
  */
@@ -114,7 +115,8 @@ static void attend(int d, double scale, const double* q, int nk,
   }
 }
 
-/* Output of one token at position t for sequence b, group g of a layer.
+/* Output of one token at position t for sequence b, query head hh of
+ * group g of a layer.
  *
  * Retrieve (ai-primer, three-operation list, item 3; model card "How Rock
  * Memory Anchors work"): queries read the committed bank; a
@@ -136,7 +138,7 @@ static void attend(int d, double scale, const double* q, int nk,
  *   - Reading: heads h = g*(H/G) ... g*(H/G)+H/G-1 share group g.
  */
 static void token_output(const orc_state* st, int32_t layer, int32_t b, int32_t g,
-                         int64_t t, const uint16_t* qtok /*[H][d]*/,
+                         int32_t hh, int64_t t, const uint16_t* qtok /*[H][d]*/,
                          const uint16_t* qatok /*[H][d]*/,
                          const uint16_t* kcur, const uint16_t* vcur,
                          const float* w_g /*[H][d]*/, double* out /*[H][d]*/) {
@@ -180,23 +182,21 @@ static void token_output(const orc_state* st, int32_t layer, int32_t b, int32_t 
   double* oloc = (double*)malloc(sizeof(double) * d);
   double* oanc = (double*)malloc(sizeof(double) * d);
 
-  for (int hh = 0; hh < hpg; ++hh) {
-    const int h = g * hpg + hh;
-    for (int i = 0; i < d; ++i) q[i] = bf16_to_double(qtok[(size_t)h * d + i]);
-    for (int i = 0; i < d; ++i) qa[i] = bf16_to_double(qatok[(size_t)h * d + i]);
+  const int h = g * hpg + hh;
+  for (int i = 0; i < d; ++i) q[i] = bf16_to_double(qtok[(size_t)h * d + i]);
+  for (int i = 0; i < d; ++i) qa[i] = bf16_to_double(qatok[(size_t)h * d + i]);
 
-    attend(d, c->scale, q, nloc, lk, lv, s, oloc);
-    if (n > 0) {
-      attend(d, c->scale, qa, n, ak, av, s, oanc);
-    } else {
-      for (int i = 0; i < d; ++i) oanc[i] = 0.0;
-    }
-
-    double zg = 0.0;
-    for (int i = 0; i < d; ++i) zg += qa[i] * (double)w_g[(size_t)h * d + i];
-    const double gate = tanh(zg);
-    for (int i = 0; i < d; ++i) out[(size_t)h * d + i] = oloc[i] + gate * oanc[i];
+  attend(d, c->scale, q, nloc, lk, lv, s, oloc);
+  if (n > 0) {
+    attend(d, c->scale, qa, n, ak, av, s, oanc);
+  } else {
+    for (int i = 0; i < d; ++i) oanc[i] = 0.0;
   }
+
+  double zg = 0.0;
+  for (int i = 0; i < d; ++i) zg += qa[i] * (double)w_g[(size_t)h * d + i];
+  const double gate = tanh(zg);
+  for (int i = 0; i < d; ++i) out[(size_t)h * d + i] = oloc[i] + gate * oanc[i];
   free(lk); free(lv); free(ak); free(av); free(s); free(q); free(qa); free(oloc); free(oanc);
 }
 
@@ -232,13 +232,15 @@ int orc_decode_step(const orc_state* st, int32_t layer,
   const int B = st->B, G = c->G, H = c->H, d = c->d;
   if (compute_out) {
     if (!out) return ORC_E_ARG;
-#pragma omp parallel for collapse(2) schedule(dynamic)
+    const int hpg = H / G;
+#pragma omp parallel for collapse(3) schedule(dynamic)
     for (int b = 0; b < B; ++b)
       for (int g = 0; g < G; ++g)
-        token_output(st, layer, b, g, t, q + (size_t)b * H * d,
-                     (q_anchor ? q_anchor : q) + (size_t)b * H * d,
-                     k + ((size_t)b * G + g) * d, v + ((size_t)b * G + g) * d,
-                     w_g, out + (size_t)b * H * d);
+        for (int hh = 0; hh < hpg; ++hh)
+          token_output(st, layer, b, g, hh, t, q + (size_t)b * H * d,
+                       (q_anchor ? q_anchor : q) + (size_t)b * H * d,
+                       k + ((size_t)b * G + g) * d, v + ((size_t)b * G + g) * d,
+                       w_g, out + (size_t)b * H * d);
   }
   /* writes only after every read of this token (slot t mod R is still
      inside this token's window) */

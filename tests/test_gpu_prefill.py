@@ -114,41 +114,6 @@ def test_prefill_equals_decode_on_gpu():
     assert A.t == D.t and A.pend_n == D.pend_n
 
 
-def test_long_prompt_start_eight_layers():
-    """The long single-sequence shape: 8 layers from position 0, the first
-    4 blocks of the prompt per layer with an admit of all layers after each
-    block, then decode steps; every output and the final state."""
-    gu.log("case long prompt, 8 layers")
-    w = synth.WORKLOADS["long_b1"]
-    seed = 55
-    st = synth.initial_state(w, seed)
-    S = gu.gpu_state(w, st)
-    o = OracleState.from_synth(st)
-    wg = synth.gate_weights(w, seed)
-    wg_dev = [gu.to_dev(wg[l]) for l in range(w.L)]
-    step = 0
-    for blk in range(4):
-        for l in range(w.L):
-            x = synth.block_inputs(w, seed, l, step, w.C)
-            vm = gu.vmax(o.ring_v[l], o.bank_v[l], x["v"])
-            out = _prefill(S, l, x, wg_dev[l])
-            ref = o.prefill_block(l, x["q"], x["k"], x["v"], x["ck"], x["cv"], x["cs"], wg[l])
-            gu.check_out(out, ref, f"long block {blk} layer {l}", p_bf16_vmax=vm)
-        S.admit(-1)
-        for l in range(w.L):
-            o.admit(l)
-        step += w.C
-    for s in range(4):
-        for l in range(w.L):
-            xs = synth.step_inputs(w, seed, l, step)
-            outd = gu.decode(S, l, gu.inputs_to_dev(xs), wg_dev[l])
-            refd = o.decode_step(l, xs["q"], xs["k"], xs["v"], xs["ck"], xs["cv"], xs["cs"], wg[l])
-            gu.check_out(outd, refd, f"long decode step {step} layer {l}")
-        step += 1
-    torch.cuda.synchronize()
-    gu.check_state(S, o, "long end")
-
-
 @pytest.mark.parametrize("n", [256, 60])
 @pytest.mark.parametrize("B", [2, 4, 8])
 def test_launch_plans(B, n):
