@@ -1024,7 +1024,59 @@ hipError_t launch_whole(const DecodeArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
+// The launch rule below: true for a whole-unit launch (and *one: one-wave
+// workgroups), false for the split launch.
+bool whole_unit_launch(const DecodeArgs& a, bool* one) {
+  const bool qa = a.qa != nullptr;
+  const int waves = kWaves * (qa ? resident_workgroups<true, true, kWaves>()
+                                 : resident_workgroups<true, false, kWaves>());
+  const int rounds = (a.units + waves - 1) / waves;
+  const int last = a.units - (rounds - 1) * waves;
+  const bool wide = (int64_t)last * 8 >= (int64_t)waves * 5;  // last round >= 5/8 of the waves
+  const bool mid = rounds > 1 && (int64_t)last * 8 >= (int64_t)waves * 3;  // later round >= 3/8
+  // one-wave workgroups with at least one unit per wave; four-wave ones
+  // for a single round (5/8 of the waves or more)
+  *one = a.units >= waves || !wide;
+  return wide || mid;
+}
+
+// Split-K partials for the allocation-free entry point: a static device
+// array, one per GPU the library runs on, held until the process ends.
+// Host code never names it directly (its name there is a host stand-in,
+// not a device address); it uses the address from hipGetSymbolAddress.
+static __device__ __align__(256) float scratch[kStaticScratchBytes / sizeof(float)];
+
 }  // namespace
+
+size_t decode_scratch_bytes(const DecodeArgs& a) {
+  bool one = false;
+  if (whole_unit_launch(a, &one)) return 0;
+  return (size_t)a.units * (a.splits_ring + a.splits_bank) * kPart * sizeof(float);
+}
+
+hipError_t static_scratch(int device, float** out) {
+  static std::atomic<float*> cached[64];  // per device, zero-initialised
+  if (device < 0 || device >= 64) return hipErrorInvalidDevice;
+  float* p = cached[device].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e != hipSuccess) return e;
+    if (cur != device && (e = hipSetDevice(device)) != hipSuccess) return e;
+    void* addr = nullptr;
+    e = hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch));
+    if (cur != device) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess) e = e2;
+    }
+    if (e != hipSuccess) return e;
+    if (addr == nullptr) return hipErrorInvalidSymbol;
+    p = static_cast<float*>(addr);
+    cached[device].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return hipSuccess;
+}
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   // Whole-unit launch when the last round of units occupies at least 5/8
@@ -1043,16 +1095,8 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   // against 281 at 192); below 5/8, one-wave ones again (232 against 240
   // at 144).
   const bool qa = a.qa != nullptr;
-  const int waves = kWaves * (qa ? resident_workgroups<true, true, kWaves>()
-                                 : resident_workgroups<true, false, kWaves>());
-  const int rounds = (a.units + waves - 1) / waves;
-  const int last = a.units - (rounds - 1) * waves;
-  const bool wide = (int64_t)last * 8 >= (int64_t)waves * 5;  // last round >= 5/8 of the waves
-  const bool mid = rounds > 1 && (int64_t)last * 8 >= (int64_t)waves * 3;  // later round >= 3/8
-  if (wide || mid) {
-    // one-wave workgroups with at least one unit per wave; four-wave ones
-    // for a single round (5/8 of the waves or more)
-    const bool one = a.units >= waves || !wide;
+  bool one = false;
+  if (whole_unit_launch(a, &one)) {
     hipError_t e = qa ? (one ? launch_whole<true, 1>(a, s) : launch_whole<true, kWaves>(a, s))
                       : (one ? launch_whole<false, 1>(a, s) : launch_whole<false, kWaves>(a, s));
     if (e != hipSuccess || a.pos == nullptr) return e;

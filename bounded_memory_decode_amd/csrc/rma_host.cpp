@@ -450,6 +450,37 @@ int rma_decode_step_at(rma_state* st, int32_t layer, const int32_t* pos, const v
   return RMA_OK;
 }
 
+int rma_decode_step_at_static(rma_state* st, int32_t layer, const int32_t* pos, const void* q,
+                              const void* q_anchor, const void* k, const void* v,
+                              const void* cand_k, const void* cand_v, const float* cand_score,
+                              const float* w_g, void* out, void* stream) {
+  int rc = check_state(st, layer);
+  if (rc != RMA_OK) return rc;
+  if (!aligned4(pos) || !aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(cand_k) ||
+      !aligned16(cand_v) || !cand_score || !w_g || !aligned16(out) ||
+      (q_anchor && !aligned16(q_anchor)))
+    return RMA_E_ARG;
+  const rma_config& c = st->cfg;
+  const int64_t H = c.q_heads, G = c.kv_groups;
+  rma::DecodeArgs a = decode_args(st, layer, 0, q, k, v, cand_k, cand_v, cand_score, w_g, out,
+                                  H * kD, G * kD, G, H * kD);
+  a.pos = pos;
+  a.qa = static_cast<const uint16_t*>(q_anchor);
+  // the partials go to the library's static array of the state's device
+  // instead of the state's scratch region; nothing is allocated
+  if (rma::decode_scratch_bytes(a) > rma::kStaticScratchBytes) return RMA_E_SCRATCH;
+  hipPointerAttribute_t attr;
+  hipError_t e = hipPointerGetAttributes(&attr, st->base);
+  if (e != hipSuccess) return hip_fail(st, e);
+  float* part = nullptr;
+  e = rma::static_scratch(attr.device, &part);
+  if (e != hipSuccess) return hip_fail(st, e);
+  a.part = part;
+  e = rma::launch_decode(a, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(st, e);
+  return RMA_OK;
+}
+
 int rma_prefill_block_at(rma_state* st, int32_t layer, int32_t n_tokens, const int32_t* pos,
                          const void* q, const void* q_anchor, const void* k, const void* v,
                          const void* cand_k, const void* cand_v, const float* cand_score,
@@ -495,6 +526,9 @@ const char* rma_strerror(int status) {
     case RMA_E_NOT_BOUNDARY: return "not at a block boundary";
     case RMA_E_HIP: return "HIP launch failed";
     case RMA_E_UNSUPPORTED: return "geometry not supported by the kernels";
+    case RMA_E_SCRATCH:
+      return "the call's split-K partials exceed the library's static scratch array "
+             "(RMA_STATIC_SCRATCH_BYTES); use rma_decode_step_at";
     default: return "unknown status";
   }
 }

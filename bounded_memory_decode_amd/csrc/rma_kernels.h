@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "rma.h"
+
 namespace rma {
 
 constexpr int kD = 256;       // head dimension the kernels are built for
@@ -72,6 +74,16 @@ struct DecodeArgs {
 // The decode of one token; with per-sequence positions (a.pos), also the
 // admit of every unit whose block the token completes.
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
+
+// Bytes of split-K partials (a.part) launch_decode(a) writes and reads on
+// the current device: 0 when it takes the whole-unit launch.
+size_t decode_scratch_bytes(const DecodeArgs& a);
+
+// Size of the library's static device scratch array (the partials of the
+// allocation-free decode call), and its address on `device`, looked up
+// once per device with hipGetSymbolAddress and cached.
+constexpr size_t kStaticScratchBytes = RMA_STATIC_SCRATCH_BYTES;
+hipError_t static_scratch(int device, float** out);
 
 // A chunked-prefill block of one layer.
 struct PrefillArgs {

@@ -26,11 +26,14 @@ LIB_PATH = os.environ.get("RMA_LIBRARY") or os.path.join(_HERE, "librma.so")
 RMA_MAX_LAYERS = 64
 RMA_OK, RMA_E_ARG, RMA_E_PENDING_FULL, RMA_E_NOT_BOUNDARY, RMA_E_HIP, RMA_E_UNSUPPORTED = \
     0, -1, -2, -3, -4, -5
+RMA_E_SCRATCH = -6
+RMA_STATIC_SCRATCH_BYTES = 40 << 20
 
 # every symbol include/rma.h declares
 EXPORTS = ("rma_config_default", "rma_state_bytes", "rma_state_layout", "rma_state_init",
            "rma_decode_step", "rma_prefill_block", "rma_admit", "rma_decode_step_at",
-           "rma_prefill_block_at", "rma_seq_reset", "rma_strerror")
+           "rma_prefill_block_at", "rma_seq_reset", "rma_strerror",
+           "rma_decode_step_at_static")
 
 
 class Config(ctypes.Structure):
@@ -88,6 +91,8 @@ def lib() -> ctypes.CDLL:
         L.rma_admit.restype = ctypes.c_int
         L.rma_decode_step_at.argtypes = [ctypes.POINTER(_State), ctypes.c_int32] + [_P] * 11
         L.rma_decode_step_at.restype = ctypes.c_int
+        L.rma_decode_step_at_static.argtypes = [ctypes.POINTER(_State), ctypes.c_int32] + [_P] * 11
+        L.rma_decode_step_at_static.restype = ctypes.c_int
         L.rma_prefill_block_at.argtypes = [ctypes.POINTER(_State), ctypes.c_int32,
                                            ctypes.c_int32] + [_P] * 11
         L.rma_prefill_block_at.restype = ctypes.c_int
@@ -314,6 +319,24 @@ class State:
         _check(lib().rma_decode_step_at(ctypes.byref(self._st), int(layer), p, ptrs[0], qa,
                                         *ptrs[1:], _stream_handle(self.device)),
                "rma_decode_step_at")
+        return out
+
+    def decode_step_at_static(self, layer: int, pos: torch.Tensor, q, k, v, cand_k, cand_v,
+                              cand_score, w_g, out: torch.Tensor,
+                              q_anchor: Optional[torch.Tensor] = None) -> torch.Tensor:
+        """decode_step_at through the allocation-free entry point: the
+        split-K partials go to the library's static device array, not to the
+        state's scratch region.  `out` must be given (nothing is allocated
+        here either).  Calls that overlap on one GPU race on that array."""
+        if out is None:
+            raise ValueError("decode_step_at_static: pass `out` (the call allocates nothing)")
+        out, ptrs = self._decode_ptrs(q, k, v, cand_k, cand_v, cand_score, w_g, out)
+        p = _dev(pos, torch.int32, (self.batch,), "pos", self.device)
+        qa = None if q_anchor is None else _dev(q_anchor, torch.bfloat16, tuple(q.shape),
+                                                "q_anchor", self.device)
+        _check(lib().rma_decode_step_at_static(ctypes.byref(self._st), int(layer), p, ptrs[0], qa,
+                                               *ptrs[1:], _stream_handle(self.device)),
+               "rma_decode_step_at_static")
         return out
 
     def prefill_block_at(self, layer: int, pos: torch.Tensor, q, k, v, cand_k, cand_v,

@@ -79,6 +79,7 @@ extern "C" {
 #define RMA_E_NOT_BOUNDARY (-3) /* admit with < C pending; prefill off a block start */
 #define RMA_E_HIP (-4)          /* a HIP launch failed; code in rma_state.hip_error */
 #define RMA_E_UNSUPPORTED (-5)  /* geometry the kernels are not built for */
+#define RMA_E_SCRATCH (-6)      /* partials beyond RMA_STATIC_SCRATCH_BYTES */
 
 /* Layer geometry.  EdgeRock values (rma_config_default): 8 layers,
  * 16 query heads, 4 KV groups, head_dim 256, window 1024 (ring 1023),
@@ -279,6 +280,26 @@ int rma_prefill_block_at(rma_state* st, int32_t layer, int32_t n_tokens, const i
                          const void* q, const void* q_anchor, const void* k, const void* v,
                          const void* cand_k, const void* cand_v, const float* cand_score,
                          const float* w_g, void* out, void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation):
+ * rma_decode_step_at with the same arguments, results and admits, whose
+ * split-K partials (the small-batch launches) go to a static device array
+ * of RMA_STATIC_SCRATCH_BYTES instead of the state's scratch region.  The
+ * library holds one such array on every GPU it runs on, from the first
+ * call on that GPU until the process ends; the call itself allocates
+ * nothing.  Every call on a GPU shares that GPU's array, so calls that
+ * overlap on one GPU (other streams, other states) race: order them.  The
+ * kernels write every partial before reading it; nothing needs clearing.
+ * Returns RMA_E_SCRATCH, before anything is enqueued, when the batch's
+ * partials exceed the array (never at the EdgeRock geometry, whose
+ * largest need is 36.3 MiB, at batches 144 and 288); otherwise as
+ * rma_decode_step_at. */
+#define RMA_STATIC_SCRATCH_BYTES ((size_t)40 << 20)
+int rma_decode_step_at_static(rma_state* st, int32_t layer, const int32_t* pos, const void* q,
+                              const void* q_anchor, const void* k, const void* v,
+                              const void* cand_k, const void* cand_v, const float* cand_score,
+                              const float* w_g, void* out, void* stream);
 
 /* Give sequences first .. first+count-1 (every layer and group) a bank of
  * `bank_n` committed anchors (0 for a new sequence in a reused batch slot;

@@ -1,0 +1,70 @@
+"""The allocation-free decode entry point (rma_decode_step_at_static)
+against rma_decode_step_at: same inputs, same positions, two identical
+states; the outputs and every state region must agree bit for bit.  Two
+calls in a row, the second with a smaller batch (the static array keeps the
+first call's partials), then a batch whose partials exceed the array."""
+import numpy as np
+import pytest
+import torch
+
+from bounded_memory_decode_amd import rma, synth
+import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_pair(B, seed, steps, anchor_query):
+    w = synth.WORKLOADS["layer_b1"].with_(B=B, bank_n=900)
+    st = synth.initial_state(w, seed)
+    A = gu.gpu_state(w, st)   # allocation-free entry point
+    D = gu.gpu_state(w, st)   # the entry point it is a variant of
+    wg = gu.to_dev(synth.gate_weights(w, seed)[0])
+    # positions a few tokens before a block end, so that some sequences
+    # complete their block (and are admitted) inside the run
+    pos0 = torch.tensor([w.t0 - 3 + (b % 5) for b in range(B)], dtype=torch.int32,
+                        device=gu.DEV)
+    pa, pd = pos0.clone(), pos0.clone()
+    oa = torch.empty((B, w.H, w.d), dtype=torch.bfloat16, device=gu.DEV)
+    od = torch.empty_like(oa)
+    for s in range(steps):
+        x = gu.inputs_to_dev(synth.step_inputs(w, seed, 0, s))
+        qa = gu.to_dev(synth.anchor_query(w, seed, 0, s)) if anchor_query else None
+        A.decode_step_at_static(0, pa, x["q"], x["k"], x["v"], x["ck"], x["cv"], x["cs"], wg, oa,
+                                q_anchor=qa)
+        D.decode_step_at(0, pd, x["q"], x["k"], x["v"], x["ck"], x["cv"], x["cs"], wg, od,
+                         q_anchor=qa)
+        assert torch.equal(oa.view(torch.int16), od.view(torch.int16)), f"batch {B} step {s}"
+        pa += 1
+        pd += 1
+    torch.cuda.synchronize()
+    for name in gu.REGIONS + ("bank_n",):
+        assert torch.equal(A.read(name), D.read(name)), f"batch {B}: region {name}"
+
+
+def test_static_scratch_decode_matches_state_scratch_decode():
+    gu.log("case allocation-free decode: batch 32, then batch 4")
+    _run_pair(32, 90, 6, anchor_query=False)   # one-tile parts: 16.1 MiB of partials
+    _run_pair(4, 91, 6, anchor_query=True)     # smaller input, separate anchor query
+
+
+def test_static_scratch_rejects_partials_beyond_the_array():
+    """Ring 1,535, bank 1,792, batch 144: the split launch cuts each read of
+    576 units into 26 parts, 61.8 MB of partials, beyond the 40 MiB array.
+    The call is refused before anything is enqueued."""
+    gu.log("case allocation-free decode: partials beyond the array")
+    cfg = rma.config_default(layers=1, window=1536, bank_cap=1792)
+    B, H, G, d = 144, cfg.q_heads, cfg.kv_groups, cfg.head_dim
+    S = rma.State(cfg, B, gu.DEV, start_pos=0, bank_n=0)
+    bf = dict(dtype=torch.bfloat16, device=gu.DEV)
+    q = torch.zeros((B, H, d), **bf)
+    kv = torch.zeros((B, G, d), **bf)
+    cs = torch.zeros((B, G), dtype=torch.float32, device=gu.DEV)
+    wg = torch.zeros((H, d), dtype=torch.float32, device=gu.DEV)
+    out = torch.empty((B, H, d), **bf)
+    pos = torch.zeros((B,), dtype=torch.int32, device=gu.DEV)
+    with pytest.raises(rma.RmaError) as e:
+        S.decode_step_at_static(0, pos, q, kv, kv, kv, kv, cs, wg, out)
+    assert e.value.code == rma.RMA_E_SCRATCH
+    torch.cuda.synchronize()
+    assert torch.equal(S.read("bank_n"), torch.zeros((1, B, G), dtype=torch.int32,
+                                                      device=gu.DEV))
