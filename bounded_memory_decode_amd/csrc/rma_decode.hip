@@ -314,13 +314,19 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs& a, int u, int lane
     ds = fmaf(bf_hi(q8.w), bf_hi(kv.w), ds);
     ds = lane < 32 ? ds : 0.f;
     const uint2 q2 = reinterpret_cast<const uint2*>((kQA ? qa_w : q_w) + h * kChunks)[lane];
-    const float4 w4 = reinterpret_cast<const float4*>(a.w_g + (size_t)(g * kHpg + h) * kD)[lane];
+    const float4 w4 = reinterpret_cast<const float4*>(
+        a.w_g + (size_t)(a.gate_group ? g : g * kHpg + h) * kD)[lane];
     float dz = bf_lo(q2.x) * w4.x;
     dz = fmaf(bf_hi(q2.x), w4.y, dz);
     dz = fmaf(bf_lo(q2.y), w4.z, dz);
     dz = fmaf(bf_hi(q2.y), w4.w, dz);
     sc[h] = wave_sum_u(ds) * a.sl2e;
     z[h] = wave_sum_u(dz);
+  }
+  if (a.gate_group) {  // one gate for the group: its mean anchor query . w_g[g]
+    const float zm = ((z[0] + z[1]) + (z[2] + z[3])) * (1.f / kHpg);
+#pragma unroll
+    for (int h = 0; h < kHpg; ++h) z[h] = zm;
   }
   // the current V: lanes 32-63 hold it; bring chunk c32 to lane c32
   uint4 v4;
@@ -888,7 +894,8 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   const uint2 qav = *reinterpret_cast<const uint2*>((a.qa ? a.qa : a.q) + qo);
   const uint2 kv = *reinterpret_cast<const uint2*>(a.k + kvo + 4 * lane);
   const uint2 vv = *reinterpret_cast<const uint2*>(a.v + kvo + 4 * lane);
-  const float4 wv = *reinterpret_cast<const float4*>(a.w_g + (size_t)(g * kHpg + h) * kD + 4 * lane);
+  const float4 wv = *reinterpret_cast<const float4*>(
+      a.w_g + (size_t)(a.gate_group ? g : g * kHpg + h) * kD + 4 * lane);
   const int n = scalar_load(a.bank_n + u);
 
   // q.k_t (current-token score) and qa.w_g (gate argument)
@@ -896,10 +903,30 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   dk = fmaf(bf_hi(qv.x), bf_hi(kv.x), dk);
   dk = fmaf(bf_lo(qv.y), bf_lo(kv.y), dk);
   dk = fmaf(bf_hi(qv.y), bf_hi(kv.y), dk);
-  float dz = bf_lo(qav.x) * wv.x;
-  dz = fmaf(bf_hi(qav.x), wv.y, dz);
-  dz = fmaf(bf_lo(qav.y), wv.z, dz);
-  dz = fmaf(bf_hi(qav.y), wv.w, dz);
+  float dz;
+  if (a.gate_group) {  // the mean of the group's anchor queries . w_g[g]
+    const uint16_t* qs = (a.qa ? a.qa : a.q) + (size_t)b * a.q_bs + (size_t)g * kHpg * kD +
+                         4 * lane;
+    float m0 = 0.f, m1 = 0.f, m2 = 0.f, m3 = 0.f;
+#pragma unroll
+    for (int hh = 0; hh < kHpg; ++hh) {
+      const uint2 x = *reinterpret_cast<const uint2*>(qs + (size_t)hh * kD);
+      m0 += bf_lo(x.x);
+      m1 += bf_hi(x.x);
+      m2 += bf_lo(x.y);
+      m3 += bf_hi(x.y);
+    }
+    dz = m0 * wv.x;
+    dz = fmaf(m1, wv.y, dz);
+    dz = fmaf(m2, wv.z, dz);
+    dz = fmaf(m3, wv.w, dz);
+    dz *= 1.f / kHpg;
+  } else {
+    dz = bf_lo(qav.x) * wv.x;
+    dz = fmaf(bf_hi(qav.x), wv.y, dz);
+    dz = fmaf(bf_lo(qav.y), wv.z, dz);
+    dz = fmaf(bf_hi(qav.y), wv.w, dz);
+  }
   const float sc = wave_sum_u(dk) * a.sl2e;
   dz = wave_sum_u(dz);
 

@@ -28,7 +28,8 @@ int check_config(const rma_config* c) {
   if (!c) return RMA_E_ARG;
   if (c->layers < 1 || c->layers > RMA_MAX_LAYERS || c->q_heads < 1 || c->kv_groups < 1 ||
       c->head_dim < 1 || c->window < 2 || c->bank_cap < 1 || c->commit < 1 ||
-      !std::isfinite(c->scale) || c->q_heads % c->kv_groups != 0)
+      !std::isfinite(c->scale) || c->q_heads % c->kv_groups != 0 ||
+      (c->gate != RMA_GATE_HEAD && c->gate != RMA_GATE_GROUP))
     return RMA_E_ARG;
   if (c->head_dim != kD || c->q_heads != kHpg * c->kv_groups) return RMA_E_UNSUPPORTED;
   if (c->window > 4097 || c->commit > 256 || c->bank_cap + c->commit > 2048)
@@ -202,6 +203,7 @@ rma::DecodeArgs decode_args(const rma_state* st, int32_t layer, int64_t t, const
   a.splits_bank = sp.bank;
   a.tiles_ring = sp.tiles_ring;
   a.tiles_bank = sp.tiles_bank;
+  a.gate_group = c.gate == RMA_GATE_GROUP;
   a.sl2e = (float)((double)c.scale * 1.4426950408889634);
   return a;
 }
@@ -247,6 +249,7 @@ rma::PrefillArgs prefill_args(const rma_state* st, int32_t layer, int32_t n_toke
   a.C = C;
   a.n = n_tokens;
   a.P = P;
+  a.gate_group = c.gate == RMA_GATE_GROUP;
   a.sl2e = (float)((double)c.scale * 1.4426950408889634);
   return a;
 }
@@ -305,6 +308,7 @@ int rma_config_default(rma_config* cfg) {
   cfg->bank_cap = 1024;
   cfg->commit = 256;
   cfg->scale = 0.0625f;
+  cfg->gate = RMA_GATE_HEAD;
   return RMA_OK;
 }
 

@@ -40,7 +40,7 @@ struct DecodeArgs {
   const uint16_t* ck;
   const uint16_t* cv;
   const float* cs;         // [B][G]
-  const float* w_g;        // [H][D]
+  const float* w_g;        // [H][D], or [G][D] with gate_group
   uint16_t* out;           // [B][H][D]
   uint16_t* ring_k;        // layer base, unit stride Rk*D
   uint16_t* ring_v;
@@ -68,6 +68,7 @@ struct DecodeArgs {
   int pend_slot;           // lockstep: t mod C
   int splits_ring, splits_bank;
   int tiles_ring, tiles_bank;  // tiles per split
+  int gate_group;          // 1: one gate per (token, group) from the mean anchor query
   float sl2e;              // scale * log2(e)
 };
 
@@ -94,7 +95,7 @@ struct PrefillArgs {
   const uint16_t* ck;
   const uint16_t* cv;
   const float* cs;         // [B][n][G]
-  const float* w_g;        // [H][D]
+  const float* w_g;        // [H][D], or [G][D] with gate_group
   uint16_t* out;           // [B][n][H][D]
   uint16_t* ring_k;        // layer bases as in DecodeArgs
   uint16_t* ring_v;
@@ -114,6 +115,7 @@ struct PrefillArgs {
   int Rk;                  // ring K plane slots (ring_k_slots(R))
   int n;                   // tokens in the block (1 .. C)
   int64_t P;               // lockstep: position of the block's first token
+  int gate_group;          // 1: one gate per (token, group) from the mean anchor query
   float sl2e;              // scale * log2(e)
 };
 

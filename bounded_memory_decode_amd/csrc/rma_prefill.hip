@@ -491,7 +491,7 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_kernel(PrefillArgs a
   if (a.qa != nullptr && t_bank == 0) load_q(a.qa);
   float z = 0.f;
   {
-    const float* wrow = a.w_g + (size_t)(g * kHpg + q_head) * kD;
+    const float* wrow = a.w_g + (size_t)(a.gate_group ? g : g * kHpg + q_head) * kD;
 #pragma unroll
     for (int st = 0; st < 8; ++st) {
       const float4 w0 = reinterpret_cast<const float4*>(wrow + st * 32 + lg * 8)[0];
@@ -508,6 +508,11 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_kernel(PrefillArgs a
     }
     z += __shfl_xor(z, 16, 64);
     z += __shfl_xor(z, 32, 64);
+    if (a.gate_group) {  // the token's 4 heads sit in lanes 4j .. 4j+3 of a row
+      z += __shfl_xor(z, 1, 64);
+      z += __shfl_xor(z, 2, 64);
+      z *= 1.f / kHpg;
+    }
   }
   const float gate = tanhf(z);
 
@@ -609,12 +614,33 @@ __device__ __forceinline__ void merge_rows(const PrefillArgs& a, int bx) {
     l[i] = on ? pi[kD + 1] : 0.f;
   }
   const uint16_t* qsrc = a.qa != nullptr ? a.qa : a.q;
-  const uint2 qv = *reinterpret_cast<const uint2*>(qsrc + (size_t)row * kD + 4 * lane);
-  const float4 wv = *reinterpret_cast<const float4*>(a.w_g + (size_t)hq * kD + 4 * lane);
-  float z = __uint_as_float(qv.x << 16) * wv.x;
-  z = fmaf(__uint_as_float(qv.x & 0xffff0000u), wv.y, z);
-  z = fmaf(__uint_as_float(qv.y << 16), wv.z, z);
-  z = fmaf(__uint_as_float(qv.y & 0xffff0000u), wv.w, z);
+  float z;
+  if (a.gate_group) {  // the mean of the token's group of anchor queries . w_g[g]
+    const int h0 = hq - hq % kHpg;
+    const float4 wv = *reinterpret_cast<const float4*>(a.w_g + (size_t)(h0 / kHpg) * kD + 4 * lane);
+    float m0 = 0.f, m1 = 0.f, m2 = 0.f, m3 = 0.f;
+#pragma unroll
+    for (int hh = 0; hh < kHpg; ++hh) {
+      const uint2 x = *reinterpret_cast<const uint2*>(qsrc + (size_t)(row - hq + h0 + hh) * kD +
+                                                       4 * lane);
+      m0 += __uint_as_float(x.x << 16);
+      m1 += __uint_as_float(x.x & 0xffff0000u);
+      m2 += __uint_as_float(x.y << 16);
+      m3 += __uint_as_float(x.y & 0xffff0000u);
+    }
+    z = m0 * wv.x;
+    z = fmaf(m1, wv.y, z);
+    z = fmaf(m2, wv.z, z);
+    z = fmaf(m3, wv.w, z);
+    z *= 1.f / kHpg;
+  } else {
+    const uint2 qv = *reinterpret_cast<const uint2*>(qsrc + (size_t)row * kD + 4 * lane);
+    const float4 wv = *reinterpret_cast<const float4*>(a.w_g + (size_t)hq * kD + 4 * lane);
+    z = __uint_as_float(qv.x << 16) * wv.x;
+    z = fmaf(__uint_as_float(qv.x & 0xffff0000u), wv.y, z);
+    z = fmaf(__uint_as_float(qv.y << 16), wv.z, z);
+    z = fmaf(__uint_as_float(qv.y & 0xffff0000u), wv.w, z);
+  }
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) z += __shfl_xor(z, off, 64);
   const float gate = tanhf(z);

@@ -27,20 +27,22 @@ RMA_MAX_LAYERS = 64
 RMA_OK, RMA_E_ARG, RMA_E_PENDING_FULL, RMA_E_NOT_BOUNDARY, RMA_E_HIP, RMA_E_UNSUPPORTED = \
     0, -1, -2, -3, -4, -5
 RMA_E_SCRATCH = -6
+RMA_GATE_HEAD, RMA_GATE_GROUP = 0, 1
 RMA_STATIC_SCRATCH_BYTES = 40 << 20
 
-# every symbol include/rma.h declares
+# every symbol include/rma.h and include/rma_calib.h declare
 EXPORTS = ("rma_config_default", "rma_state_bytes", "rma_state_layout", "rma_state_init",
            "rma_decode_step", "rma_prefill_block", "rma_admit", "rma_decode_step_at",
            "rma_prefill_block_at", "rma_seq_reset", "rma_strerror",
-           "rma_decode_step_at_static")
+           "rma_decode_step_at_static", "rma_calib_stream_read")
 
 
 class Config(ctypes.Structure):
     _fields_ = [("layers", ctypes.c_int32), ("q_heads", ctypes.c_int32),
                 ("kv_groups", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("window", ctypes.c_int32), ("bank_cap", ctypes.c_int32),
-                ("commit", ctypes.c_int32), ("scale", ctypes.c_float)]
+                ("commit", ctypes.c_int32), ("scale", ctypes.c_float),
+                ("gate", ctypes.c_int32)]
 
     def __repr__(self):
         return "Config(" + ", ".join(f"{n}={getattr(self, n)}" for n, _ in self._fields_) + ")"
@@ -99,6 +101,8 @@ def lib() -> ctypes.CDLL:
         L.rma_seq_reset.argtypes = [ctypes.POINTER(_State), ctypes.c_int32, ctypes.c_int32,
                                     ctypes.c_int32, _P]
         L.rma_seq_reset.restype = ctypes.c_int
+        L.rma_calib_stream_read.argtypes = [_P, ctypes.c_size_t, ctypes.c_int32, _P, _P]
+        L.rma_calib_stream_read.restype = ctypes.c_int
         L.rma_strerror.argtypes = [ctypes.c_int]
         L.rma_strerror.restype = ctypes.c_char_p
         _lib = L
@@ -133,6 +137,23 @@ def state_layout(cfg: Config, batch: int) -> Layout:
     out = Layout()
     _check(lib().rma_state_layout(ctypes.byref(cfg), batch, ctypes.byref(out)), "rma_state_layout")
     return out
+
+
+def calib_stream_read(buf: torch.Tensor, waves: int, sink: torch.Tensor):
+    """Enqueue one streaming read of the whole device buffer `buf` (a
+    contiguous tensor whose byte size is a multiple of waves * 8 KiB) with
+    `waves` waves; each wave's xor of its words goes to sink[w] (a device
+    int32 tensor of `waves` entries).  Measurement support, not part of the
+    layer step."""
+    if not buf.is_contiguous() or sink.dtype != torch.int32 or sink.numel() < waves or \
+            sink.device != buf.device:
+        raise ValueError("calib_stream_read: contiguous buffer and an int32 sink of `waves` "
+                         "entries on the same device expected")
+    nbytes = buf.numel() * buf.element_size()
+    rc = lib().rma_calib_stream_read(buf.data_ptr(), nbytes, int(waves), sink.data_ptr(),
+                                     _stream_handle(buf.device))
+    if rc != 0:
+        raise RuntimeError(f"rma_calib_stream_read: status {rc}")
 
 
 def _stream_handle(device) -> Optional[int]:
@@ -263,6 +284,11 @@ class State:
         return v[layers, batch].clone()
 
     # ------------------------------------------------------------- compute
+    def _wg_rows(self) -> int:
+        """Rows of the gate weights: one per query head, or one per KV group
+        with cfg.gate == RMA_GATE_GROUP."""
+        return self.cfg.kv_groups if self.cfg.gate == RMA_GATE_GROUP else self.cfg.q_heads
+
     def _decode_ptrs(self, q, k, v, cand_k, cand_v, cand_score, w_g, out):
         c, B = self.cfg, self.batch
         H, G, d = c.q_heads, c.kv_groups, c.head_dim
@@ -273,7 +299,8 @@ class State:
                 _dev(v, bf, (B, G, d), "v", dev), _dev(cand_k, bf, (B, G, d), "cand_k", dev),
                 _dev(cand_v, bf, (B, G, d), "cand_v", dev),
                 _dev(cand_score, f32, (B, G), "cand_score", dev),
-                _dev(w_g, f32, (H, d), "w_g", dev), _dev(out, bf, (B, H, d), "out", dev)]
+                _dev(w_g, f32, (self._wg_rows(), d), "w_g", dev),
+                _dev(out, bf, (B, H, d), "out", dev)]
         return out, ptrs
 
     def _prefill_ptrs(self, q, k, v, cand_k, cand_v, cand_score, w_g, out):
@@ -287,7 +314,8 @@ class State:
                 _dev(v, bf, (B, n, G, d), "v", dev), _dev(cand_k, bf, (B, n, G, d), "cand_k", dev),
                 _dev(cand_v, bf, (B, n, G, d), "cand_v", dev),
                 _dev(cand_score, f32, (B, n, G), "cand_score", dev),
-                _dev(w_g, f32, (H, d), "w_g", dev), _dev(out, bf, (B, n, H, d), "out", dev)]
+                _dev(w_g, f32, (self._wg_rows(), d), "w_g", dev),
+                _dev(out, bf, (B, n, H, d), "out", dev)]
         return n, out, ptrs
 
     def decode_step(self, layer: int, q, k, v, cand_k, cand_v, cand_score, w_g,
@@ -336,7 +364,7 @@ class State:
                                                 "q_anchor", self.device)
         _check(lib().rma_decode_step_at_static(ctypes.byref(self._st), int(layer), p, ptrs[0], qa,
                                                *ptrs[1:], _stream_handle(self.device)),
-               "rma_decode_step_at_static")
+               "rma_decode_step_at_static", "rma_calib_stream_read")
         return out
 
     def prefill_block_at(self, layer: int, pos: torch.Tensor, q, k, v, cand_k, cand_v,

@@ -129,10 +129,12 @@ def _batch(w: Workload, batch: Optional[Sequence[int]]):
 
 # ----------------------------------------------------------------- numpy side
 
-def gate_weights(w: Workload, seed: int = 0) -> np.ndarray:
-    """w_g [L][H][d] fp32, N(0, w_std^2)."""
+def gate_weights(w: Workload, seed: int = 0, per_group: bool = False) -> np.ndarray:
+    """w_g [L][H][d] fp32, N(0, w_std^2); [L][G][d] for a gate per KV
+    group."""
     rng = _rng(seed, w, "w_g")
-    return (rng.standard_normal((w.L, w.H, w.d), dtype=np.float32)
+    rows = w.G if per_group else w.H
+    return (rng.standard_normal((w.L, rows, w.d), dtype=np.float32)
             * np.float32(w.w_std))
 
 

@@ -85,7 +85,7 @@ extern "C" {
  * 16 query heads, 4 KV groups, head_dim 256, window 1024 (ring 1023),
  * bank_cap 1024, commit 256, scale 1/16 (model card history-component
  * table; Rock Matrix models page spec list; head_dim from the card's
- * persistent-history MiB table).  Limits: 1 <= layers <= RMA_MAX_LAYERS,
+ * persistent-history MiB table), gate per head.  Limits: 1 <= layers <= RMA_MAX_LAYERS,
  * q_heads == 4 * kv_groups, head_dim == 256, 2 <= window <= 4097,
  * 1 <= bank_cap, 1 <= commit <= 256, commit <= window - 1 (a block's
  * tokens take distinct ring slots), bank_cap + commit <= 2048. */
@@ -98,7 +98,18 @@ typedef struct {
   int32_t bank_cap;  /* N: committed anchors per (sequence, layer, group) */
   int32_t commit;    /* C: pending slots = tokens between admits */
   float scale;       /* softmax scale on q.k, normally 1/sqrt(head_dim) */
+  int32_t gate;      /* RMA_GATE_HEAD or RMA_GATE_GROUP (below) */
 } rma_config;
+
+/* Gate granularity (rma_config.gate).  RMA_GATE_HEAD: one gate per (token,
+ * query head), tanh(qa_h . w_g[h]), w_g [q_heads][head_dim].
+ * RMA_GATE_GROUP: one gate per (token, KV group) shared by the group's
+ * heads, tanh(mean of the group's qa_h . w_g[g]), w_g [kv_groups][head_dim]
+ * (a reading of the models page's and tpsreport's "separate RMA modules",
+ * whose selection is per KV group; the pages fix no gate form).  qa is the
+ * anchor query where a call takes one, else q. */
+#define RMA_GATE_HEAD 0
+#define RMA_GATE_GROUP 1
 
 /* Byte offsets of the regions inside the state buffer.  Every region is
  * indexed by unit u = (layer * batch + b) * kv_groups + g first, and is
@@ -193,6 +204,8 @@ int rma_state_init(rma_state* st, const rma_config* cfg, int32_t batch,
  *   cand_k/v   [batch][kv_groups][head_dim] bf16  its candidate record
  *   cand_score [batch][kv_groups]           f32   the candidate's score
  *   w_g        [q_heads][head_dim]          f32   gate weights of the layer
+ *                                                 ([kv_groups][head_dim] with
+ *                                                 cfg.gate == RMA_GATE_GROUP)
  *   out        [batch][q_heads][head_dim]   bf16  result
  * Returns RMA_E_PENDING_FULL (state unchanged) when C candidates are
  * pending; call rma_admit first. */

@@ -36,7 +36,8 @@ def build(force: bool = True) -> str:
 class _Cfg(ctypes.Structure):
     _fields_ = [("L", ctypes.c_int32), ("H", ctypes.c_int32), ("G", ctypes.c_int32),
                 ("d", ctypes.c_int32), ("R", ctypes.c_int32), ("N", ctypes.c_int32),
-                ("C", ctypes.c_int32), ("scale", ctypes.c_double)]
+                ("C", ctypes.c_int32), ("scale", ctypes.c_double),
+                ("gate_group", ctypes.c_int32)]
 
 
 _P = ctypes.c_void_p
@@ -70,6 +71,8 @@ def lib():
         L.orc_round_bf16_array.restype = None
         L.orc_num_threads.argtypes = []
         L.orc_num_threads.restype = ctypes.c_int
+        L.orc_set_num_threads.argtypes = [ctypes.c_int]
+        L.orc_set_num_threads.restype = None
         _lib = L
     return _lib
 
@@ -95,6 +98,12 @@ def num_threads() -> int:
     return lib().orc_num_threads()
 
 
+def set_num_threads(n: int) -> None:
+    """Threads of the oracle's parallel loops from now on (results do not
+    depend on it)."""
+    lib().orc_set_num_threads(int(n))
+
+
 class OracleError(RuntimeError):
     def __init__(self, code: int, what: str):
         super().__init__(f"{what}: oracle status {code}")
@@ -106,10 +115,14 @@ class OracleState:
 
     def __init__(self, L: int, B: int, H: int = 16, G: int = 4, d: int = 256,
                  R: int = 1023, N: int = 1024, C: int = 256,
-                 scale: Optional[float] = None):
+                 scale: Optional[float] = None, gate_group: bool = False):
+        """gate_group: one gate per (token, KV group) from the mean of the
+        group's anchor queries and gate weights [G][d] per layer, instead
+        of one gate per (token, head) with weights [H][d]."""
         self.L, self.B, self.H, self.G, self.d = L, B, H, G, d
         self.R, self.N, self.C = R, N, C
         self.scale = float(d) ** -0.5 if scale is None else float(scale)
+        self.gate_group = bool(gate_group)
         self.ring_k = np.zeros((L, B, G, R, d), np.uint16)
         self.ring_v = np.zeros((L, B, G, R, d), np.uint16)
         self.bank_k = np.zeros((L, B, G, N, d), np.uint16)
@@ -128,11 +141,11 @@ class OracleState:
 
     @classmethod
     def from_synth(cls, st: Dict[str, np.ndarray], H=16, G=4, d=256, R=1023, N=1024,
-                   C=256, scale=None) -> "OracleState":
+                   C=256, scale=None, gate_group=False) -> "OracleState":
         """Build from synth.initial_state() output (t0 must be block aligned,
         or the caller sets pend_n/pending contents itself)."""
         L, B = st["ring_k"].shape[:2]
-        o = cls(L, B, H, G, d, R, N, C, scale)
+        o = cls(L, B, H, G, d, R, N, C, scale, gate_group)
         for k in ("ring_k", "ring_v", "bank_k", "bank_v", "bscore", "bsrc", "bank_n",
                   "pend_k", "pend_v", "pscore"):
             getattr(o, k)[...] = st[k]
@@ -142,18 +155,22 @@ class OracleState:
 
     def clone(self) -> "OracleState":
         o = OracleState(self.L, self.B, self.H, self.G, self.d, self.R, self.N, self.C,
-                        self.scale)
+                        self.scale, self.gate_group)
         for k in self.ARRAYS:
             getattr(o, k)[...] = getattr(self, k)
         return o
 
     def _struct(self) -> _State:
         s = _State()
-        s.cfg = _Cfg(self.L, self.H, self.G, self.d, self.R, self.N, self.C, self.scale)
+        s.cfg = _Cfg(self.L, self.H, self.G, self.d, self.R, self.N, self.C, self.scale,
+                     int(self.gate_group))
         s.B = self.B
         for k in self.ARRAYS:
             setattr(s, k, _ptr(getattr(self, k)))
         return s
+
+    def _wg_rows(self) -> int:
+        return self.G if self.gate_group else self.H
 
     def decode_step(self, layer: int, q, k, v, ck, cv, cs, w_g,
                     compute_out: bool = True, q_anchor=None) -> Optional[np.ndarray]:
@@ -164,7 +181,7 @@ class OracleState:
         B, H, G, d = self.B, self.H, self.G, self.d
         qa = None if q_anchor is None else _c(q_anchor, np.uint16).reshape(B, H, d)
         arrs = [_c(x, np.uint16).reshape(B, G, d) for x in (k, v, ck, cv)] + \
-               [_c(cs, np.float32).reshape(B, G), _c(w_g, np.float32).reshape(H, d)]
+               [_c(cs, np.float32).reshape(B, G), _c(w_g, np.float32).reshape(self._wg_rows(), d)]
         q = _c(q, np.uint16).reshape(B, H, d)
         out = np.empty((B, H, d), np.float64) if compute_out else None
         st = self._struct()
@@ -193,7 +210,7 @@ class OracleState:
         q = q.reshape(B, n, H, d)
         qa = None if q_anchor is None else _c(q_anchor, np.uint16).reshape(B, n, H, d)
         arrs = [_c(x, np.uint16).reshape(B, n, G, d) for x in (k, v, ck, cv)] + \
-               [_c(cs, np.float32).reshape(B, n, G), _c(w_g, np.float32).reshape(H, d)]
+               [_c(cs, np.float32).reshape(B, n, G), _c(w_g, np.float32).reshape(self._wg_rows(), d)]
         out = np.empty((B, n, H, d), np.float64) if compute_out else None
         st = self._struct()
         rc = lib().orc_prefill_block(ctypes.byref(st), layer, n, _ptr(q),

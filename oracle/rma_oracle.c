@@ -73,6 +73,14 @@ int orc_num_threads(void) {
 #endif
 }
 
+void orc_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 /* ------------------------------------------------------------- indexing */
 
 static size_t unit_index(const orc_state* st, int32_t l, int32_t b, int32_t g) {
@@ -136,6 +144,11 @@ static void attend(int d, double scale, const double* q, int nk,
  *     card's "separate RMA modules" and "query-dependent read"); when no
  *     such query is given, qa = q, the attention query of the head.
  *   - Reading: heads h = g*(H/G) ... g*(H/G)+H/G-1 share group g.
+ *   - Reading (per-group gate, cfg.gate_group; the separate RMA modules of
+ *     the models page and the tpsreport "How it works" paragraph, which
+ *     select per KV group): one gate per (token, group),
+ *     tanh(<mean of the group's anchor queries, w_g[g]>), one weight
+ *     vector per group; every head of the group uses it.
  */
 static void token_output(const orc_state* st, int32_t layer, int32_t b, int32_t g,
                          int32_t hh, int64_t t, const uint16_t* qtok /*[H][d]*/,
@@ -194,7 +207,16 @@ static void token_output(const orc_state* st, int32_t layer, int32_t b, int32_t 
   }
 
   double zg = 0.0;
-  for (int i = 0; i < d; ++i) zg += qa[i] * (double)w_g[(size_t)h * d + i];
+  if (c->gate_group) {
+    /* the mean of the group's anchor queries against the group's weights */
+    double* qm = (double*)calloc((size_t)d, sizeof(double));
+    for (int h2 = g * hpg; h2 < (g + 1) * hpg; ++h2)
+      for (int i = 0; i < d; ++i) qm[i] += bf16_to_double(qatok[(size_t)h2 * d + i]);
+    for (int i = 0; i < d; ++i) zg += (qm[i] / hpg) * (double)w_g[(size_t)g * d + i];
+    free(qm);
+  } else {
+    for (int i = 0; i < d; ++i) zg += qa[i] * (double)w_g[(size_t)h * d + i];
+  }
   const double gate = tanh(zg);
   for (int i = 0; i < d; ++i) out[(size_t)h * d + i] = oloc[i] + gate * oanc[i];
   free(lk); free(lv); free(ak); free(av); free(s); free(q); free(qa); free(oloc); free(oanc);

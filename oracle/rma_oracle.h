@@ -47,6 +47,8 @@ typedef struct {
   int32_t N;      /* anchor-bank capacity per group              */
   int32_t C;      /* pending slots = commit interval             */
   double scale;   /* softmax scale applied to q.k                */
+  int32_t gate_group; /* 0: one gate per (token, head), w_g [H][d];
+                         1: one gate per (token, KV group), w_g [G][d] */
 } orc_cfg;
 
 typedef struct {
@@ -75,7 +77,8 @@ typedef struct {
  *         NULL: q
  *   k, v  [B][G][d] bf16 (current token)
  *   ck,cv [B][G][d] bf16 (candidate record)   cs [B][G] float (its score)
- *   w_g   [H][d] float (gate weights of this layer)
+ *   w_g   [H][d] float (gate weights of this layer), or [G][d] with
+ *         cfg.gate_group
  *   out   [B][H][d] double (unrounded output), may be NULL when
  *         compute_out == 0 (state update only).
  * Reads come first; then the ring write, the pending append, t += 1.
@@ -105,8 +108,11 @@ int orc_prefill_block(const orc_state* st, int32_t layer, int32_t n,
 uint16_t orc_round_bf16(double x);
 void orc_round_bf16_array(const double* x, uint16_t* y, int64_t n);
 
-/* Threads OpenMP will use for the per-(sequence, group) loops. */
+/* Threads OpenMP will use for the parallel loops. */
 int orc_num_threads(void);
+/* Threads for later parallel loops (n > 0; used to time the oracle on one
+ * core).  Results do not depend on it. */
+void orc_set_num_threads(int n);
 
 #ifdef __cplusplus
 }

@@ -32,10 +32,13 @@ def _softmax_read(q, K, V, scale):
 
 class BruteForce:
     def __init__(self, H, G, d, R, N, C, scale, t0, ring_k, ring_v, bank_k, bank_v,
-                 bscore, bsrc, bank_n):
+                 bscore, bsrc, bank_n, gate_group=False):
         """ring_*/bank_* [G][slots][d] bf16 bits for ONE sequence of ONE layer.
-        Ring slot s holds the position p in [t0-R, t0) with p % R == s."""
+        Ring slot s holds the position p in [t0-R, t0) with p % R == s.
+        gate_group: one gate per KV group, tanh of the mean anchor query of
+        the group against w_g[g] (w_g [G][d]), instead of one per head."""
         self.H, self.G, self.d, self.R, self.N, self.C = H, G, d, R, N, C
+        self.gate_group = gate_group
         self.scale = scale
         self.t = int(t0)
         self.hist_k = [dict() for _ in range(G)]
@@ -65,6 +68,8 @@ class BruteForce:
             lo = max(0, t - self.R)
             Kl = np.stack([self.hist_k[g][p] for p in range(lo, t + 1)])
             Vl = np.stack([self.hist_v[g][p] for p in range(lo, t + 1)])
+            qsrc = q if q_anchor is None else q_anchor
+            qbar = np.mean([_f(qsrc[g * hpg + i]) for i in range(hpg)], axis=0)
             for hh in range(hpg):
                 h = g * hpg + hh
                 qh = _f(q[h])
@@ -76,7 +81,11 @@ class BruteForce:
                     oa = _softmax_read(qa, Kb, Vb, self.scale)
                 else:
                     oa = np.zeros(d)
-                out[h] = ol + np.tanh(qa @ np.asarray(w_g[h], np.float64)) * oa
+                if self.gate_group:
+                    z = qbar @ np.asarray(w_g[g], np.float64)
+                else:
+                    z = qa @ np.asarray(w_g[h], np.float64)
+                out[h] = ol + np.tanh(z) * oa
             self.pending[g].append({"score": float(cs[g]), "pos": t,
                                     "k": _f(ck[g]), "v": _f(cv[g])})
             # positions older than the window are never read again

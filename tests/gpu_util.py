@@ -26,9 +26,10 @@ def log(msg: str):
     sys.stdout.flush()
 
 
-def cfg_for(w: synth.Workload) -> rma.Config:
+def cfg_for(w: synth.Workload, gate: int = rma.RMA_GATE_HEAD) -> rma.Config:
     return rma.config_default(layers=w.L, q_heads=w.H, kv_groups=w.G, head_dim=w.d,
-                              window=w.R + 1, bank_cap=w.N, commit=w.C, scale=w.d ** -0.5)
+                              window=w.R + 1, bank_cap=w.N, commit=w.C, scale=w.d ** -0.5,
+                              gate=gate)
 
 
 def to_dev(a: np.ndarray) -> torch.Tensor:
@@ -45,8 +46,8 @@ REGIONS = ("ring_k", "ring_v", "bank_k", "bank_v", "bscore", "bsrc", "pend_k", "
            "pscore")
 
 
-def gpu_state(w: synth.Workload, st_np: dict) -> rma.State:
-    S = rma.State(cfg_for(w), w.B, DEV, start_pos=w.t0, bank_n=w.bank_n)
+def gpu_state(w: synth.Workload, st_np: dict, gate: int = rma.RMA_GATE_HEAD) -> rma.State:
+    S = rma.State(cfg_for(w, gate), w.B, DEV, start_pos=w.t0, bank_n=w.bank_n)
     for name in REGIONS:
         S.write(name, st_np[name])
     torch.cuda.synchronize()

@@ -1,5 +1,5 @@
 """C-ABI checks that need no GPU: the library loads, exports every symbol
-include/rma.h declares, reproduces the pages' memory accounting, and
+include/*.h declares, reproduces the pages' memory accounting, and
 rejects bad arguments on the host before anything is enqueued."""
 import ctypes
 import os
@@ -11,13 +11,17 @@ import pytest
 from bounded_memory_decode_amd import rma
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "rma.h")
+INCLUDE = os.path.join(ROOT, "include")
 
 
 def declared_functions():
-    src = open(HEADER).read()
-    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"\b(rma_[a-z_]+)\s*\(", src)))
+    names = set()
+    for h in sorted(os.listdir(INCLUDE)):
+        if h.endswith(".h"):
+            src = open(os.path.join(INCLUDE, h)).read()
+            src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+            names |= set(re.findall(r"\b(rma_[a-z_]+)\s*\(", src))
+    return sorted(names)
 
 
 def test_library_exports_every_declared_symbol():
@@ -93,6 +97,7 @@ def test_layout_matches_the_pages_memory_table():
     ("window", 256, rma.RMA_E_UNSUPPORTED),   # commit 256 > ring 255
     ("bank_cap", 1900, rma.RMA_E_UNSUPPORTED),
     ("scale", float("nan"), rma.RMA_E_ARG),
+    ("gate", 2, rma.RMA_E_ARG),
 ])
 def test_invalid_configs_are_rejected(field, value, code):
     c = rma.config_default(**{field: value})

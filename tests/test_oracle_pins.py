@@ -329,6 +329,91 @@ def test_planted_anchor_key_follows_the_anchor_query():
     np.testing.assert_allclose(anchor, f32(st["bank_v"][0, 0, g, slot]), rtol=0, atol=1e-6)
 
 
+# ------------------------------------------------------- a gate per KV group
+
+
+def make_group_oracle(w, seed):
+    st = synth.initial_state(w, seed)
+    o = OracleState.from_synth(st, H=w.H, G=w.G, d=w.d, R=w.R, N=w.N, C=w.C, gate_group=True)
+    return o, st
+
+
+@pytest.mark.parametrize("anchor_query", [False, True], ids=["q", "q_anchor"])
+@pytest.mark.parametrize("t0,bank_n,steps", [(0, 0, 30), (14, 4, 24)])
+def test_group_gate_equals_full_history_bruteforce(t0, bank_n, steps, anchor_query):
+    """A gate per (token, KV group): tanh of the group's mean anchor query
+    against the group's weight vector, shared by the group's heads.  The
+    oracle against the full-history model, across admits."""
+    w = tiny(t0=t0, bank_n=bank_n, steps=steps, ring_full=t0 > 0)
+    seed = 23
+    o, st = make_group_oracle(w, seed)
+    wg = synth.gate_weights(w, seed, per_group=True)
+    assert wg.shape == (w.L, w.G, w.d)
+    bfs = [BruteForce(w.H, w.G, w.d, w.R, w.N, w.C, w.d ** -0.5, t0,
+                      st["ring_k"][0, b], st["ring_v"][0, b], st["bank_k"][0, b],
+                      st["bank_v"][0, b], st["bscore"][0, b], st["bsrc"][0, b],
+                      st["bank_n"][0, b], gate_group=True) for b in range(w.B)]
+    for s in range(steps):
+        x = synth.step_inputs(w, seed, 0, s)
+        qa = synth.anchor_query(w, seed, 0, s) if anchor_query else None
+        out = o.decode_step(0, x["q"], x["k"], x["v"], x["ck"], x["cv"], x["cs"], wg[0],
+                            q_anchor=qa)
+        if o.pend_n[0] == o.C:
+            o.admit(0)
+        for b in range(w.B):
+            ref = bfs[b].step(x["q"][b], x["k"][b], x["v"][b], x["ck"][b], x["cv"][b],
+                              x["cs"][b], wg[0], q_anchor=None if qa is None else qa[b])
+            np.testing.assert_allclose(out[b], ref, rtol=0, atol=1e-12)
+
+
+def test_group_gate_constant_values_closed_form():
+    """V == c everywhere: both reads return c, so every head of group g gives
+    c (1 + tanh(mean_h(qa_h) . w_g[g])) -- one value for the whole group."""
+    w = synth.WORKLOADS["sharp_b1"].with_(bank_n=1024)
+    seed = 24
+    o, _ = make_group_oracle(w, seed)
+    c = synth.bf16_bits(np.float32(0.375))
+    o.ring_v[...] = c
+    o.bank_v[...] = c
+    wg = synth.gate_weights(w, seed, per_group=True)
+    x = synth.step_inputs(w, seed, 0, 0)
+    x["v"][...] = c
+    qa = synth.anchor_query(w, seed, 0, 0)
+    out = o.decode_step(0, x["q"], x["k"], x["v"], x["ck"], x["cv"], x["cs"], wg[0], q_anchor=qa)
+    hpg = w.H // w.G
+    for g in range(w.G):
+        qbar = f32(qa[0, g * hpg:(g + 1) * hpg]).mean(axis=0)
+        want = 0.375 * (1.0 + math.tanh(float(qbar @ wg[0, g].astype(np.float64))))
+        np.testing.assert_allclose(out[0, g * hpg:(g + 1) * hpg], want, rtol=0, atol=1e-12)
+
+
+def test_group_gate_reduces_to_head_gate():
+    """When the heads of a group share one anchor query and the per-head
+    weights all equal the group's vector, the per-group gate is the
+    per-head gate: the outputs agree (to rounding of the mean)."""
+    w = synth.WORKLOADS["sharp_b1"].with_(B=2, bank_n=800)
+    seed = 25
+    oh, st = make_oracle(w, seed)
+    og = OracleState.from_synth(st, gate_group=True)
+    wgg = synth.gate_weights(w, seed, per_group=True)
+    hpg = w.H // w.G
+    wgh = np.repeat(wgg, hpg, axis=1)
+    x = synth.step_inputs(w, seed, 0, 0)
+    qa = synth.anchor_query(w, seed, 0, 0)
+    for g in range(w.G):
+        qa[:, g * hpg:(g + 1) * hpg] = qa[:, g * hpg][:, None]
+    a = oh.decode_step(0, x["q"], x["k"], x["v"], x["ck"], x["cv"], x["cs"], wgh[0], q_anchor=qa)
+    b = og.decode_step(0, x["q"], x["k"], x["v"], x["ck"], x["cv"], x["cs"], wgg[0], q_anchor=qa)
+    np.testing.assert_allclose(a, b, rtol=0, atol=1e-14)
+    # and it is not the per-head gate in general: distinct anchor queries
+    qa2 = synth.anchor_query(w, seed, 0, 1)
+    a = oh.clone().decode_step(0, x["q"], x["k"], x["v"], x["ck"], x["cv"], x["cs"], wgh[0],
+                               q_anchor=qa2)
+    b = og.clone().decode_step(0, x["q"], x["k"], x["v"], x["ck"], x["cv"], x["cs"], wgg[0],
+                               q_anchor=qa2)
+    assert np.abs(a - b).max() > 1e-6
+
+
 # ----------------------------------------------------------- invariances
 
 
