@@ -7,11 +7,17 @@ ring write and the pending append; plus, every 256 tokens, the admit of
 all layers.  Workload: 512 sequences, state pre-filled as after a 32K
 prompt (ring and bank full), synthetic N(0,1)/16 bf16 inputs from a
 device-resident pool of 16 input sets per layer (the pool changes none of
-the state traffic).  Prints ONE JSON line: the headline decode figure with
-its HBM roofline and the CPU oracle beside it, plus the admit round, the
-same batch with per-sequence positions and with a separate anchor query,
-batch-1 token latency (eager and HIP-graph replay) and the MFMA prefill
-block at batch 1 and 8.
+the state traffic).  The timed window always ends with a step that
+completes a block, so it contains at least one admit of all layers.
+
+Prints ONE JSON line: the headline decode figure with its HBM roofline, a
+streaming-read calibration and the CPU oracle beside it, plus
+  admit_stress  one all-layer admit with scores on 64 levels (heavy ties);
+  staggered     the same batch with per-sequence positions;
+  anchor_query  the same batch with a separate anchor query;
+  long          one sequence: a 131,072-token prompt in 256-token prefill
+                blocks (admit after each), then decode as HIP-graph replays;
+  prefill       the MFMA prefill block at batch 1 and 8.
 
     python bench.py [--gpus 1] [--steps 1024] [--warmup 16]
 """
@@ -21,6 +27,7 @@ import argparse
 import hashlib
 import json
 import os
+import platform
 import sys
 import time
 
@@ -42,6 +49,12 @@ BANK_BYTES = 1024 * 1024
 UNIT_READ = RING_BYTES + BANK_BYTES + 2048 + 1024 + 1028
 UNIT_WRITE = 2048 + 1024 + 1028
 UNIT_BYTES = UNIT_READ + UNIT_WRITE          # 2,104,328
+
+# Algorithmic bytes of one (sequence, layer, group) admit, given n anchors,
+# C candidates and m records moved: read n + C scores; for each moved
+# record read its K/V (1,024 B) and score; write its K/V, score and source
+# position into the bank; write the bank count.
+REC_BYTES = 1024
 
 
 # Sources that define the decode kernel; the committed counter summary is
@@ -116,16 +129,12 @@ def make_pool(w, seed, device, pool=POOL):
     return sets, wg, outs
 
 
-def run_step(S, sets, wg, outs, step, events=None, admit_events=None):
+def run_step(S, sets, wg, outs, step, admit_events=None):
     """One token through all layers (+ admit at the block end)."""
     L = S.cfg.layers
     for l in range(L):
         x = sets[l][step % len(sets[l])]
-        if events is not None:
-            events[l][0].record()
         S.decode_step(l, x["q"], x["k"], x["v"], x["ck"], x["cv"], x["cs"], wg[l], outs[l])
-        if events is not None:
-            events[l][1].record()
     if S.pend_n[0] == S.cfg.commit:
         if admit_events is not None:
             admit_events.append((_event(), _event()))
@@ -142,13 +151,109 @@ def _event():
     return torch.cuda.Event(enable_timing=True)
 
 
+def _median(xs):
+    s = sorted(xs)
+    return s[len(s) // 2]
+
+
 # Prefill work of one 256-token block of one layer with a full ring and
 # bank, masked work excluded: per group, 1,024 query rows (256 tokens x 4
 # heads) each against 1,024 local keys and 1,024 anchors, QK and PV at
 # 2 flop per multiply-add over 256 dims.
 PREFILL_FLOP_PER_GROUP = 1024 * (1024 + 1024) * 256 * 2 * 2   # 2.147 GFLOP
 MFMA_BF16_PEAK_TFLOPS = 2500.0
-EVENT_EVERY = 8  # headline loop: steps between two steps with per-launch events
+
+
+def bench_calibration(device, gib=8, waves=1024, reps=7):
+    """Achievable read bandwidth: rma_calib_stream_read (a streaming-read
+    kernel of this library, 16-byte non-temporal loads) over a `gib` GiB
+    buffer with `waves` waves (the decode kernel's resident wave count),
+    median of `reps` passes timed with events."""
+    import torch
+    from bounded_memory_decode_amd import rma
+    n = gib << 30
+    buf = torch.empty(n, dtype=torch.uint8, device=device)
+    buf.fill_(1)
+    sink = torch.empty(waves, dtype=torch.int32, device=device)
+    rma.calib_stream_read(buf, waves, sink)  # warm-up
+    ms = []
+    for _ in range(reps):
+        e0, e1 = _event(), _event()
+        e0.record()
+        rma.calib_stream_read(buf, waves, sink)
+        e1.record()
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+    del buf, sink
+    torch.cuda.empty_cache()
+    m = _median(ms)
+    return {"kernel": "stream_read_kernel (rma_calib_stream_read): every wave reads its own "
+                      "contiguous share with 16-byte non-temporal loads",
+            "bytes": n, "waves": waves, "passes": reps, "ms": round(m, 4),
+            "GBps": round(n / (m * 1e-3) / 1e9, 1)}
+
+
+def bench_admit_stress(S, w, seed, reps=5):
+    """Config of the admit stress: every (sequence, layer, group) of the
+    headline state gets a full pending buffer and scores on 64 levels
+    (integers 0..63, so ties straddle the cut in nearly every group), then
+    one admit of all layers is timed; the bank metadata is restored
+    between passes.  Moved records are counted from the result."""
+    import torch
+    from bounded_memory_decode_amd import synth
+    ws = synth.WORKLOADS["admit_b512"].with_(B=w.B, L=w.L)
+    dev = S.device
+    C, N = w.C, w.N
+    # a block-aligned position for the lockstep admit; source positions
+    # 0 .. N-1 for the anchors, so that every record the admit moves in
+    # (source position >= the block start > N) can be counted
+    t_al = (S.t[0] // C + 1) * C
+    S.region_view("bsrc").copy_(torch.arange(N, dtype=torch.int32, device=dev).expand(
+        w.L, w.B, w.G, N))
+    for l in range(w.L):
+        sc = synth.torch_scores((1, w.B, w.G, N), ws, seed, dev, (ws.wid, synth.KIND["bscore"], l))
+        S.write("bscore", sc, layers=slice(l, l + 1))
+        ps = synth.torch_scores((1, w.B, w.G, C), ws, seed, dev, (ws.wid, synth.KIND["pscore"], l))
+        S.write("pscore", ps, layers=slice(l, l + 1))
+        for name in ("pend_k", "pend_v"):
+            x = synth.torch_normal_bf16((1, w.B, w.G, C, w.d), ws.qkv_std, seed, dev,
+                                        (ws.wid, synth.KIND[name], l))
+            S.write(name, x.view(torch.int16), layers=slice(l, l + 1))
+    saved = {k: S.region_view(k).clone() for k in ("bscore", "bsrc", "bank_n")}
+    n_before = S.region_view("bank_n").to(torch.int64)
+    host_n = list(S.bank_n)
+    ms = []
+    moved = None
+    for r in range(reps):
+        for k, v in saved.items():
+            S.region_view(k).copy_(v)
+        for l in range(w.L):
+            S._st.t[l] = t_al
+            S._st.pend_n[l] = C
+            S._st.bank_n[l] = host_n[l]
+        torch.cuda.synchronize()
+        e0, e1 = _event(), _event()
+        e0.record()
+        S.admit(-1)
+        e1.record()
+        torch.cuda.synchronize()
+        ms.append(e0.elapsed_time(e1))
+        if moved is None:
+            moved = int((S.region_view("bsrc") >= N).sum().item())
+    m = _median(ms)
+    units = w.L * w.B * w.G
+    nsum = int(n_before.sum().item())
+    bytes_round = (nsum + units * C) * 4 + moved * (REC_BYTES + 4) + moved * (REC_BYTES + 8) + \
+        units * 4
+    return {"workload": f"admit_b512: {w.L} layers x batch {w.B} x {w.G} groups, each the top "
+                        f"{N} of {N} anchors + {C} candidates, scores integers 0..63 (heavy ties)",
+            "selections": units, "passes": reps, "ms_per_round": round(m, 4),
+            "selections_per_s": round(units / (m * 1e-3)),
+            "records_moved": moved, "bytes_per_round": bytes_round,
+            "roofline": {"bound": "hbm", "achieved": round(bytes_round / (m * 1e-3) / 1e9, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(bytes_round / (m * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                         "kernel": "admit_kernel"}}
 
 
 def bench_prefill(device, seed, batch, blocks):
@@ -159,17 +264,7 @@ def bench_prefill(device, seed, batch, blocks):
     w = synth.WORKLOADS["stack_b512"].with_(B=batch)
     S = make_state(w, seed, device)
     n = w.C
-    ins = []
-    for l in range(w.L):
-        key = lambda kind: (w.wid, synth.KIND[kind], l, 99, 2)
-        ins.append({
-            "q": synth.torch_normal_bf16((w.B, n, w.H, w.d), w.qkv_std, seed, device, key("q")),
-            "k": synth.torch_normal_bf16((w.B, n, w.G, w.d), w.qkv_std, seed, device, key("k")),
-            "v": synth.torch_normal_bf16((w.B, n, w.G, w.d), w.qkv_std, seed, device, key("v")),
-            "ck": synth.torch_normal_bf16((w.B, n, w.G, w.d), w.qkv_std, seed, device, key("ck")),
-            "cv": synth.torch_normal_bf16((w.B, n, w.G, w.d), w.qkv_std, seed, device, key("cv")),
-            "cs": synth.torch_scores((w.B, n, w.G), w, seed, device, key("cs")),
-        })
+    ins = [synth.torch_block_inputs(w, seed, l, 99, device, sets=2) for l in range(w.L)]
     wg = (torch.randn((w.L, w.H, w.d), device=device) * w.w_std).contiguous()
     outs = [torch.empty((w.B, n, w.H, w.d), dtype=torch.bfloat16, device=device) for _ in range(w.L)]
 
@@ -206,30 +301,54 @@ def bench_prefill(device, seed, batch, blocks):
                          "kernel": "prefill_attn_kernel + prefill_commit_kernel (one layer, one block)"}}
 
 
-def bench_latency(device, seed, steps, warmup):
-    """One sequence, 8 layers, decoding after a 131,072-token prompt (ring
-    and bank full): the token step launched call by call (lockstep calls,
-    admit every 256 tokens) and the same step captured once in a HIP graph
-    (per-sequence calls with the admit inside, plus the position increment)
-    and replayed.  The state of one sequence (64 MiB) stays in the 256 MB
-    last-level cache, so this is a latency figure, not an HBM one."""
+def bench_long(device, seed, prompt_blocks, decode_steps, eager_steps):
+    """The long single-sequence path: one sequence, 8 layers, from an empty
+    history.  A prompt of prompt_blocks x 256 tokens through
+    rma_prefill_block (all layers admitted after every block), timed as a
+    whole; then decode: `eager_steps` token steps launched call by call
+    (lockstep calls, admit every 256 tokens), then `decode_steps` token
+    steps as replays of one captured HIP graph (8 per-sequence calls with
+    the admit inside, plus the position increment).  The state of one
+    sequence (64 MiB) stays in the 256 MB last-level cache, so these are
+    latency figures, not HBM ones."""
     import torch
-    from bounded_memory_decode_amd import synth
-    w = synth.WORKLOADS["long_b1"].with_(t0=131072, bank_n=1024, ring_full=True)
-    S = make_state(w, seed, device)
-    sets, wg, outs = make_pool(w, seed, device, pool=4)
-    for s in range(warmup):
-        run_step(S, sets, wg, outs, s)
+    from bounded_memory_decode_amd import rma, synth
+    w = synth.WORKLOADS["long_b1"]
+    cfg = rma.config_default(layers=w.L)
+    S = rma.State(cfg, 1, device, start_pos=0, bank_n=0)
+    S.buf.zero_()
+    ins = [[synth.torch_block_inputs(w, seed, l, p, device, sets=4) for p in range(4)]
+           for l in range(w.L)]
+    g = torch.Generator(device=device)
+    g.manual_seed(seed * 7919 + w.wid)
+    wg = (torch.randn((w.L, w.H, w.d), generator=g, device=device) * w.w_std).contiguous()
+    pout = [torch.empty((1, w.C, w.H, w.d), dtype=torch.bfloat16, device=device)
+            for _ in range(w.L)]
     torch.cuda.synchronize()
     e0, e1 = _event(), _event()
     e0.record()
-    for s in range(steps):
-        run_step(S, sets, wg, outs, warmup + s)
+    for blk in range(prompt_blocks):
+        for l in range(w.L):
+            x = ins[l][blk % 4]
+            S.prefill_block(l, x["q"], x["k"], x["v"], x["ck"], x["cv"], x["cs"], wg[l], pout[l])
+        S.admit(-1)
     e1.record()
     torch.cuda.synchronize()
-    eager_us = e0.elapsed_time(e1) * 1e3 / steps
+    prompt_ms = e0.elapsed_time(e1)
+    prompt_tokens = prompt_blocks * w.C
 
-    pos = torch.full((w.B,), S.t[0], dtype=torch.int32, device=device)
+    # decode inputs: token i of the pool's blocks, per layer
+    sets = [[{k: v[:, i].contiguous() for k, v in ins[l][i % 4].items()} for i in range(4)]
+            for l in range(w.L)]
+    outs = [torch.empty((1, w.H, w.d), dtype=torch.bfloat16, device=device) for _ in range(w.L)]
+    e0.record()
+    for s in range(eager_steps):
+        run_step(S, sets, wg, outs, s)
+    e1.record()
+    torch.cuda.synchronize()
+    eager_us = e0.elapsed_time(e1) * 1e3 / max(1, eager_steps)
+
+    pos = torch.full((1,), S.t[0], dtype=torch.int32, device=device)
     x = [sets[l][0] for l in range(w.L)]
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
@@ -237,23 +356,28 @@ def bench_latency(device, seed, steps, warmup):
             S.decode_step_at(l, pos, x[l]["q"], x[l]["k"], x[l]["v"], x[l]["ck"], x[l]["cv"],
                              x[l]["cs"], wg[l], outs[l])
         pos.add_(1)
-    for _ in range(warmup):
+    for _ in range(16):
         graph.replay()
     torch.cuda.synchronize()
     e0.record()
-    for _ in range(steps):
+    for _ in range(decode_steps):
         graph.replay()
     e1.record()
     torch.cuda.synchronize()
-    graph_us = e0.elapsed_time(e1) * 1e3 / steps
+    graph_us = e0.elapsed_time(e1) * 1e3 / max(1, decode_steps)
+    end_pos = int(pos.item())
     del graph, S
     torch.cuda.empty_cache()
-    return {"workload": f"long_b1 decode: 1 sequence x {w.L} layers after a {w.t0}-token prompt "
-                        f"(ring and bank full)",
-            "steps": steps,
-            "eager_us_per_token": round(eager_us, 2),
-            "graph_us_per_token": round(graph_us, 2),
-            "graph_tokens_per_s": round(1e6 / graph_us, 1),
+    return {"workload": f"long_b1: 1 sequence x {w.L} layers from an empty history: a "
+                        f"{prompt_tokens}-token prompt in {w.C}-token prefill blocks (all layers "
+                        f"admitted after each block), then decode",
+            "prompt_tokens": prompt_tokens, "prompt_ms": round(prompt_ms, 3),
+            "prefill_tokens_per_s": round(prompt_tokens / (prompt_ms * 1e-3), 1),
+            "us_per_block_layer_with_admit": round(prompt_ms * 1e3 / (prompt_blocks * w.L), 2),
+            "eager_steps": eager_steps, "eager_us_per_token": round(eager_us, 2),
+            "decode_steps": decode_steps, "graph_us_per_token": round(graph_us, 2),
+            "decode_tokens_per_s": round(1e6 / graph_us, 1),
+            "end_position": end_pos,
             "graph": "8 x rma_decode_step_at (attention, combine, admit-if-block-end) + "
                      "position increment, captured once"}
 
@@ -287,26 +411,24 @@ def bench_staggered(S, w, sets, wg, outs, steps):
 def bench_anchor_query(S, w, sets, wg, outs, steps):
     """The headline batch through the per-sequence call with a separate
     anchor query (the anchor read and the gate use q_anchor; here the q of
-    another input set of the pool), every sequence at the same position."""
+    another input set of the pool), every sequence at the same position,
+    no block end inside the window."""
     import torch
     pos = torch.full((w.B,), S.t[0], dtype=torch.int32, device=S.device)
     e0, e1 = _event(), _event()
-    ev = [(_event(), _event()) for _ in range(steps * w.L)]
     torch.cuda.synchronize()
     e0.record()
     for s in range(steps):
         for l in range(w.L):
             x = sets[l][s % len(sets[l])]
             qa = sets[l][(s + 1) % len(sets[l])]["q"]
-            ev[s * w.L + l][0].record()
             S.decode_step_at(l, pos, x["q"], x["k"], x["v"], x["ck"], x["cv"], x["cs"], wg[l],
                              outs[l], q_anchor=qa)
-            ev[s * w.L + l][1].record()
         pos += 1
     e1.record()
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1)
-    launch_ms = sum(a.elapsed_time(b) for a, b in ev) / len(ev)
+    launch_ms = ms / (steps * w.L)
     return {"workload": f"{w.name} through rma_decode_step_at with a separate anchor query",
             "steps": steps, "ms_per_step": round(ms / steps, 4),
             "tokens_per_s": round(w.B * steps / (ms * 1e-3), 1),
@@ -314,42 +436,78 @@ def bench_anchor_query(S, w, sets, wg, outs, steps):
             "GBps": round(w.B * w.G * (UNIT_BYTES + 2048) / (launch_ms * 1e-3) / 1e9, 1)}
 
 
-def cpu_baseline(S, w, sets, wg, sample_b: int, seed: int, steps: int = 8):
-    """The oracle, timed on the host cores on a bounded sample: `sample_b`
-    sequences of the same state, `steps` tokens through all layers."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return platform.processor() or "unknown"
+
+
+def cpu_baseline(S, w, sets, wg, sample_b: int, steps: int, one_b: int, one_steps: int):
+    """The oracle, timed on the host cores on a bounded sample of the same
+    state: `sample_b` sequences, `steps` tokens through all layers with
+    every thread, crossing a block end (so the admit is in the sample);
+    then `one_b` sequences x `one_steps` tokens on one thread.  The state
+    is copied to the host when S's layers stand a few tokens before a
+    block end."""
     import numpy as np
     import torch
     import oracle
     from oracle import OracleState
-    b_idx = list(range(sample_b))
-    o = OracleState(L=w.L, B=sample_b, H=w.H, G=w.G, d=w.d, R=w.R, N=w.N, C=w.C,
-                    scale=float(S.cfg.scale))
-    for name in ("ring_k", "ring_v", "bank_k", "bank_v", "pend_k", "pend_v"):
-        getattr(o, name)[...] = S.read(name, batch=b_idx).cpu().numpy().view(np.uint16)
-    for name in ("bscore", "bsrc", "pscore", "bank_n"):
-        getattr(o, name)[...] = S.read(name, batch=b_idx).cpu().numpy()
-    o.t[:] = S.t[:w.L]
-    o.pend_n[:] = S.pend_n[:w.L]
-    ins = [[{k: (v[:sample_b].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
-                 if v.dtype == torch.bfloat16 else v[:sample_b].cpu().numpy())
-             for k, v in sets[l][p].items()} for p in range(len(sets[l]))] for l in range(w.L)]
-    wgn = wg.cpu().numpy()
-    admits = 0
-    t0 = time.perf_counter()
-    for s in range(steps):
-        for l in range(w.L):
-            x = ins[l][s % len(ins[l])]
-            o.decode_step(l, x["q"], x["k"], x["v"], x["ck"], x["cv"], x["cs"], wgn[l])
-        if o.pend_n[0] == w.C:
+
+    def load(nb):
+        b_idx = list(range(nb))
+        o = OracleState(L=w.L, B=nb, H=w.H, G=w.G, d=w.d, R=w.R, N=w.N, C=w.C,
+                        scale=float(S.cfg.scale))
+        for name in ("ring_k", "ring_v", "bank_k", "bank_v", "pend_k", "pend_v"):
+            getattr(o, name)[...] = S.read(name, batch=b_idx).cpu().numpy().view(np.uint16)
+        for name in ("bscore", "bsrc", "pscore", "bank_n"):
+            getattr(o, name)[...] = S.read(name, batch=b_idx).cpu().numpy()
+        o.t[:] = S.t[:w.L]
+        o.pend_n[:] = S.pend_n[:w.L]
+        return o
+
+    def run(o, nb, n_steps):
+        ins = [[{k: (v[:nb].contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+                     if v.dtype == torch.bfloat16 else v[:nb].cpu().numpy())
+                 for k, v in sets[l][p].items()} for p in range(len(sets[l]))]
+               for l in range(w.L)]
+        wgn = wg.cpu().numpy()
+        admits = 0
+        t0 = time.perf_counter()
+        for s in range(n_steps):
             for l in range(w.L):
-                o.admit(l)
-            admits += 1
-    dt = time.perf_counter() - t0
+                x = ins[l][s % len(ins[l])]
+                o.decode_step(l, x["q"], x["k"], x["v"], x["ck"], x["cv"], x["cs"], wgn[l])
+            if o.pend_n[0] == w.C:
+                for l in range(w.L):
+                    o.admit(l)
+                admits += 1
+        return time.perf_counter() - t0, admits
+
     cores = oracle.num_threads()
+    dt, admits = run(load(sample_b), sample_b, steps)
+    oracle.set_num_threads(1)
+    try:
+        dt1, admits1 = run(load(one_b), one_b, one_steps)
+    finally:
+        oracle.set_num_threads(cores)
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = os.cpu_count()
     return {"value": sample_b * steps / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"{sample_b} of {w.B} sequences, {steps} tokens through all {w.L} layers "
-                      f"(decode, ring write, pending append; {admits} admit rounds), "
-                      f"{dt:.2f} s wall on {cores} threads"}
+                      f"(decode, ring write, pending append; {admits} admit round of all layers "
+                      f"for these sequences), {dt:.2f} s wall on {cores} threads",
+            "value_1_thread": one_b * one_steps / dt1,
+            "sample_1_thread": f"{one_b} sequences, {one_steps} tokens through all {w.L} layers "
+                               f"({admits1} admit rounds), {dt1:.2f} s wall on 1 thread",
+            "cpu_model": cpu_model(), "nproc": os.cpu_count(), "affinity_cpus": affinity}
 
 
 def read_traffic(sha: str):
@@ -380,16 +538,24 @@ def main():
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--repeats", type=int, default=3,
                     help="timed runs of --steps steps each; the median run is reported")
+    ap.add_argument("--calibration-gib", type=int, default=8,
+                    help="GiB read by the streaming-read calibration (0: skip)")
+    ap.add_argument("--admit-passes", type=int, default=5,
+                    help="timed passes of the admit stress (0: skip)")
     ap.add_argument("--cpu-sample", type=int, default=64,
                     help="sequences in the CPU-oracle sample (0: skip)")
     ap.add_argument("--cpu-steps", type=int, default=32,
                     help="tokens per sequence in the CPU-oracle sample")
-    ap.add_argument("--latency-steps", type=int, default=512,
-                    help="batch-1 token steps timed eager and as graph replays (0: skip)")
     ap.add_argument("--staggered-steps", type=int, default=256,
                     help="steps of the per-sequence-position run at the headline batch (0: skip)")
     ap.add_argument("--anchor-steps", type=int, default=64,
                     help="steps with a separate anchor query at the headline batch (0: skip)")
+    ap.add_argument("--long-blocks", type=int, default=512,
+                    help="256-token prompt blocks of the long single-sequence run (0: skip)")
+    ap.add_argument("--long-decode", type=int, default=131072,
+                    help="decode tokens (graph replays) after the long prompt")
+    ap.add_argument("--long-eager", type=int, default=512,
+                    help="decode tokens launched call by call before the graph replays")
     ap.add_argument("--prefill-blocks", type=int, default=4,
                     help="256-token blocks timed per prefill batch size (0: skip)")
     ap.add_argument("--calibration-copy-gib", type=int, default=0,
@@ -431,43 +597,51 @@ def main():
         say(f"[bench] calibration copy: 3 x {n} bytes")
         del src, dst
     say(f"[bench] state {S.buf.numel() / 2**30:.2f} GiB; warmup {args.warmup} steps")
-    for s in range(args.warmup):
-        run_step(S, sets, wg, outs, s)
-    torch.cuda.synchronize()
-
+    step = 0
+    for _ in range(args.warmup):
+        run_step(S, sets, wg, outs, step)
+        step += 1
     K = args.steps
+    C = w.C
+
+    def align():
+        """Untimed steps so that the next K steps end on a block end."""
+        nonlocal step
+        extra = (-(S.pend_n[0] + K)) % C
+        for _ in range(extra):
+            run_step(S, sets, wg, outs, step)
+            step += 1
+        return extra
+
+    torch.cuda.synchronize()
     runs = []
-    step0 = args.warmup
-    # Per-launch events on every EVENT_EVERY-th step only: each event is a
-    # marker packet on the stream, and events around all 8 launches of
-    # every step cost about 0.9% of the step time on MI355X (measured).
-    sampled = [s for s in range(K) if s % EVENT_EVERY == 0]
     for r in range(max(1, args.repeats)):
-        ev = [[(_event(), _event()) for _ in range(w.L)] if s % EVENT_EVERY == 0 else None
-              for s in range(K)]
+        extra = align()
+        torch.cuda.synchronize()
         start, stop = _event(), _event()
-        say(f"[bench] timing {K} steps (run {r + 1})")
+        say(f"[bench] timing {K} steps (run {r + 1}, after {extra} alignment steps)")
         admits = 0
         admit_ev = []
-        torch.cuda.synchronize()
         t_wall = time.perf_counter()
         start.record()
         for s in range(K):
-            admits += run_step(S, sets, wg, outs, step0 + s, ev[s], admit_ev)
+            admits += run_step(S, sets, wg, outs, step, admit_ev)
+            step += 1
         stop.record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t_wall
-        step0 += K
         ms_total = start.elapsed_time(stop)
-        dec_ms = [ev[s][l][0].elapsed_time(ev[s][l][1]) for s in sampled for l in range(w.L)]
-        runs.append({"ms_total": ms_total, "dec_avg_ms": sum(dec_ms) / len(dec_ms),
-                     "admits": admits, "admit_ev": admit_ev, "wall": wall})
-        say(f"[bench] run {r + 1}: {w.B * K / (ms_total * 1e-3):,.0f} tok/s, decode launch "
-            f"{runs[-1]['dec_avg_ms'] * 1e3:.1f} us")
+        adm_ms = [a.elapsed_time(b) for a, b in admit_ev]
+        runs.append({"ms_total": ms_total, "admits": admits, "admit_ms": adm_ms, "wall": wall})
+        dec = (ms_total - sum(adm_ms)) / (K * w.L)
+        say(f"[bench] run {r + 1}: {w.B * K / (ms_total * 1e-3):,.0f} tok/s, {admits} admit "
+            f"rounds, decode launch {dec * 1e3:.1f} us")
     med = sorted(runs, key=lambda x: x["ms_total"])[len(runs) // 2]
-    ms_total, dec_avg_ms, admits = med["ms_total"], med["dec_avg_ms"], med["admits"]
-    admit_ev, wall = med["admit_ev"], med["wall"]
+    ms_total, admits, adm_ms, wall = med["ms_total"], med["admits"], med["admit_ms"], med["wall"]
     ms_step = ms_total / K
+    # decode launch time: the timed window minus its admits, per launch
+    # (launch gaps included, so at most the kernel's own duration)
+    dec_avg_ms = (ms_total - sum(adm_ms)) / (K * w.L)
 
     units = w.B * w.G
     launch_bytes = units * UNIT_BYTES
@@ -494,6 +668,9 @@ def main():
                                f"4 KV groups, head_dim 256, ring 1023 + current, bank 1024, "
                                f"commit 256, start position {w.t0} (ring and bank full)",
                    "batch": w.B, "layers": w.L, "admit_rounds": admits,
+                   "admit_ms_in_window": round(sum(adm_ms), 4),
+                   "alignment": "untimed steps before each run so that the timed window ends on "
+                                "a block end (every run holds at least one admit of all layers)",
                    "runs": len(runs), "run_tokens_per_s": [round(w.B * K / (x["ms_total"] * 1e-3), 1)
                                                           for x in runs],
                    "step_bytes_algorithmic": step_bytes,
@@ -504,23 +681,31 @@ def main():
                      "kernel": "decode_attn_kernel<true, false, 1>: the whole decode step of one layer "
                                "(one launch at this batch)",
                      "avg_launch_ms": round(dec_avg_ms, 5),
-                     "launches_timed": len(sampled) * w.L,
+                     "launch_time": "timed window minus its admit rounds, divided by the decode "
+                                    "launches in it (gaps between launches included)",
                      "bytes_per_launch": launch_bytes,
                      "kernel_sources_sha": sha},
         "cpu_baseline": None,
     }
-    if admit_ev:
-        adm_ms = [a.elapsed_time(b) for a, b in admit_ev]
-        result["admit"] = {"workload": f"all {w.L} layers x batch {w.B} x 4 groups: top-1024 of "
-                                       f"1024 anchors + 256 candidates each",
-                           "rounds": len(adm_ms), "ms_per_round": round(sum(adm_ms) / len(adm_ms), 4),
+    if adm_ms:
+        result["admit"] = {"workload": f"all {w.L} layers x batch {w.B} x 4 groups inside the timed "
+                                       f"window: top-1024 of 1024 anchors + 256 candidates each",
+                           "rounds": len(adm_ms),
+                           "ms_per_round": round(sum(adm_ms) / len(adm_ms), 4),
                            "selections_per_s": round(w.L * w.B * w.G / (sum(adm_ms) / len(adm_ms) * 1e-3))}
     say(f"[bench] {tokens_s:,.0f} tok/s, {ms_step:.3f} ms/step, decode launch {dec_avg_ms*1e3:.1f} us "
         f"= {achieved:,.0f} GB/s ({100*achieved/HBM_PEAK_GBS:.1f}% of peak); wall {wall:.2f} s")
     if args.cpu_sample > 0:
-        say(f"[bench] CPU oracle on {args.cpu_sample} sequences x {args.cpu_steps} tokens")
-        result["cpu_baseline"] = cpu_baseline(S, w, sets, wg, args.cpu_sample, args.seed,
-                                              args.cpu_steps)
+        # stand a few tokens before a block end so that the sample holds an admit
+        lead = min(8, args.cpu_steps)
+        while (C - S.pend_n[0]) != lead:
+            run_step(S, sets, wg, outs, step)
+            step += 1
+        torch.cuda.synchronize()
+        say(f"[bench] CPU oracle on {args.cpu_sample} sequences x {args.cpu_steps} tokens, "
+            f"then 1 thread")
+        result["cpu_baseline"] = cpu_baseline(S, w, sets, wg, args.cpu_sample, args.cpu_steps,
+                                              one_b=4, one_steps=lead + 2)
     if args.staggered_steps > 0:
         say(f"[bench] per-sequence positions, {args.staggered_steps} steps")
         result["staggered"] = bench_staggered(S, w, sets, wg, outs, args.staggered_steps)
@@ -530,13 +715,28 @@ def main():
         result["anchor_query"] = bench_anchor_query(S, w, sets, wg, outs, args.anchor_steps)
         say(f"[bench] anchor query: {result['anchor_query']['tokens_per_s']:,.0f} tok/s, decode "
             f"launch {result['anchor_query']['decode_launch_us']} us")
+    if args.admit_passes > 0:
+        say(f"[bench] admit stress, {args.admit_passes} passes")
+        result["admit_stress"] = bench_admit_stress(S, w, args.seed, args.admit_passes)
+        a = result["admit_stress"]
+        say(f"[bench] admit stress: {a['ms_per_round']} ms per round, {a['records_moved']} records "
+            f"moved, {a['roofline']['achieved']} GB/s")
     del S, sets, outs
     torch.cuda.empty_cache()
-    if args.latency_steps > 0:
-        say(f"[bench] batch-1 latency, {args.latency_steps} steps")
-        result["latency"] = bench_latency(device, args.seed, args.latency_steps, 16)
-        say(f"[bench] batch 1: eager {result['latency']['eager_us_per_token']} us/token, "
-            f"graph {result['latency']['graph_us_per_token']} us/token")
+    if args.calibration_gib > 0:
+        say(f"[bench] streaming-read calibration, {args.calibration_gib} GiB")
+        cal = bench_calibration(device, args.calibration_gib)
+        cal["decode_frac_of_stream"] = round(achieved / cal["GBps"], 4)
+        result["calibration"] = cal
+        say(f"[bench] stream read: {cal['GBps']} GB/s; decode at {100 * cal['decode_frac_of_stream']:.1f}%")
+    if args.long_blocks > 0:
+        say(f"[bench] long path: {args.long_blocks} prompt blocks, {args.long_decode} decode tokens")
+        result["long"] = bench_long(device, args.seed, args.long_blocks, args.long_decode,
+                                    args.long_eager)
+        r = result["long"]
+        say(f"[bench] long: prefill {r['prefill_tokens_per_s']:,.0f} tok/s "
+            f"({r['us_per_block_layer_with_admit']} us per block-layer), decode "
+            f"{r['graph_us_per_token']} us/token as graph replays, {r['eager_us_per_token']} eager")
     if args.prefill_blocks > 0:
         torch.cuda.empty_cache()
         result["prefill"] = []

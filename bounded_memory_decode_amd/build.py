@@ -19,7 +19,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "librma.so")
-SOURCES = ["rma_host.cpp", "rma_decode.hip", "rma_admit.hip", "rma_prefill.hip"]
+SOURCES = ["rma_host.cpp", "rma_decode.hip", "rma_admit.hip", "rma_prefill.hip", "rma_calib.hip"]
 ARCH = "gfx950"
 
 # Packed fp32 VALU ops are switched off (the compiler would otherwise fuse
