@@ -141,7 +141,7 @@ def state_layout(cfg: Config, batch: int) -> Layout:
 
 def calib_stream_read(buf: torch.Tensor, waves: int, sink: torch.Tensor):
     """Enqueue one streaming read of the whole device buffer `buf` (a
-    contiguous tensor whose byte size is a multiple of waves * 8 KiB) with
+    contiguous tensor whose byte size is a multiple of waves * 16 KiB) with
     `waves` waves; each wave's xor of its words goes to sink[w] (a device
     int32 tensor of `waves` entries).  Measurement support, not part of the
     layer step."""

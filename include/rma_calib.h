@@ -19,7 +19,7 @@ extern "C" {
  * 4): wave w reads the w-th contiguous share with 16-byte non-temporal
  * loads, folds the words by xor and writes the result to sink[w]
  * (DEVICE memory of `waves` uint32, caller-owned).  `bytes` must be a
- * multiple of waves * 8 KiB.  Enqueued on `stream` (a hipStream_t, NULL =
+ * multiple of waves * 16 KiB.  Enqueued on `stream` (a hipStream_t, NULL =
  * the null stream).  Returns 0, -1 for invalid arguments (nothing
  * enqueued), or -4 if the launch failed. */
 int rma_calib_stream_read(const void* buf, size_t bytes, int32_t waves, uint32_t* sink,
