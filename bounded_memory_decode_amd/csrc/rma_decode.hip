@@ -282,7 +282,7 @@ __device__ __forceinline__ AuxPtrs aux_ptrs(const DecodeArgs& a, const Seg& nxt,
 // out = o_local + tanh(q . w_g) * o_anchor, the ring write and the pending
 // append.  Every read of the unit's ring by this launch is already done:
 // only this wave reads it.
-template <bool kQA>
+template <bool kQA, bool kGG>
 __device__ __forceinline__ void finish_unit(const DecodeArgs& a, int u, int lane,
                                             const uint4* q_w, const uint4* qa_w,
                                             const float* o_r, const float* mr,
@@ -314,8 +314,8 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs& a, int u, int lane
     ds = fmaf(bf_hi(q8.w), bf_hi(kv.w), ds);
     ds = lane < 32 ? ds : 0.f;
     const uint2 q2 = reinterpret_cast<const uint2*>((kQA ? qa_w : q_w) + h * kChunks)[lane];
-    const float4 w4 = reinterpret_cast<const float4*>(
-        a.w_g + (size_t)(a.gate_group ? g : g * kHpg + h) * kD)[lane];
+    const float4 w4 =
+        reinterpret_cast<const float4*>(a.w_g + (size_t)(kGG ? g : g * kHpg + h) * kD)[lane];
     float dz = bf_lo(q2.x) * w4.x;
     dz = fmaf(bf_hi(q2.x), w4.y, dz);
     dz = fmaf(bf_lo(q2.y), w4.z, dz);
@@ -323,7 +323,7 @@ __device__ __forceinline__ void finish_unit(const DecodeArgs& a, int u, int lane
     sc[h] = wave_sum_u(ds) * a.sl2e;
     z[h] = wave_sum_u(dz);
   }
-  if (a.gate_group) {  // one gate for the group: its mean anchor query . w_g[g]
+  if (kGG) {  // one gate for the group: its mean anchor query . w_g[g]
     const float zm = ((z[0] + z[1]) + (z[2] + z[3])) * (1.f / kHpg);
 #pragma unroll
     for (int h = 0; h < kHpg; ++h) z[h] = zm;
@@ -448,7 +448,7 @@ __device__ __forceinline__ void load_k_tile(const uint4* base, int slots, int hi
 // load_k_tile as the A operand, the 4 query rows as B columns, repeated
 // over the 16 columns); P.V runs on the vector ALU, a half-wave per key
 // and 8 dims per lane, on V rows as stored.
-template <bool kWhole, bool kQA, int kW>
+template <bool kWhole, bool kQA, int kW, bool kGG = false>
 __global__ __launch_bounds__(64 * kW) void decode_attn_kernel(DecodeArgs a, int items) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
@@ -669,8 +669,8 @@ __global__ __launch_bounds__(64 * kW) void decode_attn_kernel(DecodeArgs a, int 
       }
       __builtin_amdgcn_wave_barrier();
     } else {
-      finish_unit<kQA>(a, item, lane, q_s[wave], qa_s[kQA ? wave : 0], or_s[kWhole ? wave : 0],
-                       mr, lr, l, acc, fin);
+      finish_unit<kQA, kGG>(a, item, lane, q_s[wave], qa_s[kQA ? wave : 0],
+                            or_s[kWhole ? wave : 0], mr, lr, l, acc, fin);
       __builtin_amdgcn_wave_barrier();
     }
 
@@ -1021,7 +1021,7 @@ __global__ void seq_bank_n_kernel(int32_t* bank_n, int L, int B, int G, int firs
 // Workgroups of a kernel that are resident at once on the current device
 // (CUs x workgroups per CU), computed once per device (host threads may
 // race to fill an entry: each computes and stores the same value).
-template <bool kWhole, bool kQA, int kW>
+template <bool kWhole, bool kQA, int kW, bool kGG = false>
 int resident_workgroups() {
   static std::atomic<int> cached[64];  // zero-initialised (static storage)
   int dev = 0;
@@ -1031,7 +1031,8 @@ int resident_workgroups() {
     int cus = 0, per_cu = 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
       cus = 256;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, decode_attn_kernel<kWhole, kQA, kW>,
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu,
+                                                     decode_attn_kernel<kWhole, kQA, kW, kGG>,
                                                      64 * kW, 0) != hipSuccess ||
         per_cu < 1)
       per_cu = 1;
@@ -1041,14 +1042,25 @@ int resident_workgroups() {
   return r;
 }
 
-template <bool kQA, int kW>
+template <bool kQA, int kW, bool kGG>
 hipError_t launch_whole(const DecodeArgs& a, hipStream_t s) {
   int grid = (a.units + kW - 1) / kW;
-  const int res = resident_workgroups<true, kQA, kW>();
+  const int res = resident_workgroups<true, kQA, kW, kGG>();
   if (grid > res) grid = res;
-  hipLaunchKernelGGL((decode_attn_kernel<true, kQA, kW>), dim3(grid), dim3(64 * kW), 0, s, a,
+  hipLaunchKernelGGL((decode_attn_kernel<true, kQA, kW, kGG>), dim3(grid), dim3(64 * kW), 0, s, a,
                      a.units);
   return hipGetLastError();
+}
+
+// The whole-unit launch with its template choices: a separate anchor
+// query (kQA), one-wave or four-wave workgroups, and the per-group gate
+// (kGG, a separate instantiation so that the default finish keeps its
+// code: a runtime test there cost 4 us per launch at batch 512).
+template <bool kQA>
+hipError_t launch_whole_gate(const DecodeArgs& a, bool one, hipStream_t s) {
+  if (a.gate_group)
+    return one ? launch_whole<kQA, 1, true>(a, s) : launch_whole<kQA, kWaves, true>(a, s);
+  return one ? launch_whole<kQA, 1, false>(a, s) : launch_whole<kQA, kWaves, false>(a, s);
 }
 
 // The launch rule below: true for a whole-unit launch (and *one: one-wave
@@ -1124,8 +1136,7 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   const bool qa = a.qa != nullptr;
   bool one = false;
   if (whole_unit_launch(a, &one)) {
-    hipError_t e = qa ? (one ? launch_whole<true, 1>(a, s) : launch_whole<true, kWaves>(a, s))
-                      : (one ? launch_whole<false, 1>(a, s) : launch_whole<false, kWaves>(a, s));
+    hipError_t e = qa ? launch_whole_gate<true>(a, one, s) : launch_whole_gate<false>(a, one, s);
     if (e != hipSuccess || a.pos == nullptr) return e;
     // per-sequence positions: admit the units whose block this token ends
     AdmitArgs ad;
