@@ -66,30 +66,59 @@ def test_whole_unit_batch256_from_empty_history():
 @pytest.mark.parametrize("bank_n", [1024, 555])
 def test_bench_configuration_batch512_8_layers(bank_n):
     """The launch configuration bench.py times: 512 sequences x 8 layers,
-    ring and bank full (or a partial bank), 3 tokens through all layers.
-    Outputs of sampled sequences are compared for every layer and token;
-    their ring and pending state after the tokens bit for bit."""
+    ring full, bank full (or partial), starting 3 tokens before a block
+    end; 6 tokens through all layers, so every layer is admitted after the
+    third.  Sampled sequences: outputs of every layer and token, and their
+    whole state at the end, bit for bit.  Every sequence: the admit's
+    selection (scores, source positions, counts of all 512 x 8 x 4 groups)
+    against an oracle that carries the same scores with stand-in records
+    of width 2 (the selection depends on the scores alone)."""
     gu.log(f"case bench configuration bank_n={bank_n}")
-    w = synth.WORKLOADS["stack_b512"].with_(bank_n=bank_n)
+    w = synth.WORKLOADS["stack_b512"].with_(bank_n=bank_n, t0=32768 - 3)
     seed = 3
     dev = torch.device("cuda", 0)
     S = bench.make_state(w, seed, dev)
-    sets, wg, outs = bench.make_pool(w, seed, dev, pool=3)
+    sets, wg, outs = bench.make_pool(w, seed, dev, pool=6)
     sample = [0, 257, 511]
     o = _oracle_from_device(S, w, sample)
+    # all sequences, scores only
+    oa = OracleState(L=w.L, B=w.B, H=w.H, G=w.G, d=2, R=w.R, N=w.N, C=w.C)
+    for name in ("bscore", "bsrc", "pscore", "bank_n"):
+        getattr(oa, name)[...] = S.read(name).cpu().numpy()
+    oa.t[:] = S.t[:w.L]
+    oa.pend_n[:] = S.pend_n[:w.L]
+    assert oa.pend_n[0] == w.C - 3
     wgn = wg.cpu().numpy()
     ins = [[{k: (_host_bits(v[sample]) if v.dtype == torch.bfloat16 else v[sample].cpu().numpy())
-             for k, v in sets[l][p].items()} for p in range(3)] for l in range(w.L)]
-    for step in range(3):
-        bench.run_step(S, sets, wg, outs, step)
+             for k, v in sets[l][p].items()} for p in range(6)] for l in range(w.L)]
+    rec2 = np.zeros((w.B, w.G, 2), np.uint16)
+    admitted = 0
+    for step in range(6):
+        admitted += bench.run_step(S, sets, wg, outs, step)
         torch.cuda.synchronize()
         for l in range(w.L):
             x = ins[l][step]
             ref = o.decode_step(l, x["q"], x["k"], x["v"], x["ck"], x["cv"], x["cs"], wgn[l])
             gu.check_out(outs[l][sample], ref, f"bench config step {step} layer {l}")
-    for name in ("ring_k", "ring_v", "pend_k", "pend_v", "pscore"):
-        g = S.read(name, batch=sample).cpu().numpy()
+            cs = sets[l][step]["cs"].cpu().numpy()
+            oa.decode_step(l, np.zeros((w.B, w.H, 2), np.uint16), rec2, rec2, rec2, rec2, cs,
+                           np.zeros((w.H, 2), np.float32), compute_out=False)
+        if o.pend_n[0] == w.C:
+            for l in range(w.L):
+                o.admit(l)
+                oa.admit(l)
+    assert admitted == 1
+    for name in gu.REGIONS + ("bank_n",):
+        g = gu.bits(S.read(name, batch=sample))
         r = getattr(o, name)
         r = r.view(np.int16) if r.dtype == np.uint16 else r
-        assert np.array_equal(g.view(np.uint32) if g.dtype == np.float32 else g,
-                              r.view(np.uint32) if r.dtype == np.float32 else r), name
+        if r.dtype == np.float32:
+            g, r = g.view(np.uint32), r.view(np.uint32)
+        assert np.array_equal(g, r), f"sampled sequences: {name}"
+    assert S.t == list(o.t) and S.pend_n == list(o.pend_n)
+    for name in ("bscore", "bsrc", "bank_n"):
+        g = gu.bits(S.read(name))
+        r = getattr(oa, name)
+        if r.dtype == np.float32:
+            g, r = g.view(np.uint32), r.view(np.uint32)
+        assert np.array_equal(g, r), f"all sequences: {name}"
