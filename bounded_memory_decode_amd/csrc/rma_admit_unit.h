@@ -196,46 +196,66 @@ __device__ inline void admit_unit(const AdmitUnit& a, AdmitShared& sh) {
   }
   __syncthreads();
 
-  // move the admitted records: chunk c of record r is one K and one V
-  // copy; 8 chunks per thread per round, all 16 loads issued before the
-  // first store (a lone unit's admit is latency-bound; named registers
-  // rather than an array keep the batch out of scratch).  Past the end, a
-  // lane repeats the last chunk's copy (same value, same place), so the
-  // batch has no branch.
+  // move the admitted records.  K: thread r moves record r (na <= C <= 256
+  // = threads) chunk plane by chunk plane, 8 chunks (128 contiguous bytes
+  // of its pending row) per batch, all 8 loads issued before the first
+  // store.  One store instruction then writes one chunk plane for 64
+  // consecutive records, whose destination slots ascend (evicted slots in
+  // ascending order, then the appended ones), so records whose slots share
+  // a cache line leave in one write request instead of one each.  V: chunk
+  // c of record r per work item as rows (a record's V row is one 512-byte
+  // run on both sides), 8 per thread per round, loads before stores;
+  // past the end a lane repeats the last copy (same value, same place), so
+  // the batch has no branch.  (A lone unit's admit is latency-bound; named
+  // registers rather than an array keep the batches out of scratch.)
   uint4* bk = reinterpret_cast<uint4*>(a.bank_k);
   uint4* bv = reinterpret_cast<uint4*>(a.bank_v);
   const uint4* pk = reinterpret_cast<const uint4*>(a.pend_k);
   const uint4* pv = reinterpret_cast<const uint4*>(a.pend_v);
+  static_assert(kAdmitThreads >= 256, "one thread per admitted record (commit <= 256)");
+  if (tid < na) {
+    const uint4* src = pk + (size_t)sh.admitted[tid] * kChunks;
+    const int dst = tid < ne ? sh.evicted[tid] : n + (tid - ne);
+#pragma unroll
+    for (int c0 = 0; c0 < kChunks; c0 += 8) {
+      const uint4 k0 = src[c0], k1 = src[c0 + 1], k2 = src[c0 + 2], k3 = src[c0 + 3],
+                  k4 = src[c0 + 4], k5 = src[c0 + 5], k6 = src[c0 + 6], k7 = src[c0 + 7];
+      bk[k_chunk_index(dst, c0, N)] = k0;
+      bk[k_chunk_index(dst, c0 + 1, N)] = k1;
+      bk[k_chunk_index(dst, c0 + 2, N)] = k2;
+      bk[k_chunk_index(dst, c0 + 3, N)] = k3;
+      bk[k_chunk_index(dst, c0 + 4, N)] = k4;
+      bk[k_chunk_index(dst, c0 + 5, N)] = k5;
+      bk[k_chunk_index(dst, c0 + 6, N)] = k6;
+      bk[k_chunk_index(dst, c0 + 7, N)] = k7;
+    }
+  }
   const int total = na * kChunks;
-  // source and destination of copy x of the round at `base`
+  // source and destination of V copy w
   auto src_of = [&](int w) {
     const int wc = w < total ? w : total - 1;
     return (size_t)sh.admitted[wc / kChunks] * kChunks + (wc % kChunks);
   };
-  auto put = [&](int w, const uint4& kx, const uint4& vx) {
+  auto put = [&](int w, const uint4& vx) {
     const int wc = w < total ? w : total - 1;
     const int r = wc / kChunks, c = wc % kChunks;
     const int dst = r < ne ? sh.evicted[r] : n + (r - ne);
-    bk[k_chunk_index(dst, c, N)] = kx;
     bv[(size_t)dst * kChunks + c] = vx;
   };
   for (int base = tid; base < total; base += 8 * kAdmitThreads) {
     constexpr int T = kAdmitThreads;
-    const size_t o0 = src_of(base), o1 = src_of(base + T), o2 = src_of(base + 2 * T),
-                 o3 = src_of(base + 3 * T), o4 = src_of(base + 4 * T), o5 = src_of(base + 5 * T),
-                 o6 = src_of(base + 6 * T), o7 = src_of(base + 7 * T);
-    const uint4 k0 = pk[o0], k1 = pk[o1], k2 = pk[o2], k3 = pk[o3], k4 = pk[o4], k5 = pk[o5],
-                k6 = pk[o6], k7 = pk[o7];
-    const uint4 v0 = pv[o0], v1 = pv[o1], v2 = pv[o2], v3 = pv[o3], v4 = pv[o4], v5 = pv[o5],
-                v6 = pv[o6], v7 = pv[o7];
-    put(base, k0, v0);
-    put(base + T, k1, v1);
-    put(base + 2 * T, k2, v2);
-    put(base + 3 * T, k3, v3);
-    put(base + 4 * T, k4, v4);
-    put(base + 5 * T, k5, v5);
-    put(base + 6 * T, k6, v6);
-    put(base + 7 * T, k7, v7);
+    const uint4 v0 = pv[src_of(base)], v1 = pv[src_of(base + T)], v2 = pv[src_of(base + 2 * T)],
+                v3 = pv[src_of(base + 3 * T)], v4 = pv[src_of(base + 4 * T)],
+                v5 = pv[src_of(base + 5 * T)], v6 = pv[src_of(base + 6 * T)],
+                v7 = pv[src_of(base + 7 * T)];
+    put(base, v0);
+    put(base + T, v1);
+    put(base + 2 * T, v2);
+    put(base + 3 * T, v3);
+    put(base + 4 * T, v4);
+    put(base + 5 * T, v5);
+    put(base + 6 * T, v6);
+    put(base + 7 * T, v7);
   }
   for (int r = tid; r < na; r += kAdmitThreads) {
     const int j = sh.admitted[r];
