@@ -364,7 +364,7 @@ class State:
                                                 "q_anchor", self.device)
         _check(lib().rma_decode_step_at_static(ctypes.byref(self._st), int(layer), p, ptrs[0], qa,
                                                *ptrs[1:], _stream_handle(self.device)),
-               "rma_decode_step_at_static", "rma_calib_stream_read")
+               "rma_decode_step_at_static")
         return out
 
     def prefill_block_at(self, layer: int, pos: torch.Tensor, q, k, v, cand_k, cand_v,
