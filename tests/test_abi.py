@@ -240,3 +240,18 @@ def test_positioned_calls_validation_on_host():
     assert L.rma_seq_reset(None, 0, 1, 0, None) == rma.RMA_E_ARG
     # host counters untouched by failed calls
     assert st.t[0] == 32768 and st.pend_n[0] == 0 and st.bank_n[0] == 1024
+
+
+@pytest.mark.parametrize("buf,nbytes,waves,sink", [
+    (0, 1 << 20, 1024, FAKE),            # null buffer
+    (FAKE + 8, 1 << 24, 1024, FAKE),     # misaligned buffer
+    (FAKE, 1 << 24, 1026, FAKE),         # waves not a multiple of 4
+    (FAKE, 1 << 24, 0, FAKE),            # no waves
+    (FAKE, (1 << 24) + 16, 1024, FAKE),  # bytes not a multiple of waves * 16 KiB
+    (FAKE, 0, 1024, FAKE),               # nothing to read
+    (FAKE, 1 << 24, 1024, 0),            # null sink
+])
+def test_calibration_probe_rejects_bad_arguments(buf, nbytes, waves, sink):
+    """rma_calib_stream_read refuses bad arguments on the host (-1) before
+    anything is launched."""
+    assert rma.lib().rma_calib_stream_read(buf, nbytes, waves, sink, None) == -1
