@@ -6,7 +6,7 @@
 //
 // Semantics: EdgeRock model card (ModelScope), "How Rock Memory Anchors
 // work" (every 256 tokens admission keeps the highest-priority records per
-// KV group; retained records stay separate and unchanged); ai-primer
+// KV group; a kept record is neither merged with others nor modified); ai-primer
 // three-operation list, item 2; tpsreport "How it works" (top 1,024 of
 // anchors plus 256 candidates, independently in each group).
 // Readings: order = score descending then global index ascending (anchor
