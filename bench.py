@@ -17,6 +17,9 @@ streaming-read calibration and the CPU oracle beside it, plus
   anchor_query  the same batch with a separate anchor query;
   long          one sequence: a 131,072-token prompt in 256-token prefill
                 blocks (admit after each), then decode as HIP-graph replays;
+  layers        one layer at batch 1 and 64 through its whole decode run
+                (512 and 2,048 steps with their admits), eager and as graph
+                replays;
   prefill       the MFMA prefill block at batch 1 and 8.
 
     python bench.py [--gpus 1] [--steps 1024] [--warmup 16]
@@ -441,6 +444,84 @@ def bench_anchor_query(S, w, sets, wg, outs, steps):
             "GBps": round(w.B * w.G * (UNIT_BYTES + 2048) / (launch_ms * 1e-3) / 1e9, 1)}
 
 
+def bench_layer_config(device, seed, name):
+    """One RMA layer at its own batch, from the pre-filled state (ring and
+    bank full at position 32,768): the workload's full decode run, all its
+    steps and admits, two ways on two copies of the state.
+      eager: lockstep rma_decode_step per token, rma_admit at each block
+             end (event pairs around the admits);
+      graph: 16 captured token steps (rma_decode_step_at, which admits
+             inside the call at a block end, plus the position increment;
+             each step with its own input set of the pool), replayed
+             steps / 16 times, so that the host's graph launch is shared
+             by 16 tokens.
+    Batch 1 keeps its whole state (8 MiB) in the 256 MB last-level cache,
+    so its figures are latency; batch 64 (537 MB) streams from HBM."""
+    import torch
+    from bounded_memory_decode_amd import synth
+    w = synth.WORKLOADS[name]
+    steps = w.steps
+    S = make_state(w, seed, device)
+    sets, wg, outs = make_pool(w, seed, device)
+    torch.cuda.synchronize()
+    adm = []
+    e0, e1 = _event(), _event()
+    e0.record()
+    for s in range(steps):
+        run_step(S, sets, wg, outs, s, adm)
+    e1.record()
+    torch.cuda.synchronize()
+    eager_ms = e0.elapsed_time(e1)
+    adm_ms = [a.elapsed_time(b) for a, b in adm]
+    dec_ms = (eager_ms - sum(adm_ms)) / (steps * w.L)
+    del S
+    torch.cuda.empty_cache()
+
+    S = make_state(w, seed, device)
+    per = 16
+    pos = torch.full((w.B,), S.t[0], dtype=torch.int32, device=device)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(per):
+            for l in range(w.L):
+                x = sets[l][i % len(sets[l])]
+                S.decode_step_at(l, pos, x["q"], x["k"], x["v"], x["ck"], x["cv"], x["cs"],
+                                 wg[l], outs[l])
+            pos.add_(1)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(steps // per):
+        graph.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    graph_ms = e0.elapsed_time(e1)
+    end_pos = int(pos[0].item())
+    del graph, S, sets, outs
+    torch.cuda.empty_cache()
+    launch_bytes = w.B * w.G * UNIT_BYTES
+    r = {"workload": f"{name}: one RMA layer, batch {w.B}, {steps} decode steps from position "
+                     f"{w.t0} (ring and bank full), {len(adm_ms)} admits",
+         "batch": w.B, "steps": steps,
+         "eager_tokens_per_s": round(w.B * steps / (eager_ms * 1e-3), 1),
+         "eager_us_per_step": round(eager_ms * 1e3 / steps, 2),
+         "eager_decode_launch_us": round(dec_ms * 1e3, 2),
+         "admits": len(adm_ms),
+         "admit_us": round(1e3 * sum(adm_ms) / max(1, len(adm_ms)), 2),
+         "graph_tokens_per_s": round(w.B * (steps // per * per) / (graph_ms * 1e-3), 1),
+         "graph_us_per_step": round(graph_ms * 1e3 / (steps // per * per), 2),
+         "graph_steps_per_replay": per,
+         "graph_end_position": end_pos,
+         "bytes_per_launch": launch_bytes}
+    if w.B > 1:
+        gbs = launch_bytes / (dec_ms * 1e-3) / 1e9
+        r["roofline"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "launch_time": "eager window minus its admits, per decode launch"}
+    else:
+        r["note"] = "state resident in the last-level cache: latency, not HBM bandwidth"
+    return r
+
+
 def cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -563,6 +644,8 @@ def main():
                     help="decode tokens launched call by call before the graph replays")
     ap.add_argument("--prefill-blocks", type=int, default=4,
                     help="256-token blocks timed per prefill batch size (0: skip)")
+    ap.add_argument("--layer-configs", type=int, default=1,
+                    help="1: time the one-layer workloads at batch 1 and 64 (0: skip)")
     ap.add_argument("--calibration-copy-gib", type=int, default=0,
                     help="before timing, copy a buffer of this many GiB three times "
                          "(a plain copy kernel of known size, for scaling HBM counters)")
@@ -755,6 +838,15 @@ def main():
         say(f"[bench] long: prefill {r['prefill_tokens_per_s']:,.0f} tok/s "
             f"({r['us_per_block_layer_with_admit']} us per block-layer), decode "
             f"{r['graph_us_per_token']} us/token as graph replays, {r['eager_us_per_token']} eager")
+    if args.layer_configs > 0:
+        result["layers"] = []
+        for name in ("layer_b1", "layer_b64"):
+            say(f"[bench] one layer: {name}")
+            r = bench_layer_config(device, args.seed, name)
+            say(f"[bench] {name}: eager {r['eager_us_per_step']} us/step (decode launch "
+                f"{r['eager_decode_launch_us']} us, admit {r['admit_us']} us), graph "
+                f"{r['graph_us_per_step']} us/step")
+            result["layers"].append(r)
     if args.prefill_blocks > 0:
         torch.cuda.empty_cache()
         result["prefill"] = []
