@@ -196,66 +196,71 @@ __device__ inline void admit_unit(const AdmitUnit& a, AdmitShared& sh) {
   }
   __syncthreads();
 
-  // move the admitted records.  K: thread r moves record r (na <= C <= 256
-  // = threads) chunk plane by chunk plane, 8 chunks (128 contiguous bytes
-  // of its pending row) per batch, all 8 loads issued before the first
-  // store.  One store instruction then writes one chunk plane for 64
-  // consecutive records, whose destination slots ascend (evicted slots in
-  // ascending order, then the appended ones), so records whose slots share
-  // a cache line leave in one write request instead of one each.  V: chunk
-  // c of record r per work item as rows (a record's V row is one 512-byte
-  // run on both sides), 8 per thread per round, loads before stores;
-  // past the end a lane repeats the last copy (same value, same place), so
-  // the batch has no branch.  (A lone unit's admit is latency-bound; named
-  // registers rather than an array keep the batches out of scratch.)
+  // move the admitted records, K and V together in 4 batches, each with
+  // all its loads issued before its first store (a lone unit's admit is a
+  // chain of memory round trips: 4 of them instead of 8 with K and V in
+  // separate loops).  K: thread r moves record r (na <= C <= 256 =
+  // threads) chunk plane by chunk plane, 8 chunks (128 contiguous bytes of
+  // its pending row) per batch; one store instruction then writes one
+  // chunk plane for 64 consecutive records, whose destination slots ascend
+  // (evicted slots in ascending order, then the appended ones), so records
+  // whose slots share a cache line leave in one write request instead of
+  // one each.  Threads past na load record 0's chunks and store nothing.
+  // V: copy w moves chunk w % 32 of record w / 32 as rows (a record's V row
+  // is one 512-byte run on both sides), 8 copies per thread per batch;
+  // past the end a lane repeats the last copy (same value, same place).
+  // Named registers rather than arrays keep the batches out of scratch.
   uint4* bk = reinterpret_cast<uint4*>(a.bank_k);
   uint4* bv = reinterpret_cast<uint4*>(a.bank_v);
   const uint4* pk = reinterpret_cast<const uint4*>(a.pend_k);
   const uint4* pv = reinterpret_cast<const uint4*>(a.pend_v);
   static_assert(kAdmitThreads >= 256, "one thread per admitted record (commit <= 256)");
-  if (tid < na) {
-    const uint4* src = pk + (size_t)sh.admitted[tid] * kChunks;
-    const int dst = tid < ne ? sh.evicted[tid] : n + (tid - ne);
-#pragma unroll
-    for (int c0 = 0; c0 < kChunks; c0 += 8) {
-      const uint4 k0 = src[c0], k1 = src[c0 + 1], k2 = src[c0 + 2], k3 = src[c0 + 3],
-                  k4 = src[c0 + 4], k5 = src[c0 + 5], k6 = src[c0 + 6], k7 = src[c0 + 7];
-      bk[k_chunk_index(dst, c0, N)] = k0;
-      bk[k_chunk_index(dst, c0 + 1, N)] = k1;
-      bk[k_chunk_index(dst, c0 + 2, N)] = k2;
-      bk[k_chunk_index(dst, c0 + 3, N)] = k3;
-      bk[k_chunk_index(dst, c0 + 4, N)] = k4;
-      bk[k_chunk_index(dst, c0 + 5, N)] = k5;
-      bk[k_chunk_index(dst, c0 + 6, N)] = k6;
-      bk[k_chunk_index(dst, c0 + 7, N)] = k7;
+  static_assert(kChunks == 32 && 4 * 8 * kAdmitThreads >= 256 * kChunks,
+                "4 batches of 8 cover every K chunk and every V copy");
+  const int total = na * kChunks;  // V copies
+  constexpr int T = kAdmitThreads;
+  const bool kmove = tid < na;
+  // na > 0 (uniform): every clamped index below names a real admitted record
+  for (int b = 0; na > 0 && b < kChunks / 8; ++b) {
+    const uint4* ksrc = pk + (size_t)sh.admitted[kmove ? tid : 0] * kChunks;
+    const int kdst = kmove ? (tid < ne ? sh.evicted[tid] : n + (tid - ne)) : 0;
+    auto vsrc = [&](int w) -> size_t {
+      const int wc = w < total ? w : total - 1;
+      return (size_t)sh.admitted[wc / kChunks] * kChunks + (wc % kChunks);
+    };
+    auto vdst = [&](int w) -> size_t {
+      const int wc = w < total ? w : total - 1;
+      const int r = wc / kChunks, c = wc % kChunks;
+      return (size_t)(r < ne ? sh.evicted[r] : n + (r - ne)) * kChunks + c;
+    };
+    const int base = tid + b * 8 * T;
+    const int c0 = 8 * b;
+    const uint4 k0 = ksrc[c0], k1 = ksrc[c0 + 1], k2 = ksrc[c0 + 2], k3 = ksrc[c0 + 3],
+                k4 = ksrc[c0 + 4], k5 = ksrc[c0 + 5], k6 = ksrc[c0 + 6], k7 = ksrc[c0 + 7];
+    const uint4 v0 = pv[vsrc(base)], v1 = pv[vsrc(base + T)], v2 = pv[vsrc(base + 2 * T)],
+                v3 = pv[vsrc(base + 3 * T)], v4 = pv[vsrc(base + 4 * T)],
+                v5 = pv[vsrc(base + 5 * T)], v6 = pv[vsrc(base + 6 * T)],
+                v7 = pv[vsrc(base + 7 * T)];
+    if (kmove) {
+      bk[k_chunk_index(kdst, c0, N)] = k0;
+      bk[k_chunk_index(kdst, c0 + 1, N)] = k1;
+      bk[k_chunk_index(kdst, c0 + 2, N)] = k2;
+      bk[k_chunk_index(kdst, c0 + 3, N)] = k3;
+      bk[k_chunk_index(kdst, c0 + 4, N)] = k4;
+      bk[k_chunk_index(kdst, c0 + 5, N)] = k5;
+      bk[k_chunk_index(kdst, c0 + 6, N)] = k6;
+      bk[k_chunk_index(kdst, c0 + 7, N)] = k7;
     }
-  }
-  const int total = na * kChunks;
-  // source and destination of V copy w
-  auto src_of = [&](int w) {
-    const int wc = w < total ? w : total - 1;
-    return (size_t)sh.admitted[wc / kChunks] * kChunks + (wc % kChunks);
-  };
-  auto put = [&](int w, const uint4& vx) {
-    const int wc = w < total ? w : total - 1;
-    const int r = wc / kChunks, c = wc % kChunks;
-    const int dst = r < ne ? sh.evicted[r] : n + (r - ne);
-    bv[(size_t)dst * kChunks + c] = vx;
-  };
-  for (int base = tid; base < total; base += 8 * kAdmitThreads) {
-    constexpr int T = kAdmitThreads;
-    const uint4 v0 = pv[src_of(base)], v1 = pv[src_of(base + T)], v2 = pv[src_of(base + 2 * T)],
-                v3 = pv[src_of(base + 3 * T)], v4 = pv[src_of(base + 4 * T)],
-                v5 = pv[src_of(base + 5 * T)], v6 = pv[src_of(base + 6 * T)],
-                v7 = pv[src_of(base + 7 * T)];
-    put(base, v0);
-    put(base + T, v1);
-    put(base + 2 * T, v2);
-    put(base + 3 * T, v3);
-    put(base + 4 * T, v4);
-    put(base + 5 * T, v5);
-    put(base + 6 * T, v6);
-    put(base + 7 * T, v7);
+    if (base < total) {
+      bv[vdst(base)] = v0;
+      bv[vdst(base + T)] = v1;
+      bv[vdst(base + 2 * T)] = v2;
+      bv[vdst(base + 3 * T)] = v3;
+      bv[vdst(base + 4 * T)] = v4;
+      bv[vdst(base + 5 * T)] = v5;
+      bv[vdst(base + 6 * T)] = v6;
+      bv[vdst(base + 7 * T)] = v7;
+    }
   }
   for (int r = tid; r < na; r += kAdmitThreads) {
     const int j = sh.admitted[r];
