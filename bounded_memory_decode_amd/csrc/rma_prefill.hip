@@ -44,6 +44,9 @@ typedef short v4i16_t __attribute__((ext_vector_type(4)));
 typedef short v8i16_t __attribute__((ext_vector_type(8)));
 
 constexpr int kPT = 32;          // keys per tile
+// Largest lead (log2 units) of a tile's score over a row's reference
+// maximum before the reference moves (conditional rescaling).
+constexpr float kLazyLog2 = 8.f;
 // Bytes per staged row (padding against LDS bank conflicts).  Chosen by
 // measurement of the batch-8 prefill over 16-byte multiples: K rows 544
 // (136 dwords) and V rows 544 ran fastest (K rows of 528: +5%, 576: +10%;
@@ -410,9 +413,16 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_kernel(PrefillArgs a
     float mt = fmaxf(fmaxf(fmaxf(sv[0][0], sv[0][1]), fmaxf(sv[0][2], sv[0][3])),
                      fmaxf(fmaxf(sv[1][0], sv[1][1]), fmaxf(sv[1][2], sv[1][3])));
     mt = max32(max16(mt));
-    const float mn = fmaxf(m_run, mt * a.sl2e);
+    // Conditional rescaling: a row's reference maximum moves only when the
+    // tile's maximum passes it by more than kLazyLog2, so the rescale of o
+    // below runs on few tiles.  Probabilities are then at most 2^kLazyLog2
+    // (exact in fp32 and in bf16's range), and the normalisation by the sum
+    // of the same probabilities cancels the reference: only rounding differs
+    // from rescaling on every new maximum.
+    const float mt2 = mt * a.sl2e;
+    const float mn = mt2 > m_run + kLazyLog2 ? mt2 : m_run;  // from -inf: any finite maximum
     const float mref = mn == -INFINITY ? 0.f : mn;
-    const float al = __builtin_amdgcn_exp2f(m_run - mref);
+    const float al = __builtin_amdgcn_exp2f(m_run - mref);   // exactly 1 where mn == m_run
     float pr[2][4];
     float ps = 0.f;
 #pragma unroll
@@ -424,8 +434,8 @@ __global__ __launch_bounds__(64 * kWaves) void prefill_attn_kernel(PrefillArgs a
       }
     ps = sum32(sum16(ps));
     l_run = l_run * al + ps;
-    // rescale only if some lane's maximum grew (elsewhere al == 1 exactly)
-    if (__any(mn > m_run)) {
+    // rescale only if some lane's reference moved (elsewhere al == 1 exactly)
+    if (__any(mn != m_run)) {
 #pragma unroll
       for (int dt = 0; dt < 16; ++dt) o[dt] *= al;
     }
