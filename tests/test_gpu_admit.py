@@ -12,11 +12,13 @@ import gpu_util as gu
 pytestmark = pytest.mark.gpu
 
 
-def _admit_case(w, seed, bank_n, layers=None):
+def _admit_case(w, seed, bank_n, layers=None, mutate=None):
     w = w.with_(bank_n=bank_n)
     st = synth.initial_state(w, seed)
     pf = synth.pending_fill(w, seed)
     st.update(pf)
+    if mutate is not None:
+        mutate(st)
     # a full pending block at position t0 + C
     w2 = w.with_(t0=w.t0 + w.C)
     S = rma.State(gu.cfg_for(w2), w2.B, gu.DEV, start_pos=w2.t0, bank_n=bank_n)
@@ -43,6 +45,39 @@ def test_admit_bit_exact_heavy_ties(bank_n):
     torch.cuda.synchronize()
     gu.check_state(S, o, f"admit bank_n={bank_n}")
     assert S.bank_n == [min(w.N, bank_n + w.C)] * w.L
+
+
+# Scores the total order has to place by rule: quiet NaNs of several
+# payloads and both signs (all equal, below -inf), +-inf, +-0 (equal),
+# the smallest denormals, the largest finite values and +-1.  Quiet NaNs
+# only: their bits survive every host copy unchanged.
+_SPECIAL_SCORES = np.array([0x7FC00000, 0xFFC00000, 0x7FC12345, 0x7F800000, 0xFF800000,
+                            0x00000000, 0x80000000, 0x00000001, 0x80000001, 0x7F7FFFFF,
+                            0xFF7FFFFF, 0x3F800000, 0xBF800000], np.uint32).view(np.float32)
+
+
+@pytest.mark.parametrize("bank_n", [1024, 900, 0])
+def test_admit_special_scores_bit_exact(bank_n):
+    """Bank and pending scores drawn, with heavy repetition, from NaNs,
+    infinities, signed zeros, denormals and the extreme finite values: the
+    kept set (score descending, then global index ascending, NaNs below
+    -inf, -0 equal to +0), the compaction and every moved record and score
+    (NaN payloads included) match the oracle bit for bit."""
+    gu.log(f"case admit special scores bank_n={bank_n}")
+    rng = np.random.default_rng(77 + bank_n)
+
+    def mutate(st):
+        for name in ("bscore", "pscore"):
+            st[name] = _SPECIAL_SCORES[rng.integers(0, len(_SPECIAL_SCORES),
+                                                    size=st[name].shape)].copy()
+
+    w = synth.WORKLOADS["admit_b512"].with_(B=4, L=2)
+    S, o = _admit_case(w, 41, bank_n, mutate=mutate)
+    S.admit(-1)
+    for l in range(w.L):
+        o.admit(l)
+    torch.cuda.synchronize()
+    gu.check_state(S, o, f"admit special scores bank_n={bank_n}")
 
 
 def test_admit_one_layer_at_a_time():

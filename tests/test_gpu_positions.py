@@ -219,6 +219,34 @@ def test_prefill_at_mixed_positions():
     assert [int(o.bank_n[0, 0, 0]) for o in oracles] == [1024, 900, 512]
 
 
+@pytest.mark.parametrize("B", [4, 448])
+def test_every_sequence_left_out_changes_nothing(B):
+    """Per-sequence decode and prefill calls with every position negative
+    (an empty batch): no output row and no byte of the history changes.
+    Batch 4 takes the split launches; batch 448 (ring 63, bank 64, commit
+    16) the whole-unit decode launch with its admit launch, and the
+    unsplit prefill."""
+    gu.log(f"case every sequence left out, B={B}")
+    w = synth.WORKLOADS["layer_b1"].with_(name=f"idle_b{B}", B=B, R=63, N=64, C=16,
+                                          t0=64 * 16, bank_n=64)
+    seed = 67
+    st = synth.initial_state(w, seed)
+    S = gu.gpu_state(w, st)
+    before = {name: S.read(name).clone() for name in gu.REGIONS + ("bank_n",)}
+    wg_dev = gu.to_dev(synth.gate_weights(w, seed)[0])
+    idle = torch.full((B,), -1, dtype=torch.int32, device=gu.DEV)
+    out = _decode_at(S, 0, [-1] * B, gu.inputs_to_dev(synth.step_inputs(w, seed, 0, 0)), wg_dev)
+    d = gu.inputs_to_dev(synth.block_inputs(w, seed, 0, 0, w.C))
+    pout = torch.full((B, w.C, w.H, w.d), SENTINEL, dtype=torch.bfloat16, device=gu.DEV)
+    S.prefill_block_at(0, idle, d["q"], d["k"], d["v"], d["ck"], d["cv"], d["cs"], wg_dev,
+                       out=pout)
+    torch.cuda.synchronize()
+    assert torch.all(out.float() == SENTINEL), "decode wrote an output row"
+    assert torch.all(pout.float() == SENTINEL), "prefill wrote an output row"
+    for name, v in before.items():
+        assert torch.equal(S.read(name), v), name
+
+
 def test_seq_reset_starts_a_new_sequence_in_a_used_slot():
     """A slot that held a long sequence is given a new one: bank count 0 in
     every layer, position 0; its stale ring and bank are never read."""
