@@ -1,5 +1,6 @@
 """GPU parity at geometries other than EdgeRock's: the largest admit pool
-(bank 1,792 + commit 256 = 2,048 keys), a small odd one (ring 99, bank 40,
+(bank 1,792 + commit 256 = 2,048 keys), the largest window (4,097: a ring
+of 4,096 positions, 64 decode tiles), a small odd one (ring 99, bank 40,
 commit 16: no tile is full, ragged everywhere) and commit 1 (an admit after
 every token).  Decode (lockstep and per-sequence), admit and prefill
 against the oracle built with the same geometry."""
@@ -16,6 +17,7 @@ pytestmark = pytest.mark.gpu
 GEOMETRIES = {
     # name: (ring R, bank N, commit C, t0, bank_n, B, steps)
     "max_pool": (1535, 1792, 256, 8192, 1792, 2, 300),
+    "max_window": (4096, 1024, 256, 8192, 1024, 2, 300),
     "small_odd": (99, 40, 16, 96, 33, 3, 70),
     "commit_1": (63, 20, 1, 70, 20, 2, 30),
 }
@@ -57,7 +59,7 @@ def test_decode_and_admit_at_other_geometries(name):
     assert admits >= 1
 
 
-@pytest.mark.parametrize("name", ["max_pool", "small_odd"])
+@pytest.mark.parametrize("name", ["max_pool", "max_window", "small_odd"])
 def test_per_sequence_decode_and_prefill_at_other_geometries(name):
     """Per-sequence calls at these geometries: a prefill block from a block
     start (admitted in the call when full), then decode steps across the
