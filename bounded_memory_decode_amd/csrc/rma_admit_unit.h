@@ -71,7 +71,10 @@ __device__ __forceinline__ uint64_t admit_pool_key(float score, uint32_t gidx) {
 }
 
 // Exclusive prefix sum over the 256 threads of the block; returns the sum
-// of the threads before this one and writes the total to *total.
+// of the threads before this one and writes the total to *total.  kSync:
+// end with a barrier, so that lds4 may be written again at once (a caller
+// that meets a barrier before its next scan passes false).
+template <bool kSync = true>
 __device__ __forceinline__ int admit_block_scan(int v, int* total, int* lds4) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   int x = v;
@@ -88,46 +91,54 @@ __device__ __forceinline__ int admit_block_scan(int v, int* total, int* lds4) {
     if (w < wave) before += lds4[w];
     all += lds4[w];
   }
-  __syncthreads();
+  if (kSync) __syncthreads();
   *total = all;
   return before + x - v;
 }
 
+// Pool entries per thread: thread tid holds entries tid * kPool ..
+// tid * kPool + kPool - 1 (bank_cap + commit <= 2,048 = 256 x 8).
+constexpr int kPool = 8;
+
 // The k-th largest (1 <= k <= valid keys) of the keys kv[r] held by the
-// block's threads (entry i = r * 256 + tid, valid iff i < P; keys are
+// block's threads (entry i = tid * kPool + r, valid iff i < P; keys are
 // distinct), by a radix select over 8-bit digits, most significant first.
-__device__ inline uint64_t admit_kth_largest(const uint64_t (&kv)[9], int P, int k,
+// Four barriers per pass: after the histogram, inside the scan, after the
+// digit is chosen, and one that both orders the reads of the choice before
+// the next pass and publishes the next pass's cleared histogram.
+__device__ inline uint64_t admit_kth_largest(const uint64_t (&kv)[kPool], int P, int k,
                                              AdmitShared& sh) {
   const int tid = threadIdx.x;
   uint64_t prefix = 0;  // the digits chosen so far
+  sh.hist[tid] = 0;
+  __syncthreads();
   for (int shift = 56; shift >= 0; shift -= 8) {
-    sh.hist[tid] = 0;
-    __syncthreads();
     const uint64_t above_mask = shift == 56 ? 0ull : (~0ull << (shift + 8));
 #pragma unroll
-    for (int r = 0; r < 9; ++r) {
-      const int i = r * kAdmitThreads + tid;
+    for (int r = 0; r < kPool; ++r) {
+      const int i = tid * kPool + r;
       if (i < P && (kv[r] & above_mask) == prefix)
         atomicAdd(&sh.hist[(int)((kv[r] >> shift) & 255u)], 1);
     }
     __syncthreads();
     // bins in descending digit order: thread tid holds digit 255 - tid
+    // (the scan's lds4 is next written after two more barriers)
     const int cnt = sh.hist[255 - tid];
     int tot = 0;
-    const int above = admit_block_scan(cnt, &tot, sh.lds4);  // keys with a larger digit
+    const int above = admit_block_scan<false>(cnt, &tot, sh.lds4);  // keys with a larger digit
     if (above < k && k <= above + cnt) {
       sh.sel[0] = 255 - tid;
       sh.sel[1] = above;
       sh.sel[2] = cnt;
     }
-    __syncthreads();
+    __syncthreads();  // the choice is visible; every bin has been read
     k -= sh.sel[1];
     prefix |= (uint64_t)sh.sel[0] << shift;
     if (sh.sel[2] == 1) {  // one key left with these digits: it is the k-th
       const uint64_t mask = ~0ull << shift;
 #pragma unroll
-      for (int r = 0; r < 9; ++r) {
-        const int i = r * kAdmitThreads + tid;
+      for (int r = 0; r < kPool; ++r) {
+        const int i = tid * kPool + r;
         if (i < P && (kv[r] & mask) == prefix) sh.kth = kv[r];
       }
       __syncthreads();
@@ -135,7 +146,8 @@ __device__ inline uint64_t admit_kth_largest(const uint64_t (&kv)[9], int P, int
       __syncthreads();  // every thread has read sel and kth before they change
       return t;
     }
-    __syncthreads();  // every thread has read sel before the next pass writes it
+    sh.hist[tid] = 0;  // the next pass's histogram
+    __syncthreads();   // ... and every thread has read sel before it is written again
   }
   return prefix;
 }
@@ -146,54 +158,60 @@ __device__ inline void admit_unit(const AdmitUnit& a, AdmitShared& sh) {
   const int n = *a.bank_n;
   const int P = n + C;
   const int K = P < N ? P : N;
-  const int R = (P + kAdmitThreads - 1) / kAdmitThreads;  // keys per thread, <= 8
+  static_assert(kAdmitThreads * kPool >= 2048, "the largest pool (bank_cap + commit)");
 
-  // the pool's keys, entry i = r * 256 + tid (past the pool: 0, below every
-  // real key); P <= N keeps everything, with no selection
-  uint64_t kv[9];
+  // the pool's keys, entry i = tid * kPool + r (past the pool: 0, below
+  // every real key); P <= N keeps everything, with no selection
+  uint64_t kv[kPool];
   uint64_t thr = 0;  // kept iff key >= thr
   if (P > N) {
     // all score loads first (one memory round trip); past the pool: a
     // clamped re-read, replaced by the key 0
-    float sv[9];
+    float sv[kPool];
 #pragma unroll
-    for (int r = 0; r < 9; ++r) {
-      const int i = r * kAdmitThreads + tid;
+    for (int r = 0; r < kPool; ++r) {
+      const int i = tid * kPool + r;
       const int ia = i < n ? i : n - 1;
       const int ic = i - n < C ? (i - n > 0 ? i - n : 0) : C - 1;
       sv[r] = i < n ? a.bscore[ia > 0 ? ia : 0] : a.pscore[ic];
     }
 #pragma unroll
-    for (int r = 0; r < 9; ++r) {
-      const int i = r * kAdmitThreads + tid;
+    for (int r = 0; r < kPool; ++r) {
+      const int i = tid * kPool + r;
       kv[r] = i < n ? admit_pool_key(sv[r], (uint32_t)i)
                     : (i < P ? admit_pool_key(sv[r], (uint32_t)(N + (i - n))) : 0ull);
     }
     thr = admit_kth_largest(kv, P, K, sh);
   } else {
 #pragma unroll
-    for (int r = 0; r < 9; ++r) kv[r] = 0;
+    for (int r = 0; r < kPool; ++r) kv[r] = 0;
   }
 
-  // evicted anchors and admitted candidates, both ascending: pool entry
-  // i = r * 256 + tid, round by round, through block scans (the two
-  // counts share one scan: each is < 2^16)
-  int ne = 0, na = 0;
-  for (int r = 0; r < R; ++r) {
-    const int i = r * kAdmitThreads + tid;
-    uint64_t key = kv[0];
+  // evicted anchors and admitted candidates, both ascending: each thread
+  // holds a contiguous run of the pool, so one block scan of the threads'
+  // counts places every entry (the two counts share the scan: each is
+  // < 2^16)
+  uint32_t evm = 0, adm = 0;  // bit r: entry tid * kPool + r is evicted / admitted
 #pragma unroll
-    for (int x = 1; x < 9; ++x) key = r == x ? kv[x] : key;
-    const bool kept = key >= thr;
-    const int ev = (i < n && !kept) ? 1 : 0;
-    const int ad = (i >= n && i < P && kept) ? 1 : 0;
-    int tot = 0;
-    const int before = admit_block_scan(ev | (ad << 16), &tot, sh.lds4);
-    if (ev) sh.evicted[ne + (before & 0xffff)] = i;
-    if (ad) sh.admitted[na + (before >> 16)] = i - n;
-    ne += tot & 0xffff;
-    na += tot >> 16;
+  for (int r = 0; r < kPool; ++r) {
+    const int i = tid * kPool + r;
+    const bool kept = kv[r] >= thr;
+    evm |= (i < n && !kept) ? 1u << r : 0u;
+    adm |= (i >= n && i < P && kept) ? 1u << r : 0u;
   }
+  int tot = 0;
+  const int before =
+      admit_block_scan(__builtin_popcount(evm) | (__builtin_popcount(adm) << 16), &tot, sh.lds4);
+  {
+    int pe = before & 0xffff, pa = before >> 16;
+#pragma unroll
+    for (int r = 0; r < kPool; ++r) {
+      const int i = tid * kPool + r;
+      if (evm & (1u << r)) sh.evicted[pe++] = i;
+      if (adm & (1u << r)) sh.admitted[pa++] = i - n;
+    }
+  }
+  const int ne = tot & 0xffff, na = tot >> 16;
   __syncthreads();
 
   // move the admitted records, K and V together in 4 batches, each with
