@@ -134,6 +134,85 @@ def test_oracle_equals_full_history_bruteforce(t0, bank_n, steps):
     assert o.t[0] == t0 + steps
 
 
+# edge geometries: (R, N, C, H, G, t0, bank_n)
+TINY_EDGES = {
+    "ring1": (1, 1, 1, 4, 2, 0, 0),
+    "ring1_full_bank": (1, 3, 1, 2, 1, 5, 3),
+    "ring2_commit2": (2, 16, 2, 4, 2, 6, 16),
+    "commit_eq_ring": (5, 2, 5, 4, 4, 10, 1),
+}
+
+
+def _random_tiny(case):
+    """A seeded tiny geometry: ring 1 .. 24, commit 1 .. min(8, ring),
+    bank 1 .. 16, heads per group 1, 2 or 4, a block-aligned start position
+    (no candidates pending, as the brute force starts) with the ring empty,
+    filling or full, and any bank count; or one of TINY_EDGES."""
+    rng = np.random.default_rng([0x7469, case if isinstance(case, int) else sum(map(ord, case))])
+    if case in TINY_EDGES:
+        R, N, C, H, G, t0, n = TINY_EDGES[case]
+        return rng, tiny(H=H, G=G, R=R, N=N, C=C, t0=t0, bank_n=n, ring_full=t0 > 0)
+    R = int(rng.integers(1, 25))
+    C = int(rng.integers(1, min(8, R) + 1))
+    N = int(rng.integers(1, 17))
+    G = int(rng.choice([1, 2, 4]))
+    H = G * int(rng.choice([1, 2, 4]))
+    t0 = C * int(rng.integers(0, (3 * R) // C + 2))
+    return rng, tiny(H=H, G=G, R=R, N=N, C=C, t0=t0, bank_n=int(rng.integers(0, N + 1)),
+                     ring_full=t0 > 0)
+
+
+@pytest.mark.parametrize("case", list(range(12)) + list(TINY_EDGES))
+def test_oracle_equals_bruteforce_at_random_geometries(case):
+    """Decode across several block ends, then a prompt block of drawn
+    length from the next block start, against the full-history brute force
+    at seeded random tiny geometries (one-slot rings, commit equal to the
+    ring, one-record banks and several heads per group all occur); the
+    bank's positions after every admit."""
+    rng, w = _random_tiny(case)
+    seed = 200 + (case if isinstance(case, int) else 50 + len(case))
+    o, st = make_oracle(w, seed)
+    wg = synth.gate_weights(w, seed)
+    bfs = [BruteForce(w.H, w.G, w.d, w.R, w.N, w.C, w.d ** -0.5, w.t0, st["ring_k"][0, b],
+                      st["ring_v"][0, b], st["bank_k"][0, b], st["bank_v"][0, b],
+                      st["bscore"][0, b], st["bsrc"][0, b], st["bank_n"][0, b])
+           for b in range(w.B)]
+    tag = f"R={w.R} N={w.N} C={w.C} H={w.H} G={w.G} t0={w.t0} bank_n={w.bank_n}"
+    step = 0
+
+    def check_bank():
+        for b in range(w.B):
+            for g in range(w.G):
+                nb = o.bank_n[0, b, g]
+                assert sorted(o.bsrc[0, b, g, :nb].tolist()) == bfs[b].bank_positions(g), tag
+
+    # decode over at least two block ends, then on to the next block start
+    end = w.t0 + 2 * w.C + 1
+    end += (-end) % w.C
+    while o.t[0] < end:
+        out, x = run_decode(o, w, seed, step, wg)
+        for b in range(w.B):
+            ref = bfs[b].step(x["q"][b], x["k"][b], x["v"][b], x["ck"][b], x["cv"][b],
+                              x["cs"][b], wg[0])
+            np.testing.assert_allclose(out[b], ref, rtol=0, atol=1e-12,
+                                       err_msg=f"{tag} step {step} sequence {b}")
+        step += 1
+        check_bank()
+    assert o.pend_n[0] == 0
+
+    n = int(rng.integers(1, w.C + 1))
+    x = synth.block_inputs(w, seed, 0, step, n)
+    out = o.prefill_block(0, x["q"], x["k"], x["v"], x["ck"], x["cv"], x["cs"], wg[0])
+    for i in range(n):
+        for b in range(w.B):
+            ref = bfs[b].step(x["q"][b, i], x["k"][b, i], x["v"][b, i], x["ck"][b, i],
+                              x["cv"][b, i], x["cs"][b, i], wg[0])
+            np.testing.assert_allclose(out[b, i], ref, rtol=0, atol=1e-12,
+                                       err_msg=f"{tag} prefill n={n} token {i} sequence {b}")
+    if n == w.C:
+        o.admit(0)
+    check_bank()
+
 def test_ring_holds_exactly_the_last_positions():
     w = tiny(steps=3 * 7 + 5)
     seed = 3
