@@ -141,8 +141,8 @@ __device__ __forceinline__ void store16(void* p, uint4 v) {
   *(__attribute__((address_space(1))) u32x4_t*)p = u32x4_t{v.x, v.y, v.z, v.w};
 }
 // The same store with the non-temporal hint, for the ring and pending
-// records the finish writes: the next read of them is the decode's own
-// non-temporal stream (about 1 us per launch at batch 512).
+// records the finish and the combine write: the next read of them is the
+// decode's own non-temporal stream (about 1 us per launch at batch 512).
 __device__ __forceinline__ void store16_nt(void* p, uint4 v) {
   __builtin_nontemporal_store(u32x4_t{v.x, v.y, v.z, v.w},
                               (__attribute__((address_space(1))) u32x4_t*)p);
@@ -973,16 +973,16 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   if (lane < 32) {
     if (h == 0) {
       uint4* rk = reinterpret_cast<uint4*>(a.ring_k + (size_t)u * a.Rk * kD);
-      rk[k_chunk_index(tp.ring_slot, lane, a.Rk)] = reinterpret_cast<const uint4*>(a.k + kvo)[lane];
+      store16_nt(&rk[k_chunk_index(tp.ring_slot, lane, a.Rk)], reinterpret_cast<const uint4*>(a.k + kvo)[lane]);
     } else if (h == 1) {
       uint4* rv = reinterpret_cast<uint4*>(a.ring_v + ((size_t)u * a.R + tp.ring_slot) * kD);
-      rv[lane] = reinterpret_cast<const uint4*>(a.v + kvo)[lane];
+      store16_nt(&rv[lane], reinterpret_cast<const uint4*>(a.v + kvo)[lane]);
     } else if (h == 2) {
       uint4* pk = reinterpret_cast<uint4*>(a.pend_k + ((size_t)u * a.C + tp.pend_slot) * kD);
-      pk[lane] = reinterpret_cast<const uint4*>(a.ck + kvo)[lane];
+      store16_nt(&pk[lane], reinterpret_cast<const uint4*>(a.ck + kvo)[lane]);
     } else {
       uint4* pv = reinterpret_cast<uint4*>(a.pend_v + ((size_t)u * a.C + tp.pend_slot) * kD);
-      pv[lane] = reinterpret_cast<const uint4*>(a.cv + kvo)[lane];
+      store16_nt(&pv[lane], reinterpret_cast<const uint4*>(a.cv + kvo)[lane]);
       if (lane == 0) a.pscore[(size_t)u * a.C + tp.pend_slot] = a.cs[(size_t)b * a.cs_bs + g];
     }
   }
@@ -990,7 +990,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs a) {
   // per-sequence positions: the token completes its block -> admit now
   // (the stores above are complete and visible to the block after the
   // barrier; no other workgroup touches this unit)
-  if (a.pos != nullptr && (tp.pos + 1) % a.C == 0) {
+  if (a.pos != nullptr && ((int64_t)tp.pos + 1) % a.C == 0) {  // 64-bit: pos may be 2^31 - 1
     __syncthreads();
     AdmitUnit au;
     au.bank_k = a.bank_k + (size_t)u * a.N * kD;

@@ -328,7 +328,7 @@ int rma_state_layout(const rma_config* cfg, int32_t batch, rma_layout* out) {
 
 int rma_state_init(rma_state* st, const rma_config* cfg, int32_t batch, void* dev_buf,
                    size_t bytes, int64_t start_pos, int32_t bank_n, void* stream) {
-  if (!st || !dev_buf || batch < 1 || start_pos < 0) return RMA_E_ARG;
+  if (!st || !dev_buf || batch < 1 || start_pos < 0 || start_pos > RMA_MAX_POS) return RMA_E_ARG;
   const int rc = check_config(cfg);
   if (rc != RMA_OK) return rc;
   if (((uintptr_t)dev_buf % kAlign) != 0) return RMA_E_ARG;
@@ -370,6 +370,7 @@ int rma_decode_step(rma_state* st, int32_t layer, const void* q, const void* k, 
   const rma_config& c = st->cfg;
   if (st->pend_n[layer] >= c.commit) return RMA_E_PENDING_FULL;
   const int64_t t = st->t[layer];
+  if (t > RMA_MAX_POS) return RMA_E_ARG;
   const int64_t H = c.q_heads, G = c.kv_groups;
   const rma::DecodeArgs a = decode_args(st, layer, t, q, k, v, cand_k, cand_v, cand_score, w_g,
                                         out, H * kD, G * kD, G, H * kD);
@@ -392,6 +393,7 @@ int rma_prefill_block(rma_state* st, int32_t layer, int32_t n_tokens, const void
     return RMA_E_ARG;
   const int64_t t0 = st->t[layer];
   if (st->pend_n[layer] != 0 || t0 % c.commit != 0) return RMA_E_NOT_BOUNDARY;
+  if (t0 + n_tokens - 1 > RMA_MAX_POS) return RMA_E_ARG;
   const rma::PrefillArgs a = prefill_args(st, layer, n_tokens, t0, nullptr, q, k, v, cand_k,
                                           cand_v, cand_score, w_g, out);
   const hipError_t e = rma::launch_prefill(a, static_cast<hipStream_t>(stream));

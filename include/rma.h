@@ -181,8 +181,13 @@ size_t rma_state_bytes(const rma_config* cfg, int32_t batch);
  * error. */
 int rma_state_layout(const rma_config* cfg, int32_t batch, rma_layout* out);
 
+/* Token positions run from 0 to RMA_MAX_POS: source positions are kept as
+ * int32 (bsrc), and the per-sequence calls take int32 positions. */
+#define RMA_MAX_POS ((int64_t)2147483647)
+
 /* Bind `dev_buf` (at least rma_state_bytes bytes, 256-byte aligned) to
- * *st and start every layer at position `start_pos` with `bank_n`
+ * *st and start every layer at position `start_pos` (0 .. RMA_MAX_POS)
+ * with `bank_n`
  * committed anchors (0 <= bank_n <= bank_cap) and start_pos % commit
  * pending candidates.  The history's memory is fixed before inference and
  * allocated once (tpsreport, "What this means"): this call takes the
@@ -208,7 +213,8 @@ int rma_state_init(rma_state* st, const rma_config* cfg, int32_t batch,
  *                                                 cfg.gate == RMA_GATE_GROUP)
  *   out        [batch][q_heads][head_dim]   bf16  result
  * Returns RMA_E_PENDING_FULL (state unchanged) when C candidates are
- * pending; call rma_admit first. */
+ * pending; call rma_admit first; RMA_E_ARG (state unchanged) when the
+ * token's position would pass RMA_MAX_POS. */
 int rma_decode_step(rma_state* st, int32_t layer, const void* q, const void* k,
                     const void* v, const void* cand_k, const void* cand_v,
                     const float* cand_score, const float* w_g, void* out,
@@ -225,7 +231,8 @@ int rma_decode_step(rma_state* st, int32_t layer, const void* q, const void* k,
  * rma_decode_step with a token axis after the batch axis:
  *   q [batch][n][q_heads][d], k/v/cand_k/cand_v [batch][n][kv_groups][d],
  *   cand_score [batch][n][kv_groups], out [batch][n][q_heads][d].
- * Returns RMA_E_NOT_BOUNDARY when t % commit != 0 or candidates pend. */
+ * Returns RMA_E_NOT_BOUNDARY when t % commit != 0 or candidates pend;
+ * RMA_E_ARG when the block's last position would pass RMA_MAX_POS. */
 int rma_prefill_block(rma_state* st, int32_t layer, int32_t n_tokens,
                       const void* q, const void* k, const void* v,
                       const void* cand_k, const void* cand_v,

@@ -156,6 +156,23 @@ def test_decode_validation_on_host():
     assert full.t[0] == 32768 and full.pend_n[0] == 256  # unchanged
 
 
+def test_positions_past_the_int32_range_are_rejected_on_host():
+    """Source positions are int32: a lockstep decode at position
+    RMA_MAX_POS + 1, a prefill block reaching past it, and a state started
+    past it are refused before anything is enqueued."""
+    L = rma.lib()
+    top = rma.RMA_MAX_POS + 1  # 2^31, a multiple of the commit interval 256
+    st = _fake_state(pend_n=0, t=top)
+    assert _decode(st) == rma.RMA_E_ARG
+    assert L.rma_prefill_block(ctypes.byref(st), 0, 1, *([FAKE] * 9)) == rma.RMA_E_ARG
+    assert st.t[0] == top and st.pend_n[0] == 0  # unchanged
+    c = rma.config_default()
+    s0 = rma._State()
+    n = rma.state_bytes(c, 2)
+    assert L.rma_state_init(ctypes.byref(s0), ctypes.byref(c), 2, FAKE, n, top, 0,
+                            None) == rma.RMA_E_ARG
+
+
 def test_admit_and_prefill_sequencing_on_host():
     L = rma.lib()
     st = _fake_state(pend_n=100, t=32768 + 100)

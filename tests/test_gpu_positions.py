@@ -247,6 +247,75 @@ def test_every_sequence_left_out_changes_nothing(B):
         assert torch.equal(S.read(name), v), name
 
 
+@pytest.mark.parametrize("B", [2, 448])
+def test_positions_at_the_int32_limit(B):
+    """Sequences whose last block ends at the last int32 position
+    (2^31 - 1; 256 divides 2^31, so that token completes a block): a
+    prompt block that ends there (admitted by the call), then decode steps
+    of other sequences across that same block end (admitted by the decode
+    call).  Batch 2 takes the split launches (the decode's admit runs in
+    its combine), batch 448 the whole-unit decode, its admit launch and
+    the unsplit prefill."""
+    gu.log(f"case positions at the int32 limit, B={B}")
+    base = synth.WORKLOADS["layer_b1"]
+    top = rma.RMA_MAX_POS
+    sampled = {0: (top + 1 - 3, 1024), B - 1: (top + 1 - 256, 700)}
+    seed = 68
+    states, oracles = _seq_oracles(base, list(sampled.values()), seed)
+    orc = dict(zip(sampled, oracles))
+    w = base.with_(B=B)
+    if B == len(sampled):
+        S = gu.assemble_state(w, states)
+    else:
+        S = rma.State(gu.cfg_for(w), B, gu.DEV, start_pos=0, bank_n=0)
+        S.buf.zero_()
+        S.seq_reset(0, B, 512)
+        for b, st in zip(sampled, states):
+            for name in gu.REGIONS + ("bank_n",):
+                S.write(name, st[name], batch=slice(b, b + 1))
+        torch.cuda.synchronize()
+    wg = synth.gate_weights(w, seed)
+    wg_dev = gu.to_dev(wg[0])
+    pos = [(b * 53) % 4096 for b in range(B)]
+    for b, (t0, _) in sampled.items():
+        pos[b] = t0
+
+    # the prompt block [2^31 - 256, 2^31) of the last sequence; the first
+    # is off a block start and left out
+    n = 256
+    x = synth.block_inputs(w, seed, 0, 0, n)
+    d = gu.inputs_to_dev(x)
+    out = torch.full((B, n, w.H, w.d), SENTINEL, dtype=torch.bfloat16, device=gu.DEV)
+    S.prefill_block_at(0, torch.tensor(pos, dtype=torch.int32, device=gu.DEV), d["q"], d["k"],
+                       d["v"], d["ck"], d["cv"], d["cs"], wg_dev, out=out)
+    o = orc[B - 1]
+    xb = _rows(x, B - 1)
+    ref = o.prefill_block(0, xb["q"], xb["k"], xb["v"], xb["ck"], xb["cv"], xb["cs"], wg[0])
+    assert o.pend_n[0] == o.C
+    o.admit(0)
+    gu.check_out(out[B - 1:B], ref, "prefill ending at 2^31 - 1",
+                 p_bf16_vmax=gu.vmax(o.ring_v, o.bank_v, xb["v"]))
+    _check_left_out(out, 0, "prefill at the int32 limit")
+    torch.cuda.synchronize()
+    gu.check_seq_state(S, B - 1, o, "after the prefill ending at 2^31 - 1")
+    assert int(o.bank_n[0, 0, 0]) == 956 and int(o.bsrc[0, 0, 0, :956].max()) >= top - 255
+
+    # decode: the first sequence crosses the same block end; the last has
+    # no position left and is left out
+    pos = [p + n if (b != 0 and p % 256 == 0) else p for b, p in enumerate(pos)]
+    pos[B - 1] = -1
+    for s in range(3):
+        x = synth.step_inputs(w, seed, 0, n + s)
+        out = _decode_at(S, 0, pos, gu.inputs_to_dev(x), wg_dev)
+        ref = _oracle_decode(orc[0], 0, _rows(x, 0), wg[0])
+        gu.check_out(out[0:1], ref, f"decode step {s} at {pos[0]}")
+        _check_left_out(out, B - 1, f"decode step {s}")
+        pos = [p + 1 if (p >= 0 and p < top) else -1 for p in pos]
+    torch.cuda.synchronize()
+    assert orc[0].t[0] == top + 1 and orc[0].pend_n[0] == 0  # admitted
+    for b in sampled:
+        gu.check_seq_state(S, b, orc[b], "int32 limit end")
+
 def test_seq_reset_starts_a_new_sequence_in_a_used_slot():
     """A slot that held a long sequence is given a new one: bank count 0 in
     every layer, position 0; its stale ring and bank are never read."""
