@@ -15,9 +15,10 @@ the largest window, a two-slot ring beside the largest pool).  Then:
   block start (one sequence off a block start is left out and must keep
   its state and output rows), then decode on from there.
 
-A last case runs a drawn geometry at batch 448, where the decode takes the
+Three cases run drawn geometries at batch 448, where the decode takes the
 whole-unit launch with its admit launch and the prefill its unsplit
-launch, and checks sampled sequences.  Outputs are compared within the
+launch, and check sampled sequences.  Four geometries run with a separate
+anchor query, under the per-head and the per-group gate.  Outputs are compared within the
 decode tolerance, the history bit for bit.  Every draw is fixed by the
 case's seed and logged before the case runs."""
 import zlib
@@ -252,3 +253,92 @@ def test_random_geometry_whole_unit_launch(name):
     torch.cuda.synchronize()
     for b in sampled:
         gu.check_seq_state(S, b, orc[b], f"{name} prefill end")
+
+
+def _states_and_oracles(w, specs, seed, gate_group):
+    states, oracles = [], []
+    for b, (t0, n) in enumerate(specs):
+        w1 = w.with_(B=1, t0=t0, bank_n=n)
+        st = synth.initial_state(w1, seed + b)
+        states.append(st)
+        oracles.append(OracleState.from_synth(st, H=w1.H, G=w1.G, d=w1.d, R=w1.R, N=w1.N,
+                                              C=w1.C, gate_group=gate_group))
+    return states, oracles
+
+
+@pytest.mark.parametrize("gate", ["head", "group"])
+@pytest.mark.parametrize("name", ["ring1_commit1", "bank1_window_max", "draw1", "draw3"])
+def test_random_geometry_anchor_query_and_gate(name, gate):
+    """The separate anchor query and both gate forms at drawn and edge
+    geometries: per-sequence decode of three sequences with a q_anchor
+    across their block ends, then a prefill block with a q_anchor for the
+    sequences at a block start (the others are left out)."""
+    rng, R, N, C = _geometry(name)
+    w = BASE.with_(name=name, R=R, N=N, C=C)
+    group = gate == "group"
+    seed = 120 + zlib.crc32(f"{name}/{gate}".encode()) % 50
+    # sequences 0 and 1 start 8 tokens before a block end (so the prefill
+    # finds them at a block start), sequence 2 at a drawn offset
+    k0 = -(-8 // C)
+    specs = [(C * int(rng.integers(k0, k0 + (3 * R) // C + 3)) - 8, int(rng.integers(0, N + 1)))
+             for _ in range(2)]
+    specs.append((_before_block_end(rng, R, C), int(rng.integers(0, N + 1))))
+    gu.log(f"case {name} gate={gate}: R={R} N={N} C={C}; decode_at with q_anchor from {specs}")
+    states, oracles = _states_and_oracles(w, specs, seed, group)
+    wb = w.with_(B=3)
+    S = rma.State(gu.cfg_for(wb, gate=rma.RMA_GATE_GROUP if group else rma.RMA_GATE_HEAD), 3,
+                  gu.DEV, start_pos=0, bank_n=0)
+    S.buf.zero_()
+    for b, st in enumerate(states):
+        for r in gu.REGIONS + ("bank_n",):
+            S.write(r, st[r], batch=slice(b, b + 1))
+    torch.cuda.synchronize()
+    wg = synth.gate_weights(wb, seed, per_group=group)
+    wg_dev = gu.to_dev(wg[0])
+    pos = [t0 for t0, _ in specs]
+    for s in range(8):
+        x = synth.step_inputs(wb, seed, 0, s)
+        qa = synth.anchor_query(wb, seed, 0, s)
+        xd = gu.inputs_to_dev(x)
+        out = S.decode_step_at(0, torch.tensor(pos, dtype=torch.int32, device=gu.DEV), xd["q"],
+                               xd["k"], xd["v"], xd["ck"], xd["cv"], xd["cs"], wg_dev,
+                               q_anchor=gu.to_dev(qa))
+        for b in range(3):
+            o = oracles[b]
+            xb = _rows(x, b)
+            ref = o.decode_step(0, xb["q"], xb["k"], xb["v"], xb["ck"], xb["cv"], xb["cs"], wg[0],
+                                q_anchor=qa[b:b + 1])
+            if o.pend_n[0] == o.C:
+                o.admit(0)
+            gu.check_out(out[b:b + 1], ref, f"{name} {gate} step {s} sequence {b} at {pos[b]}")
+            pos[b] += 1
+    torch.cuda.synchronize()
+    for b in range(3):
+        gu.check_seq_state(S, b, oracles[b], f"{name} {gate} decode end")
+
+    # the sequences now at a block start take a prefill block with a q_anchor
+    n = _logu(rng, 1, C)
+    at_start = [b for b in range(3) if pos[b] % C == 0]
+    assert 0 in at_start and 1 in at_start
+    gu.log(f"case {name} gate={gate}: prefill_at n={n}, sequences at a block start {at_start}")
+    x = synth.block_inputs(wb, seed, 0, 8, n)
+    qa = synth.block_anchor_query(wb, seed, 0, 8, n)
+    d = gu.inputs_to_dev(x)
+    out = torch.full((3, n, w.H, w.d), SENTINEL, dtype=torch.bfloat16, device=gu.DEV)
+    S.prefill_block_at(0, torch.tensor(pos, dtype=torch.int32, device=gu.DEV), d["q"], d["k"],
+                       d["v"], d["ck"], d["cv"], d["cs"], wg_dev, out=out, q_anchor=gu.to_dev(qa))
+    for b in range(3):
+        if b not in at_start:
+            assert torch.all(out[b].float() == SENTINEL), f"{name}: prefill wrote row {b}"
+            continue
+        o = oracles[b]
+        xb = _rows(x, b)
+        ref = o.prefill_block(0, xb["q"], xb["k"], xb["v"], xb["ck"], xb["cv"], xb["cs"], wg[0],
+                              q_anchor=qa[b:b + 1])
+        if o.pend_n[0] == o.C:
+            o.admit(0)
+        gu.check_out(out[b:b + 1], ref, f"{name} {gate} prefill sequence {b}",
+                      p_bf16_vmax=gu.vmax(o.ring_v, o.bank_v, xb["v"]))
+    torch.cuda.synchronize()
+    for b in range(3):
+        gu.check_seq_state(S, b, oracles[b], f"{name} {gate} prefill end")
