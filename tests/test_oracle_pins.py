@@ -213,6 +213,52 @@ def test_oracle_equals_bruteforce_at_random_geometries(case):
         o.admit(0)
     check_bank()
 
+
+@pytest.mark.parametrize("gate", ["head", "group"])
+@pytest.mark.parametrize("case", [1, 4, 6, 9, "ring1", "commit_eq_ring"])
+def test_oracle_anchor_query_and_gate_at_random_geometries(case, gate):
+    """The separate anchor query under both gate forms at seeded random and
+    edge tiny geometries: decode across two block ends, then a prompt block
+    of drawn length, against the full-history brute force."""
+    rng, w = _random_tiny(case)
+    group = gate == "group"
+    seed = 300 + (case if isinstance(case, int) else 50 + len(case)) + (7 if group else 0)
+    st = synth.initial_state(w, seed)
+    o = OracleState.from_synth(st, H=w.H, G=w.G, d=w.d, R=w.R, N=w.N, C=w.C, gate_group=group)
+    wg = synth.gate_weights(w, seed, per_group=group)
+    bfs = [BruteForce(w.H, w.G, w.d, w.R, w.N, w.C, w.d ** -0.5, w.t0, st["ring_k"][0, b],
+                      st["ring_v"][0, b], st["bank_k"][0, b], st["bank_v"][0, b],
+                      st["bscore"][0, b], st["bsrc"][0, b], st["bank_n"][0, b],
+                      gate_group=group) for b in range(w.B)]
+    tag = f"R={w.R} N={w.N} C={w.C} H={w.H} G={w.G} gate={gate}"
+    step = 0
+    end = w.t0 + 2 * w.C + 1
+    end += (-end) % w.C
+    while o.t[0] < end:
+        x = synth.step_inputs(w, seed, 0, step)
+        qa = synth.anchor_query(w, seed, 0, step)
+        out = o.decode_step(0, x["q"], x["k"], x["v"], x["ck"], x["cv"], x["cs"], wg[0],
+                            q_anchor=qa)
+        if o.pend_n[0] == o.C:
+            o.admit(0)
+        for b in range(w.B):
+            ref = bfs[b].step(x["q"][b], x["k"][b], x["v"][b], x["ck"][b], x["cv"][b],
+                              x["cs"][b], wg[0], q_anchor=qa[b])
+            np.testing.assert_allclose(out[b], ref, rtol=0, atol=1e-12,
+                                       err_msg=f"{tag} step {step} sequence {b}")
+        step += 1
+    n = int(rng.integers(1, w.C + 1))
+    x = synth.block_inputs(w, seed, 0, step, n)
+    qa = synth.block_anchor_query(w, seed, 0, step, n)
+    out = o.prefill_block(0, x["q"], x["k"], x["v"], x["ck"], x["cv"], x["cs"], wg[0],
+                          q_anchor=qa)
+    for i in range(n):
+        for b in range(w.B):
+            ref = bfs[b].step(x["q"][b, i], x["k"][b, i], x["v"][b, i], x["ck"][b, i],
+                              x["cv"][b, i], x["cs"][b, i], wg[0], q_anchor=qa[b, i])
+            np.testing.assert_allclose(out[b, i], ref, rtol=0, atol=1e-12,
+                                       err_msg=f"{tag} prefill n={n} token {i} sequence {b}")
+
 def test_ring_holds_exactly_the_last_positions():
     w = tiny(steps=3 * 7 + 5)
     seed = 3
