@@ -3,12 +3,13 @@
 // merges the two reads, the ring write and the pending append.
 //
 // Three launch shapes (launch_decode picks one per batch):
-//   * whole-unit (batch 96 and up, except where the last round of units
-//     would leave most waves idle): a wave of the persistent,
+//   * whole-unit (with 4 KV groups: batch 160-256 and 352 and up, where
+//     the units fill at least 5/8 of the resident waves in a single round,
+//     or 3/8 in a round after full ones): a wave of the persistent,
 //     wave-pipelined attention kernel owns a (sequence, group) unit, reads
 //     its ring then its bank, and finishes the token in-wave (current
 //     token, gate, output, ring write, pending append): one launch;
-//   * split, multi-tile parts (batch 33-95 and a few larger ones): reads
+//   * split, multi-tile parts (batch 33-159 and 257-351): reads
 //     are cut into parts of whole 64-key tiles taken by the same persistent
 //     kernel; partials go to scratch and a combine kernel finishes the
 //     token;
