@@ -19,6 +19,10 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "rma_oracle.c")
 _LIB = os.path.join(_HERE, "librma_oracle.so")
+# RMA_ORACLE_LIBRARY may name another build of this source, used as is: the
+# mutation test (tests/test_oracle_mutations.py) points it at copies with a
+# planted mistake to show that the pins fail on them.
+_OVERRIDE = os.environ.get("RMA_ORACLE_LIBRARY")
 
 ORC_OK, ORC_E_ARG, ORC_E_PENDING_FULL, ORC_E_NOT_BOUNDARY = 0, -1, -2, -3
 
@@ -56,9 +60,12 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
-            build(force=True)
-        L = ctypes.CDLL(_LIB)
+        if _OVERRIDE:
+            L = ctypes.CDLL(_OVERRIDE)
+        else:
+            if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+                build(force=True)
+            L = ctypes.CDLL(_LIB)
         L.orc_decode_step.argtypes = [ctypes.POINTER(_State), ctypes.c_int32] + [_P] * 8 + [_P, ctypes.c_int32]
         L.orc_decode_step.restype = ctypes.c_int
         L.orc_admit.argtypes = [ctypes.POINTER(_State), ctypes.c_int32, _P]
