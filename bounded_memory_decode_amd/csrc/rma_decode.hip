@@ -3,19 +3,22 @@
 // merges the two reads, the ring write and the pending append.
 //
 // Three launch shapes (launch_decode picks one per batch):
-//   * whole-unit (with 4 KV groups: batch 160-256 and 352 and up, where
-//     the units fill at least 5/8 of the resident waves in a single round,
-//     or 3/8 in a round after full ones): a wave of the persistent,
+//   * whole-unit (with 4 KV groups: batch 160-256 and 416-512, where
+//     the units fill at least 5/8 of the resident waves in their last
+//     round): a wave of the persistent,
 //     wave-pipelined attention kernel owns a (sequence, group) unit, reads
 //     its ring then its bank, and finishes the token in-wave (current
 //     token, gate, output, ring write, pending append): one launch;
-//   * split, multi-tile parts (batch 33-159 and 257-351): reads
-//     are cut into parts of whole 64-key tiles taken by the same persistent
-//     kernel; partials go to scratch and a combine kernel finishes the
-//     token;
+//   * split, multi-tile parts (batch 33-159): reads are cut into parts
+//     of whole 64-key tiles taken by the same persistent kernel; partials
+//     go to scratch and a combine kernel finishes the token;
 //   * split, one-tile parts (batch 1-32): one four-wave workgroup per
 //     64-key tile in decode_part_kernel (all loads at once, a 16-key block
 //     per wave, scores on MFMA), then the combine kernel.
+// A batch whose whole units would leave a later round less than 5/8 full
+// (batch 257-415) goes through two of these in turn (decode_whole_prefix):
+// the whole-unit launch for the sequences of the full rounds, then the
+// shape of the remaining batch for the rest.
 // Positions come from the lockstep arguments or, per sequence, from a
 // device array (TokPos); with per-sequence positions a completed block is
 // admitted right after the token (in the combine workgroup, or by an admit
@@ -1094,6 +1097,18 @@ bool whole_unit_launch(const DecodeArgs& a, bool* one) {
 static __device__ __align__(256) float scratch[kStaticScratchBytes / sizeof(float)];
 
 }  // namespace
+
+int decode_whole_prefix(const DecodeArgs& a) {
+  const bool qa = a.qa != nullptr;
+  const int waves = kWaves * (qa ? resident_workgroups<true, true, kWaves>()
+                                 : resident_workgroups<true, false, kWaves>());
+  if (waves <= 0 || a.units <= waves) return 0;
+  const int rounds = (a.units + waves - 1) / waves;
+  const int last = a.units - (rounds - 1) * waves;
+  if ((int64_t)last * 8 >= (int64_t)waves * 5) return 0;  // whole units fill the last round
+  const int k = (rounds - 1) * waves;
+  return k - k % a.G;  // whole sequences
+}
 
 size_t decode_scratch_bytes(const DecodeArgs& a) {
   bool one = false;

@@ -91,6 +91,23 @@ Splits choose_splits(const rma_config* c, int32_t batch) {
   return best;
 }
 
+// Sequences left to the split launch when a hybrid decode launch gives
+// the full rounds of 1,024 resident waves whole units (the rule of
+// rma::decode_whole_prefix with MI355X's 1,024 waves), or 0.  The layout
+// sizes its scratch for them; on a device with another wave count the
+// launch checks the need against the scratch it has.
+int32_t rest_batch(const rma_config* c, int32_t batch) {
+  constexpr int64_t kWavesPerLaunch = 1024;
+  const int64_t units = (int64_t)batch * c->kv_groups;
+  if (units <= kWavesPerLaunch) return 0;
+  const int64_t rounds = ceil_div64(units, kWavesPerLaunch);
+  const int64_t last = units - (rounds - 1) * kWavesPerLaunch;
+  if (last * 8 >= kWavesPerLaunch * 5) return 0;
+  int64_t k = (rounds - 1) * kWavesPerLaunch;
+  k -= k % c->kv_groups;
+  return (int32_t)(batch - k / c->kv_groups);
+}
+
 int make_layout(const rma_config* c, int32_t batch, rma_layout* L) {
   std::memset(L, 0, sizeof(*L));
   const uint64_t units = (uint64_t)c->layers * batch * c->kv_groups;
@@ -116,6 +133,14 @@ int make_layout(const rma_config* c, int32_t batch, rma_layout* L) {
   // split-K partials of the decode launch and, for small batches, of the
   // split prefill launch (never both at once: calls on a state are ordered)
   L->scratch_bytes = (uint64_t)batch * c->kv_groups * (sp.ring + sp.bank) * kPart * 4;
+  // ... and of the split launch of the sequences a hybrid decode launch
+  // leaves after its whole-unit rounds (rest_batch)
+  const int32_t rb = rest_batch(c, batch);
+  if (rb > 0) {
+    const Splits sr = choose_splits(c, rb);
+    const uint64_t r = (uint64_t)rb * c->kv_groups * (sr.ring + sr.bank) * kPart * 4;
+    L->scratch_bytes = r > L->scratch_bytes ? r : L->scratch_bytes;
+  }
   const rma::PrefillPlan pp = rma::prefill_plan(batch, c->kv_groups);
   if (pp.split()) {
     const uint64_t pf = (uint64_t)batch * c->commit * c->q_heads * pp.parts() * rma::kPfPart * 4;
@@ -206,6 +231,74 @@ rma::DecodeArgs decode_args(const rma_state* st, int32_t layer, int64_t t, const
   a.gate_group = c.gate == RMA_GATE_GROUP;
   a.sl2e = (float)((double)c.scale * 1.4426950408889634);
   return a;
+}
+
+// The decode of one layer's token as one or two launch_decode calls.  A
+// batch whose whole units would leave a later round of the resident waves
+// less than 5/8 full (rma::decode_whole_prefix) is decoded in two parts
+// on the stream, one after the other: the sequences of the full rounds
+// with the whole-unit launch (one unit per wave and round, nothing to
+// merge), then the remaining sequences with the launch shape and split
+// plan of their own batch.  The two parts touch disjoint units.  Where
+// the remaining part's partials would exceed `scratch_cap`, the whole
+// batch takes the single launch.
+struct DecodePlan {
+  rma::DecodeArgs head, rest;
+  bool two;
+};
+
+DecodePlan plan_decode(const rma_state* st, const rma::DecodeArgs& a, uint64_t scratch_cap) {
+  DecodePlan p;
+  p.head = a;
+  p.rest = a;
+  p.two = false;
+  const int k = rma::decode_whole_prefix(a);
+  if (k <= 0 || k >= a.units) return p;
+  const rma_config& c = st->cfg;
+  const int G = a.G, b0 = k / G;
+  const int64_t R = a.R, N = a.N, C = a.C, Rk = a.Rk;
+  rma::DecodeArgs r = a;
+  r.q += b0 * a.q_bs;
+  if (r.qa) r.qa += b0 * a.q_bs;
+  r.k += b0 * a.kv_bs;
+  r.v += b0 * a.kv_bs;
+  r.ck += b0 * a.kv_bs;
+  r.cv += b0 * a.kv_bs;
+  r.cs += b0 * a.cs_bs;
+  r.out += b0 * a.out_bs;
+  r.ring_k += (int64_t)k * Rk * kD;
+  r.ring_v += (int64_t)k * R * kD;
+  r.bank_k += (int64_t)k * N * kD;
+  r.bank_v += (int64_t)k * N * kD;
+  r.bank_n += k;
+  r.bscore += (int64_t)k * N;
+  r.bsrc += (int64_t)k * N;
+  r.pend_k += (int64_t)k * C * kD;
+  r.pend_v += (int64_t)k * C * kD;
+  r.pscore += (int64_t)k * C;
+  if (r.pos) r.pos += b0;
+  r.units = a.units - k;
+  const Splits sp = choose_splits(&c, r.units / G);
+  r.splits_ring = sp.ring;
+  r.splits_bank = sp.bank;
+  r.tiles_ring = sp.tiles_ring;
+  r.tiles_bank = sp.tiles_bank;
+  if (rma::decode_scratch_bytes(r) > scratch_cap) return p;
+  p.head.units = k;
+  p.rest = r;
+  p.two = true;
+  return p;
+}
+
+// Partials the plan writes (the whole-unit head writes none).
+uint64_t plan_scratch_bytes(const DecodePlan& p) {
+  return p.two ? rma::decode_scratch_bytes(p.rest) : rma::decode_scratch_bytes(p.head);
+}
+
+hipError_t launch_plan(const DecodePlan& p, hipStream_t s) {
+  const hipError_t e = rma::launch_decode(p.head, s);
+  if (e != hipSuccess || !p.two) return e;
+  return rma::launch_decode(p.rest, s);
 }
 
 rma::PrefillArgs prefill_args(const rma_state* st, int32_t layer, int32_t n_tokens, int64_t P,
@@ -374,7 +467,8 @@ int rma_decode_step(rma_state* st, int32_t layer, const void* q, const void* k, 
   const int64_t H = c.q_heads, G = c.kv_groups;
   const rma::DecodeArgs a = decode_args(st, layer, t, q, k, v, cand_k, cand_v, cand_score, w_g,
                                         out, H * kD, G * kD, G, H * kD);
-  const hipError_t e = rma::launch_decode(a, static_cast<hipStream_t>(stream));
+  const hipError_t e =
+      launch_plan(plan_decode(st, a, st->layout.scratch_bytes), static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(st, e);
   st->t[layer] = t + 1;
   st->pend_n[layer] += 1;
@@ -451,7 +545,8 @@ int rma_decode_step_at(rma_state* st, int32_t layer, const int32_t* pos, const v
                                   H * kD, G * kD, G, H * kD);
   a.pos = pos;
   a.qa = static_cast<const uint16_t*>(q_anchor);
-  const hipError_t e = rma::launch_decode(a, static_cast<hipStream_t>(stream));
+  const hipError_t e =
+      launch_plan(plan_decode(st, a, st->layout.scratch_bytes), static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(st, e);
   return RMA_OK;
 }
@@ -474,15 +569,17 @@ int rma_decode_step_at_static(rma_state* st, int32_t layer, const int32_t* pos, 
   a.qa = static_cast<const uint16_t*>(q_anchor);
   // the partials go to the library's static array of the state's device
   // instead of the state's scratch region; nothing is allocated
-  if (rma::decode_scratch_bytes(a) > rma::kStaticScratchBytes) return RMA_E_SCRATCH;
+  DecodePlan p = plan_decode(st, a, rma::kStaticScratchBytes);
+  if (plan_scratch_bytes(p) > rma::kStaticScratchBytes) return RMA_E_SCRATCH;
   hipPointerAttribute_t attr;
   hipError_t e = hipPointerGetAttributes(&attr, st->base);
   if (e != hipSuccess) return hip_fail(st, e);
   float* part = nullptr;
   e = rma::static_scratch(attr.device, &part);
   if (e != hipSuccess) return hip_fail(st, e);
-  a.part = part;
-  e = rma::launch_decode(a, static_cast<hipStream_t>(stream));
+  p.head.part = part;
+  p.rest.part = part;
+  e = launch_plan(p, static_cast<hipStream_t>(stream));
   if (e != hipSuccess) return hip_fail(st, e);
   return RMA_OK;
 }

@@ -76,6 +76,14 @@ struct DecodeArgs {
 // admit of every unit whose block the token completes.
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t s);
 
+// Units of a batch that the hybrid launch gives the whole-unit kernel:
+// its full rounds of resident waves, in whole sequences, when a
+// whole-unit launch of the batch would fill less than 5/8 of the waves in
+// a later round; 0 for a batch of one round or a well-filled last round.
+// The caller decodes those sequences with launch_decode on their own,
+// then the rest with their own split plan.
+int decode_whole_prefix(const DecodeArgs& a);
+
 // Bytes of split-K partials (a.part) launch_decode(a) writes and reads on
 // the current device: 0 when it takes the whole-unit launch.
 size_t decode_scratch_bytes(const DecodeArgs& a);

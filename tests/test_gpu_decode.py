@@ -55,14 +55,15 @@ def _run_trajectory(w, seed, steps, check_every=1, state_at_admit=True, out_batc
     return worst
 
 
-@pytest.mark.parametrize("B,kind", [(300, "split, two rounds of parts"),
+@pytest.mark.parametrize("B,kind", [(300, "two launches: 256 whole-unit sequences, 44 split"),
                                      (448, "whole-unit, a partial second round")])
 def test_launch_shapes_large_batch(B, kind):
     """Launch shapes that depend only on the number of units, run on a small
     geometry (ring 63, bank 64, commit 16) so that every sequence's state
-    and outputs can be checked: batch 300 (1,200 units; the last round of
-    whole units would leave most waves idle, so the split launch) and 448
-    (1,792 units: whole units in one-wave workgroups, the second round
+    and outputs can be checked: batch 300 (1,200 units; a second round of
+    whole units would leave most waves idle, so sequences 0-255 take the
+    whole-unit launch and 256-299 the split launch of a batch of 44) and
+    448 (1,792 units: whole units in one-wave workgroups, the second round
     partial).  40 steps across three block ends; every output every 4th step,
     the whole state at each admit and at the end."""
     gu.log(f"case launch shape B={B} ({kind})")

@@ -124,15 +124,20 @@ def test_staggered_positions_and_idle_sequence_vs_oracle():
     assert [int(o.bank_n[0, 0, 0]) for o in oracles] == [1024, 856, 1024, 256]
 
 
-def test_whole_unit_launch_staggered_sampled():
-    """Batch 256 (the whole-unit launch, one wave per sequence and group):
-    every sequence at its own position, some idle on even steps; six
-    sampled sequences against their oracles, every step."""
-    gu.log("case staggered positions, B=256 (whole-unit launch), 6 sampled sequences")
+@pytest.mark.parametrize("B", [256, 300])
+def test_whole_unit_launch_staggered_sampled(B):
+    """Batch 256 (the whole-unit launch, one wave per sequence and group)
+    and batch 300 (two launches: sequences 0-255 whole-unit with the admit
+    launch, 256-299 the split launch of a batch of 44 with the admit in its
+    combine): every sequence at its own position, some idle on even steps;
+    six sampled sequences against their oracles, every step."""
+    gu.log(f"case staggered positions, B={B} (whole-unit launch), 6 sampled sequences")
     base = synth.WORKLOADS["layer_b1"]
-    B = 256
     sampled = {0: (250, 1024), 3: (0, 0), 7: (1020, 768), 100: (511, 256), 203: (33010, 1024),
                255: (767, 512)}
+    if B == 300:
+        sampled = {0: (250, 1024), 255: (0, 0), 256: (1020, 768), 263: (511, 256),
+                   280: (33010, 1024), 299: (767, 512)}
     seed = 62
     states, oracles = _seq_oracles(base, list(sampled.values()), seed)
     w = base.with_(B=B)
@@ -219,13 +224,13 @@ def test_prefill_at_mixed_positions():
     assert [int(o.bank_n[0, 0, 0]) for o in oracles] == [1024, 900, 512]
 
 
-@pytest.mark.parametrize("B", [4, 448])
+@pytest.mark.parametrize("B", [4, 300, 448])
 def test_every_sequence_left_out_changes_nothing(B):
     """Per-sequence decode and prefill calls with every position negative
     (an empty batch): no output row and no byte of the history changes.
     Batch 4 takes the split launches; batch 448 (ring 63, bank 64, commit
     16) the whole-unit decode launch with its admit launch, and the
-    unsplit prefill."""
+    unsplit prefill; batch 300 both decode launches in turn."""
     gu.log(f"case every sequence left out, B={B}")
     w = synth.WORKLOADS["layer_b1"].with_(name=f"idle_b{B}", B=B, R=63, N=64, C=16,
                                           t0=64 * 16, bank_n=64)
