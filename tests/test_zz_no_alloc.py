@@ -1,8 +1,9 @@
 """The allocation-free decode entry point (rma_decode_step_at_static)
 against rma_decode_step_at: same inputs, same positions, two identical
-states; the outputs and every state region must agree bit for bit.  Two
-calls in a row, the second with a smaller batch (the static array keeps the
-first call's partials), then a batch whose partials exceed the array."""
+states; the outputs and every state region must agree bit for bit.  Calls
+in a row with ever smaller batches (the static array keeps the previous
+call's partials): batch 300 (two launches, the second split), 32 and 4;
+then a batch whose partials exceed the array."""
 import numpy as np
 import pytest
 import torch
@@ -42,7 +43,8 @@ def _run_pair(B, seed, steps, anchor_query):
 
 
 def test_static_scratch_decode_matches_state_scratch_decode():
-    gu.log("case allocation-free decode: batch 32, then batch 4")
+    gu.log("case allocation-free decode: batch 300, then 32, then 4")
+    _run_pair(300, 89, 4, anchor_query=False)  # whole-unit launch for 256, split for 44
     _run_pair(32, 90, 6, anchor_query=False)   # one-tile parts: 16.1 MiB of partials
     _run_pair(4, 91, 6, anchor_query=True)     # smaller input, separate anchor query
 
