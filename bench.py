@@ -264,6 +264,43 @@ def bench_admit_stress(S, w, seed, reps=5):
                          "kernel": "admit_kernel"}}
 
 
+def sdpa_reference(device, batch, reps=20):
+    """Yardstick for the prefill roofline: torch's own fused attention
+    (scaled_dot_product_attention, flash backend) on a dense problem of the
+    same algorithmic flop as one block-layer at this batch: per sequence 16
+    heads x 256 queries against 2,048 keys, head_dim 256, no mask, each
+    head with its own K/V rows (so the flop equals the block's 1,024 query
+    rows x 2,048 keys per group).  Measurement only; nothing on the
+    library's path uses it.  None where the backend is unavailable."""
+    import torch
+    try:
+        from torch.nn.attention import SDPBackend, sdpa_kernel
+        g = torch.Generator(device=device)
+        g.manual_seed(7)
+        H, T, S, D = 16, 256, 2048, 256
+        q, k, v = ((torch.randn((batch, H, n, D), generator=g, device=device) / 16)
+                   .to(torch.bfloat16).contiguous() for n in (T, S, S))
+        f = torch.nn.functional.scaled_dot_product_attention
+        with sdpa_kernel([SDPBackend.FLASH_ATTENTION]):
+            for _ in range(3):
+                f(q, k, v)
+            torch.cuda.synchronize()
+            e0, e1 = _event(), _event()
+            e0.record()
+            for _ in range(reps):
+                f(q, k, v)
+            e1.record()
+            torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / reps
+    except Exception as ex:  # backend missing on this build: report, do not fail the bench
+        return {"kernel": "torch scaled_dot_product_attention (flash)", "error": str(ex)[:200]}
+    flop = 4.0 * batch * H * T * S * D
+    return {"kernel": "torch scaled_dot_product_attention (flash backend), bf16",
+            "shape": f"batch {batch} x 16 heads x 256 queries x 2048 keys x head_dim 256, no mask",
+            "flop": flop, "us": round(us, 2), "TFLOP/s": round(flop / us / 1e6, 2),
+            "frac": round(flop / us / 1e6 / MFMA_BF16_PEAK_TFLOPS, 4)}
+
+
 def bench_prefill(device, seed, batch, blocks):
     """Time rma_prefill_block on full-history states: `blocks` blocks of
     256 tokens through all 8 layers, admit after each block."""
@@ -296,10 +333,12 @@ def bench_prefill(device, seed, batch, blocks):
     avg_ms = sum(ms) / len(ms)
     flop = PREFILL_FLOP_PER_GROUP * w.G * w.B
     tflops = flop / (avg_ms * 1e-3) / 1e12
-    del S
+    del S, ins, outs
     torch.cuda.empty_cache()
+    ref = sdpa_reference(device, batch)
     return {"workload": f"{w.L} layers x batch {w.B}, 256-token blocks on a full ring and bank "
                         f"(position {w.t0})",
+            "library_reference": ref,
             "batch": w.B, "blocks": blocks, "us_per_block_layer": round(avg_ms * 1e3, 2),
             "prefill_tokens_per_s": round(w.B * n / (avg_ms * 1e-3 * w.L), 1),
             "roofline": {"bound": "mfma", "achieved": round(tflops, 2),
@@ -855,6 +894,10 @@ def main():
             r = bench_prefill(device, args.seed, pb, args.prefill_blocks)
             say(f"[bench] prefill batch {pb}: {r['us_per_block_layer']} us per block-layer, "
                 f"{r['roofline']['achieved']} TFLOP/s ({100 * r['roofline']['frac']:.1f}% of bf16 MFMA peak)")
+            ref = r["library_reference"]
+            if "us" in ref:
+                say(f"[bench] torch flash attention, same flop: {ref['us']} us, {ref['TFLOP/s']} TFLOP/s "
+                    f"({100 * ref['frac']:.1f}% of peak)")
             result["prefill"].append(r)
     print(json.dumps(result), flush=True)
 
