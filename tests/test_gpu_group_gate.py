@@ -25,14 +25,18 @@ def _setup(w, seed):
     return S, o, wg, gu.to_dev(wg[0])
 
 
-@pytest.mark.parametrize("B,anchor_query", [(448, False), (448, True), (3, False), (4, True)],
-                         ids=["whole-unit", "whole-unit-qa", "split", "split-qa"])
+@pytest.mark.parametrize("B,anchor_query", [(448, False), (448, True), (300, False), (300, True),
+                                             (3, False), (4, True)],
+                         ids=["whole-unit", "whole-unit-qa", "two-launch", "two-launch-qa", "split",
+                              "split-qa"])
 def test_group_gate_decode(B, anchor_query):
-    """Decode across block ends with the per-group gate.  Batch 448 runs on
-    a small geometry (ring 63, bank 64, commit 16: 1,792 units, the
-    whole-unit launch), batches 3 and 4 on the EdgeRock geometry (the split
-    launch).  Per-sequence calls with a separate anchor query, lockstep
-    calls without; every output every few steps and the state at the end."""
+    """Decode across block ends with the per-group gate.  Batches 448 and
+    300 run on a small geometry (ring 63, bank 64, commit 16: 1,792 units,
+    the whole-unit launch; 1,200 units, the whole-unit launch for sequences
+    0-255 and the split launch for the rest), batches 3 and 4 on the
+    EdgeRock geometry (the split launch).  Per-sequence calls with a
+    separate anchor query, lockstep calls without; every output every few
+    steps and the state at the end (in both parts of the two-launch batch)."""
     gu.log(f"case group gate decode B={B} q_anchor={anchor_query}")
     if B >= 160:
         w = synth.WORKLOADS["sharp_b1"].with_(name=f"group_b{B}", B=B, R=63, N=64, C=16,
@@ -68,7 +72,7 @@ def test_group_gate_decode(B, anchor_query):
                 S.admit(0)
             o.admit(0)
     torch.cuda.synchronize()
-    for b in (0, B // 2, B - 1):
+    for b in sorted({0, B // 2, min(B - 1, 255), min(B - 1, 256), B - 1}):
         gu.check_seq_state(S, b, _one(o, b), f"group gate B={B}")
     gu.log(f"group gate decode B={B}: worst error {worst:.3e}")
 
