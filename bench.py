@@ -167,20 +167,7 @@ PREFILL_FLOP_PER_GROUP = 1024 * (1024 + 1024) * 256 * 2 * 2   # 2.147 GFLOP
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
-def bench_calibration(device, gib=8, waves=1024, reps=9, warm=3):
-    """Achievable read bandwidth: rma_calib_stream_read (a streaming-read
-    kernel of this library, 16-byte non-temporal loads, 16 in flight per
-    lane) over a `gib` GiB buffer with `waves` waves (the decode kernel's
-    resident wave count).  `warm` untimed passes, then `reps` passes timed
-    with events; the best pass is the achievable figure (the median is
-    listed beside it).  Run first, before the state is allocated: after a
-    minute of load it read up to 6% lower on the same box."""
-    import torch
-    from bounded_memory_decode_amd import rma
-    n = gib << 30
-    buf = torch.empty(n, dtype=torch.uint8, device=device)
-    buf.fill_(1)
-    sink = torch.empty(waves, dtype=torch.int32, device=device)
+def _time_stream(rma, buf, waves, sink, reps, warm):
     for _ in range(warm):
         rma.calib_stream_read(buf, waves, sink)
     ms = []
@@ -189,16 +176,45 @@ def bench_calibration(device, gib=8, waves=1024, reps=9, warm=3):
         e0.record()
         rma.calib_stream_read(buf, waves, sink)
         e1.record()
+        import torch
         torch.cuda.synchronize()
         ms.append(e0.elapsed_time(e1))
+    return min(ms), _median(ms)
+
+
+def bench_calibration(device, gib=8, waves=1024, reps=9, warm=3, launch_bytes=None):
+    """Achievable read bandwidth: rma_calib_stream_read (a streaming-read
+    kernel of this library, 16-byte non-temporal loads, 16 in flight per
+    lane) over a `gib` GiB buffer with `waves` waves (the decode kernel's
+    resident wave count).  `warm` untimed passes, then `reps` passes timed
+    with events; the best pass is the achievable figure (the median is
+    listed beside it).  Run first, before the state is allocated: after a
+    minute of load it read up to 6% lower on the same box.  With
+    `launch_bytes`, the same probe also reads a prefix of the buffer of
+    that size (rounded up to the probe's granularity): a launch as long as
+    the decode's, whose ramp-up and tail weigh as much as the decode's do."""
+    import torch
+    from bounded_memory_decode_amd import rma
+    n = gib << 30
+    buf = torch.empty(n, dtype=torch.uint8, device=device)
+    buf.fill_(1)
+    sink = torch.empty(waves, dtype=torch.int32, device=device)
+    best, med = _time_stream(rma, buf, waves, sink, reps, warm)
+    r = {"kernel": "stream_read_kernel (rma_calib_stream_read): every wave reads its own "
+                   "contiguous share with 16-byte non-temporal loads",
+         "bytes": n, "waves": waves, "passes": reps, "ms": round(best, 4),
+         "GBps": round(n / (best * 1e-3) / 1e9, 1),
+         "median_GBps": round(n / (med * 1e-3) / 1e9, 1)}
+    if launch_bytes:
+        gran = waves * 16 * 1024
+        nb = min(n, -(-launch_bytes // gran) * gran)
+        lb, lm = _time_stream(rma, buf[:nb], waves, sink, reps, warm)
+        r["launch_size"] = {"bytes": nb, "ms": round(lb, 4),
+                            "GBps": round(nb / (lb * 1e-3) / 1e9, 1),
+                            "median_GBps": round(nb / (lm * 1e-3) / 1e9, 1)}
     del buf, sink
     torch.cuda.empty_cache()
-    best, med = min(ms), _median(ms)
-    return {"kernel": "stream_read_kernel (rma_calib_stream_read): every wave reads its own "
-                      "contiguous share with 16-byte non-temporal loads",
-            "bytes": n, "waves": waves, "passes": reps, "ms": round(best, 4),
-            "GBps": round(n / (best * 1e-3) / 1e9, 1),
-            "median_GBps": round(n / (med * 1e-3) / 1e9, 1)}
+    return r
 
 
 def bench_admit_stress(S, w, seed, reps=5):
@@ -715,8 +731,10 @@ def main():
     if args.calibration_gib > 0:
         # first, on a device with nothing else allocated
         say(f"[bench] streaming-read calibration, {args.calibration_gib} GiB")
-        cal = bench_calibration(device, args.calibration_gib)
-        say(f"[bench] stream read: {cal['GBps']} GB/s")
+        cal = bench_calibration(device, args.calibration_gib,
+                                launch_bytes=w.B * w.G * UNIT_BYTES)
+        say(f"[bench] stream read: {cal['GBps']} GB/s; a launch of the decode's "
+            f"{cal['launch_size']['bytes']:,} B: {cal['launch_size']['GBps']} GB/s")
     say(f"[bench] building state: {w.name} B={w.B} L={w.L}")
     S = make_state(w, args.seed, device)
     sets, wg, outs = make_pool(w, args.seed, device)
@@ -867,8 +885,10 @@ def main():
     torch.cuda.empty_cache()
     if cal is not None:
         cal["decode_frac_of_stream"] = round(achieved / cal["GBps"], 4)
+        cal["decode_frac_of_stream_launch_size"] = round(achieved / cal["launch_size"]["GBps"], 4)
         result["calibration"] = cal
-        say(f"[bench] decode at {100 * cal['decode_frac_of_stream']:.1f}% of the stream read")
+        say(f"[bench] decode at {100 * cal['decode_frac_of_stream']:.1f}% of the stream read, "
+            f"{100 * cal['decode_frac_of_stream_launch_size']:.1f}% of a stream read of its own size")
     if args.long_blocks > 0:
         say(f"[bench] long path: {args.long_blocks} prompt blocks, {args.long_decode} decode tokens")
         result["long"] = bench_long(device, args.seed, args.long_blocks, args.long_decode,
