@@ -1150,7 +1150,10 @@ hipError_t launch_decode(const DecodeArgs& a, hipStream_t s) {
   // below 160 (at 96: 142 against 153 us; at 128: 178 against 190; at 112
   // whole units win by 3%) and at 288-320 (last rounds of 128-256 units:
   // 455 against 466 us at 320); at 352 (a last round of 384 after a full
-  // one) whole units win, 491 against 518 us.  With at least one unit per wave, one-wave
+  // one) whole units win, 491 against 518 us.  (Callers hand a batch
+  // with a later round under 5/8 full to this function in two parts, see
+  // decode_whole_prefix; the 3/8 rule remains for the whole batch when the
+  // remainder's partials would not fit the scratch.)  With at least one unit per wave, one-wave
   // workgroups (704 against 713 us per launch at batch 512, 637 against
   // 651 at 448); for a single round of 5/8 or more, four-wave ones, which
   // fill fewer CUs completely (237 against 241 us at batch 160, 272
