@@ -572,6 +572,12 @@ def bench_layer_config(device, seed, name):
         r["roofline"] = {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                          "launch_time": "eager window minus its admits, per decode launch"}
+        # the streaming-read probe over a launch of the same size (its ramp-up
+        # and tail weigh as much as this short launch's do)
+        gib = -(-launch_bytes // (1 << 30))
+        probe = bench_calibration(device, gib, launch_bytes=launch_bytes)["launch_size"]
+        r["roofline"]["stream_probe_same_size"] = probe
+        r["roofline"]["frac_of_probe"] = round(gbs / probe["GBps"], 4)
     else:
         r["note"] = "state resident in the last-level cache: latency, not HBM bandwidth"
     return r
@@ -905,6 +911,11 @@ def main():
             say(f"[bench] {name}: eager {r['eager_us_per_step']} us/step (decode launch "
                 f"{r['eager_decode_launch_us']} us, admit {r['admit_us']} us), graph "
                 f"{r['graph_us_per_step']} us/step")
+            if "roofline" in r:
+                rf = r["roofline"]
+                say(f"[bench] {name}: decode launch {rf['achieved']} GB/s, "
+                    f"{100 * rf['frac_of_probe']:.1f}% of a stream read of its size "
+                    f"({rf['stream_probe_same_size']['GBps']} GB/s)")
             result["layers"].append(r)
     if args.prefill_blocks > 0:
         torch.cuda.empty_cache()
