@@ -168,6 +168,8 @@ MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
 def _time_stream(rma, buf, waves, sink, reps, warm):
+    """Best and median ms of `reps` timed streaming reads of `buf`."""
+    import torch
     for _ in range(warm):
         rma.calib_stream_read(buf, waves, sink)
     ms = []
@@ -176,7 +178,6 @@ def _time_stream(rma, buf, waves, sink, reps, warm):
         e0.record()
         rma.calib_stream_read(buf, waves, sink)
         e1.record()
-        import torch
         torch.cuda.synchronize()
         ms.append(e0.elapsed_time(e1))
     return min(ms), _median(ms)
