@@ -28,7 +28,7 @@ RMA_OK, RMA_E_ARG, RMA_E_PENDING_FULL, RMA_E_NOT_BOUNDARY, RMA_E_HIP, RMA_E_UNSU
     0, -1, -2, -3, -4, -5
 RMA_E_SCRATCH = -6
 RMA_GATE_HEAD, RMA_GATE_GROUP = 0, 1
-RMA_STATIC_SCRATCH_BYTES = 40 << 20
+RMA_STATIC_SCRATCH_BYTES = 80 << 20
 RMA_MAX_POS = 2 ** 31 - 1
 
 # every symbol include/rma.h and include/rma_calib.h declare

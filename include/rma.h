@@ -312,10 +312,13 @@ int rma_prefill_block_at(rma_state* st, int32_t layer, int32_t n_tokens, const i
  * overlap on one GPU (other streams, other states) race: order them.  The
  * kernels write every partial before reading it; nothing needs clearing.
  * Returns RMA_E_SCRATCH, before anything is enqueued, when the batch's
- * partials exceed the array (never at the EdgeRock geometry, whose
- * largest need is 36.3 MiB, at batches 144 and 288); otherwise as
- * rma_decode_step_at. */
-#define RMA_STATIC_SCRATCH_BYTES ((size_t)40 << 20)
+ * partials would exceed the array; otherwise as rma_decode_step_at.  On
+ * MI355X the array holds the partials of every configuration and batch
+ * the library accepts: a split launch covers fewer than 640 units, at
+ * most 32 partials of 4,128 B each, and the largest need, 76.6 MiB, is
+ * the EdgeRock geometry's at batch 152 (and at 408, 664, ..., whose
+ * second launch is that batch).  The check guards the bound. */
+#define RMA_STATIC_SCRATCH_BYTES ((size_t)80 << 20)
 int rma_decode_step_at_static(rma_state* st, int32_t layer, const int32_t* pos, const void* q,
                               const void* q_anchor, const void* k, const void* v,
                               const void* cand_k, const void* cand_v, const float* cand_score,

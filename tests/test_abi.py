@@ -272,3 +272,15 @@ def test_calibration_probe_rejects_bad_arguments(buf, nbytes, waves, sink):
     """rma_calib_stream_read refuses bad arguments on the host (-1) before
     anything is launched."""
     assert rma.lib().rma_calib_stream_read(buf, nbytes, waves, sink, None) == -1
+
+
+def test_binding_constants_follow_the_header():
+    """The binding's copies of the header's size constants are the header's."""
+    import re
+    h = open(os.path.join(ROOT, "include", "rma.h")).read()
+    m = re.search(r"#define RMA_STATIC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", h)
+    assert m, "RMA_STATIC_SCRATCH_BYTES not found in include/rma.h"
+    assert rma.RMA_STATIC_SCRATCH_BYTES == int(m.group(1)) << int(m.group(2))
+    # the largest split-K partials of an accepted configuration: 608 units
+    # (batch 152 of the EdgeRock geometry) in 32 one-tile parts of 4,128 B
+    assert 608 * 32 * 4128 <= rma.RMA_STATIC_SCRATCH_BYTES

@@ -2,8 +2,8 @@
 against rma_decode_step_at: same inputs, same positions, two identical
 states; the outputs and every state region must agree bit for bit.  Calls
 in a row with ever smaller batches (the static array keeps the previous
-call's partials): batch 300 (two launches, the second split), 32 and 4;
-then a batch whose partials exceed the array."""
+call's partials): batch 300 (two launches, the second split), 152 (the
+largest partials of any accepted configuration), 32 and 4."""
 import numpy as np
 import pytest
 import torch
@@ -43,30 +43,9 @@ def _run_pair(B, seed, steps, anchor_query):
 
 
 def test_static_scratch_decode_matches_state_scratch_decode():
-    gu.log("case allocation-free decode: batch 300, then 32, then 4")
+    gu.log("case allocation-free decode: batch 300, then 152, 32 and 4")
     _run_pair(300, 89, 4, anchor_query=False)  # whole-unit launch for 256, split for 44
+    _run_pair(152, 88, 4, anchor_query=False)  # the largest need: 608 units x 32 parts, 76.6 MiB
     _run_pair(32, 90, 6, anchor_query=False)   # one-tile parts: 16.1 MiB of partials
     _run_pair(4, 91, 6, anchor_query=True)     # smaller input, separate anchor query
 
-
-def test_static_scratch_rejects_partials_beyond_the_array():
-    """Ring 1,535, bank 1,792, batch 144: the split launch cuts each read of
-    576 units into 26 parts, 61.8 MB of partials, beyond the 40 MiB array.
-    The call is refused before anything is enqueued."""
-    gu.log("case allocation-free decode: partials beyond the array")
-    cfg = rma.config_default(layers=1, window=1536, bank_cap=1792)
-    B, H, G, d = 144, cfg.q_heads, cfg.kv_groups, cfg.head_dim
-    S = rma.State(cfg, B, gu.DEV, start_pos=0, bank_n=0)
-    bf = dict(dtype=torch.bfloat16, device=gu.DEV)
-    q = torch.zeros((B, H, d), **bf)
-    kv = torch.zeros((B, G, d), **bf)
-    cs = torch.zeros((B, G), dtype=torch.float32, device=gu.DEV)
-    wg = torch.zeros((H, d), dtype=torch.float32, device=gu.DEV)
-    out = torch.empty((B, H, d), **bf)
-    pos = torch.zeros((B,), dtype=torch.int32, device=gu.DEV)
-    with pytest.raises(rma.RmaError) as e:
-        S.decode_step_at_static(0, pos, q, kv, kv, kv, kv, cs, wg, out)
-    assert e.value.code == rma.RMA_E_SCRATCH
-    torch.cuda.synchronize()
-    assert torch.equal(S.read("bank_n"), torch.zeros((1, B, G), dtype=torch.int32,
-                                                      device=gu.DEV))
