@@ -425,3 +425,69 @@ def test_token_step_graph_replays_match_eager_and_oracle():
     for name in gu.REGIONS + ("bank_n",):
         assert torch.equal(A.read(name), D.read(name)), name
     gu.check_seq_state(A, 0, o, "graph end")
+
+
+def test_graph_replays_of_the_two_launch_batch():
+    """Batch 300 on a small geometry (ring 63, bank 64, commit 16): the
+    per-sequence decode takes two launches (whole units for sequences
+    0-255 with their admit launch, the split launch with the admit in its
+    combine for 256-299).  Two layers of one token, captured once with the
+    position increment, replayed across block ends with staggered
+    positions: every replay equals the eager calls bit for bit, and so does
+    the whole history at the end."""
+    gu.log("case graph replay, B=300 (two launches), 2 layers")
+    B = 300
+    w = synth.WORKLOADS["layer_b1"].with_(name="graph_b300", B=B, L=2, R=63, N=64, C=16,
+                                          t0=64 * 16, bank_n=64)
+    seed = 66
+    st = synth.initial_state(w, seed)
+    A = gu.gpu_state(w, st)
+    D = gu.gpu_state(w, st)
+    wg = synth.gate_weights(w, seed)
+    wg_dev = [gu.to_dev(wg[l]) for l in range(w.L)]
+    L, H, G, d = w.L, w.H, w.G, w.d
+    q_s = torch.zeros((L, B, H, d), dtype=torch.bfloat16, device=gu.DEV)
+    kv_s = {k: torch.zeros((L, B, G, d), dtype=torch.bfloat16, device=gu.DEV)
+            for k in ("k", "v", "ck", "cv")}
+    cs_s = torch.zeros((L, B, G), dtype=torch.float32, device=gu.DEV)
+    out_s = torch.zeros((L, B, H, d), dtype=torch.bfloat16, device=gu.DEV)
+    # staggered: sequence b at block offset b mod 16, so every replay ends
+    # some sequences' blocks on both sides of the two launches
+    pos0 = torch.tensor([w.t0 + (b % 16) for b in range(B)], dtype=torch.int32, device=gu.DEV)
+    pos_a, pos_d = pos0.clone(), pos0.clone()
+
+    Wst = rma.State(gu.cfg_for(w), B, gu.DEV, start_pos=0, bank_n=0)
+    Wst.decode_step_at(0, torch.zeros((B,), dtype=torch.int32, device=gu.DEV), q_s[0],
+                       kv_s["k"][0], kv_s["v"][0], kv_s["ck"][0], kv_s["cv"][0], cs_s[0],
+                       wg_dev[0])
+    torch.cuda.synchronize()
+
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for l in range(L):
+            A.decode_step_at(l, pos_a, q_s[l], kv_s["k"][l], kv_s["v"][l], kv_s["ck"][l],
+                             kv_s["cv"][l], cs_s[l], wg_dev[l], out=out_s[l])
+        pos_a.add_(1)
+    torch.cuda.synchronize()
+
+    for s in range(20):
+        for l in range(L):
+            xd = gu.inputs_to_dev(synth.step_inputs(w, seed, l, s))
+            q_s[l].copy_(xd["q"])
+            for k in kv_s:
+                kv_s[k][l].copy_(xd[k])
+            cs_s[l].copy_(xd["cs"])
+        g.replay()
+        torch.cuda.synchronize()
+        for l in range(L):
+            xd = gu.inputs_to_dev(synth.step_inputs(w, seed, l, s))
+            od = D.decode_step_at(l, pos_d, xd["q"], xd["k"], xd["v"], xd["ck"], xd["cv"],
+                                  xd["cs"], wg_dev[l])
+            torch.cuda.synchronize()
+            assert torch.equal(out_s[l].view(torch.int16), od.view(torch.int16)), \
+                f"replay {s} layer {l}"
+        pos_d += 1
+    torch.cuda.synchronize()
+    assert torch.equal(pos_a, pos_d)
+    for name in gu.REGIONS + ("bank_n",):
+        assert torch.equal(A.read(name), D.read(name)), name
