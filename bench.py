@@ -512,7 +512,9 @@ def bench_layer_config(device, seed, name):
              steps / 16 times, so that the host's graph launch is shared
              by 16 tokens.
     Batch 1 keeps its whole state (8 MiB) in the 256 MB last-level cache,
-    so its figures are latency; batch 64 (537 MB) streams from HBM."""
+    so its figures are latency; batch 64 (537 MB) and batch 288 (2.4 GB,
+    decoded in two launches: whole units for 256 sequences, the split
+    launch for 32) stream from HBM."""
     import torch
     from bounded_memory_decode_amd import synth
     w = synth.WORKLOADS[name]
@@ -707,7 +709,7 @@ def main():
     ap.add_argument("--prefill-blocks", type=int, default=4,
                     help="256-token blocks timed per prefill batch size (0: skip)")
     ap.add_argument("--layer-configs", type=int, default=1,
-                    help="1: time the one-layer workloads at batch 1 and 64 (0: skip)")
+                    help="1: time the one-layer workloads at batch 1, 64 and 288 (0: skip)")
     ap.add_argument("--calibration-copy-gib", type=int, default=0,
                     help="before timing, copy a buffer of this many GiB three times "
                          "(a plain copy kernel of known size, for scaling HBM counters)")
@@ -906,7 +908,7 @@ def main():
             f"{r['graph_us_per_token']} us/token as graph replays, {r['eager_us_per_token']} eager")
     if args.layer_configs > 0:
         result["layers"] = []
-        for name in ("layer_b1", "layer_b64"):
+        for name in ("layer_b1", "layer_b64", "layer_b288"):
             say(f"[bench] one layer: {name}")
             r = bench_layer_config(device, args.seed, name)
             say(f"[bench] {name}: eager {r['eager_us_per_step']} us/step (decode launch "

@@ -85,6 +85,9 @@ WORKLOADS: Dict[str, Workload] = {
     # sharp variant of layer_b1: q/K/V ~ N(0,1)
     "sharp_b1": Workload("sharp_b1", 6, B=1, L=1, steps=512, t0=32768, bank_n=1024,
                          qkv_std=1.0),
+    # one layer, batch 288 (a full round of whole units and 32 more
+    # sequences), 512 decode steps (2 admits)
+    "layer_b288": Workload("layer_b288", 7, B=288, L=1, steps=512, t0=32768, bank_n=1024),
 }
 
 
